@@ -1,0 +1,112 @@
+"""Low-rank indexer: projection, candidate scoring and top-k selection (fp64).
+
+[RTPurboV2] key finding 2: a learned projector maps each head's D-dim query
+and key to r = 16 dims that keep the low-frequency (semantic) RoPE components.
+[RTPurbo]: the 16-dim indexer acts as a scout that picks candidate keys from
+the past context; exact attention then runs on that small set in full
+dimension.  [TriangleMix] interview, top-k matching: keys are grouped into
+blocks and a query is scored against block representatives; the selection is
+the top-k of those scores.
+
+Block mode (one selection per query head and query block b of Bq rows):
+  rows R_b = [b*Bq, min(N, (b+1)*Bq)), qe = max R_b
+  eligible E_b = {c >= f0 : c*Bk <= qe - w}     (blocks holding a causal key
+                 that some row of b can only reach through selection)
+  s_{b,c} = max{ qlow_i . klow_j : i in R_b, j in block c, j <= i }
+  S_b = the k best of E_b by (score desc, index asc); all of E_b if |E_b| <= k
+Cluster mode replaces key blocks by k-means clusters of the low-rank keys:
+  E_b = {m : cluster m has a member j <= qe - w}
+  s_{b,m} = max_{i in R_b} qlow_i . C_m
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def project(X: np.ndarray, P: np.ndarray) -> np.ndarray:
+    """xlow = x P, X [n, D], P [D, r] -> [n, r] in fp64.
+    Pinned: P = [e_0 .. e_{r-1}] returns the first r coordinates of x."""
+    return np.asarray(X, dtype=np.float64) @ np.asarray(P, dtype=np.float64)
+
+
+def eligible_blocks(qe: int, w: int, f0: int, Bk: int) -> np.ndarray:
+    """Key blocks c >= f0 with c*Bk <= qe - w (empty when qe < w)."""
+    if qe - w < 0:
+        return np.zeros(0, dtype=np.int64)
+    c_hi = (qe - w) // Bk
+    return np.arange(f0, c_hi + 1, dtype=np.int64)
+
+
+def block_scores(qlow_rows: np.ndarray, row_ids: np.ndarray, klow: np.ndarray,
+                 blocks: np.ndarray, Bk: int) -> np.ndarray:
+    """Max over causal (query, key) pairs of the low-rank dot product, per
+    candidate key block.  Pinned by a double-loop brute force (N <= 256)."""
+    N = klow.shape[0]
+    out = np.empty(blocks.size, dtype=np.float64)
+    row_ids = np.asarray(row_ids, dtype=np.int64)
+    for t, c in enumerate(blocks):
+        keys = np.arange(c * Bk, min(N, (c + 1) * Bk), dtype=np.int64)
+        dots = qlow_rows @ klow[keys].T                      # [rows, keys]
+        causal = keys[None, :] <= row_ids[:, None]
+        out[t] = np.max(np.where(causal, dots, -np.inf))
+    return out
+
+
+def topk_order(scores: np.ndarray, ids: np.ndarray, k: int) -> np.ndarray:
+    """The k best ids by (score desc, id asc), returned in ascending id order.
+    Pinned: exact ties planted by duplicated key blocks keep the lower ids."""
+    ids = np.asarray(ids, dtype=np.int64)
+    if k <= 0 or ids.size == 0:
+        return np.zeros(0, dtype=np.int64)
+    order = np.lexsort((ids, -np.asarray(scores, dtype=np.float64)))
+    return np.sort(ids[order[:k]])
+
+
+def select_blocks(qlow_h: np.ndarray, klow_g: np.ndarray, N: int, w: int,
+                  Bq: int, Bk: int, k: int, f0: int):
+    """Per query block: the selected key blocks (ascending) and the scores of
+    all eligible blocks (for tie-band checks)."""
+    n_qb = (N + Bq - 1) // Bq
+    sel, scored = [], []
+    for b in range(n_qb):
+        rows = np.arange(b * Bq, min(N, (b + 1) * Bq), dtype=np.int64)
+        qe = int(rows[-1])
+        E = eligible_blocks(qe, w, f0, Bk)
+        s = block_scores(qlow_h[rows], rows, klow_g, E, Bk) if E.size else np.zeros(0)
+        sel.append(topk_order(s, E, k))
+        scored.append((E, s))
+    return sel, scored
+
+
+def eligible_clusters(assign: np.ndarray, M: int, qe: int, w: int) -> np.ndarray:
+    """Clusters with at least one member key j <= qe - w."""
+    lim = qe - w
+    if lim < 0:
+        return np.zeros(0, dtype=np.int64)
+    members = assign[: lim + 1]
+    return np.unique(members).astype(np.int64)
+
+
+def cluster_scores(qlow_rows: np.ndarray, C: np.ndarray, clusters: np.ndarray) -> np.ndarray:
+    """max_{i in block} qlow_i . C_m for each candidate cluster m."""
+    if clusters.size == 0:
+        return np.zeros(0)
+    return np.max(qlow_rows @ C[clusters].T, axis=0)
+
+
+def select_clusters(qlow_h: np.ndarray, C: np.ndarray, assign: np.ndarray, N: int,
+                    w: int, Bq: int, k: int, blocks=None):
+    """Per query block (all, or the listed ones): selected clusters and the
+    scores of the eligible ones."""
+    M = C.shape[0]
+    n_qb = (N + Bq - 1) // Bq
+    blocks = range(n_qb) if blocks is None else blocks
+    sel, scored = {}, {}
+    for b in blocks:
+        rows = np.arange(b * Bq, min(N, (b + 1) * Bq), dtype=np.int64)
+        qe = int(rows[-1])
+        E = eligible_clusters(assign, M, qe, w)
+        s = cluster_scores(qlow_h[rows], C, E)
+        sel[b] = topk_order(s, E, k)
+        scored[b] = (E, s)
+    return sel, scored

@@ -1,0 +1,202 @@
+"""One attention layer's prefill, head by head, in fp64.
+
+Head roles follow [RTPurboV2] (retrieval vs streaming heads, ~15% / ~85%) and
+the all-sparse case where every head is a retrieval head; the static masks
+follow [TriangleMix] and [Orthros].
+
+Retrieval head h, query block b (rows R_b):
+  K(i) = SWA(w)(i)  U  {j <= i : block(j) in S_b}  U  (f0 ? {j <= i : j < Bk} : {})
+  (cluster mode: {j <= i : a_j in S_b} in place of the block term)
+[RTPurbo]: exact softmax over the selected candidates in full dimension, with
+the local window of the head's own neighbourhood.
+
+Orthros, output positions p in [N - n_out, N):
+  q'_{h,p} = q_{h,p} * s_h + o_h   (elementwise, per head; [Orthros] "Scale-Offset"
+  separates the cross-attention query from the SWA query that shares weights)
+  O_out[p, h] = attention of q' over keys {0..p}   ("Prefilling" section: only
+  the last prompt token runs full cross-attention over the whole KV).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Callable, Dict, Optional, Sequence
+
+import numpy as np
+
+from .attention import attend_rows, softmax_attention, visible_dense, visible_swa, visible_triangle
+from .indexer import (cluster_scores, eligible_blocks, eligible_clusters, block_scores,
+                      project, topk_order)
+from .kmeans import lloyd
+
+SWA, RETRIEVAL, TRIANGLE, DENSE = 0, 1, 2, 3
+
+
+def head_group(h: int, Hq: int, Hkv: int) -> int:
+    """Query head h reads KV head h // (Hq / Hkv) (consecutive GQA groups)."""
+    return h // (Hq // Hkv)
+
+
+def retrieval_key_set(rows: np.ndarray, w: int, Bk: int, f0: int, *,
+                      blocks: Optional[np.ndarray] = None,
+                      clusters: Optional[np.ndarray] = None,
+                      assign: Optional[np.ndarray] = None,
+                      n_clusters: int = 0):
+    """Candidate key ids and the exact visibility predicate for a retrieval
+    head's query block (window  U  selected blocks or clusters  U  block 0)."""
+    r0, r1 = int(rows[0]), int(rows[-1]) + 1
+    parts = [np.arange(max(0, r0 - w + 1), r1, dtype=np.int64)]
+    if blocks is not None:
+        for c in blocks:
+            parts.append(np.arange(c * Bk, min(r1, (c + 1) * Bk), dtype=np.int64))
+    if f0:
+        parts.append(np.arange(0, min(r1, Bk), dtype=np.int64))
+    sel_mask = None
+    if clusters is not None:
+        sel_mask = np.zeros(max(n_clusters, int(assign.max()) + 1 if assign.size else 1), dtype=bool)
+        if clusters.size:
+            sel_mask[clusters] = True
+        members = np.nonzero(sel_mask[assign[:r1]])[0].astype(np.int64)
+        parts.append(members)
+    keys = np.unique(np.concatenate(parts))
+    blockset = np.zeros(0, dtype=np.int64) if blocks is None else np.asarray(blocks, dtype=np.int64)
+
+    def visible(ri, kj):
+        win = visible_swa(ri, kj, w)
+        causal = kj[None, :] <= ri[:, None]
+        chosen = np.isin(kj // Bk, blockset)
+        if f0:
+            chosen = chosen | (kj < Bk)
+        if clusters is not None:
+            chosen = chosen | sel_mask[assign[kj]]
+        return win | (causal & chosen[None, :])
+
+    return keys, visible
+
+
+@dataclasses.dataclass
+class OracleResult:
+    rows: np.ndarray                       # query rows computed, ascending
+    O: np.ndarray                          # [len(rows), Hq, D] fp64
+    O_out: Optional[np.ndarray]            # [n_out, Hq, D] fp64
+    sel: Dict[int, Dict[int, np.ndarray]]  # head -> query block -> selected ids
+    scored: Dict[int, Dict[int, tuple]]    # head -> block -> (eligible ids, scores)
+    klow: Dict[int, np.ndarray]            # KV head -> [N, r]
+    qlow: Dict[int, Dict[int, np.ndarray]]  # head -> block -> [rows, r]
+    centroids: Dict[int, np.ndarray]
+    assign: Dict[int, np.ndarray]
+
+
+def orthros_cross(q: np.ndarray, s: np.ndarray, o: np.ndarray, K: np.ndarray,
+                  V: np.ndarray, p: int, scale: float) -> np.ndarray:
+    """Cross-attention of the scale-offset query at output position p over
+    keys {0..p}.  Pinned: s = 1, o = 0 gives the dense causal row p."""
+    qp = np.asarray(q, np.float64) * np.asarray(s, np.float64) + np.asarray(o, np.float64)
+    keys = np.arange(p + 1)
+    vis = np.ones((1, p + 1), dtype=bool)
+    return softmax_attention(qp[None, :], K[keys], V[keys], vis, scale)[0]
+
+
+def layer_prefill(w, q_rows: Callable[[int, int], np.ndarray], K: np.ndarray, V: np.ndarray,
+                  P: Optional[np.ndarray] = None, xa_scale=None, xa_offset=None, *,
+                  blocks: Optional[Sequence[int]] = None,
+                  heads: Optional[Sequence[int]] = None,
+                  sel_override: Optional[Dict[int, Dict[int, np.ndarray]]] = None,
+                  kmeans_override: Optional[Dict[int, tuple]] = None,
+                  scale: Optional[float] = None,
+                  with_out: bool = True) -> OracleResult:
+    """Oracle output of one layer.
+
+    w          a ``synth.Workload`` (sizes, head roles, parameters)
+    q_rows     (r0, r1) -> Q rows [r1-r0, Hq, D] as fp64
+    K, V       [N, Hkv, D] fp64
+    P          [Hkv, D, r] indexer projection (retrieval heads only)
+    blocks     query blocks to compute (default: all)
+    sel_override  head -> block -> selection to use instead of the oracle's own
+                  (to grade attention given a validated GPU selection)
+    kmeans_override  KV head -> (centroids, assign) to use instead of Lloyd
+    """
+    N, Hq, Hkv, D = w.n_tokens, w.n_q_heads, w.n_kv_heads, w.head_dim
+    Bq, Bk = w.q_block, w.k_block
+    n_qb = (N + Bq - 1) // Bq
+    sc = (1.0 / np.sqrt(D)) if scale is None else scale
+    blocks = list(range(n_qb)) if blocks is None else sorted(set(int(b) for b in blocks))
+    heads = list(range(Hq)) if heads is None else list(heads)
+    rows_all = np.concatenate([np.arange(b * Bq, min(N, (b + 1) * Bq)) for b in blocks]) \
+        if blocks else np.zeros(0, dtype=np.int64)
+    O = np.zeros((rows_all.size, Hq, D), dtype=np.float64)
+    res = OracleResult(rows_all, O, None, {}, {}, {}, {}, {}, {})
+
+    ret = [h for h in heads if w.head_kind[h] == RETRIEVAL]
+    for g in sorted({head_group(h, Hq, Hkv) for h in ret}):
+        res.klow[g] = project(K[:, g], P[g])
+        if w.n_clusters > 0:
+            if kmeans_override is not None and g in kmeans_override:
+                C, a = kmeans_override[g]
+                C = np.asarray(C, np.float64)
+                a = np.asarray(a, np.int64)
+            else:
+                C, a, _ = lloyd(res.klow[g], w.n_clusters, w.kmeans_stride, w.kmeans_iters)
+            res.centroids[g], res.assign[g] = C, a
+
+    off = 0
+    for b in blocks:
+        r0, r1 = b * Bq, min(N, (b + 1) * Bq)
+        rows = np.arange(r0, r1, dtype=np.int64)
+        Qb = q_rows(r0, r1)
+        qe = r1 - 1
+        for h in heads:
+            g = head_group(h, Hq, Hkv)
+            kind = w.head_kind[h]
+            q = Qb[:, h]
+            if kind == DENSE:
+                keys = np.arange(0, r1)
+                o = attend_rows(q, rows, K[:, g], V[:, g], keys, visible_dense, sc)
+            elif kind == SWA:
+                keys = np.arange(max(0, r0 - w.window + 1), r1)
+                o = attend_rows(q, rows, K[:, g], V[:, g], keys,
+                                lambda ri, kj: visible_swa(ri, kj, w.window), sc)
+            elif kind == TRIANGLE:
+                if r1 > N - w.last_q:
+                    keys = np.arange(0, r1)
+                else:
+                    keys = np.unique(np.r_[np.arange(0, min(w.sink, r1)),
+                                           np.arange(max(0, r0 - w.window + 1), r1)])
+                o = attend_rows(q, rows, K[:, g], V[:, g], keys,
+                                lambda ri, kj: visible_triangle(ri, kj, N, w.sink, w.window, w.last_q), sc)
+            elif kind == RETRIEVAL:
+                ql = project(q, P[g])
+                res.qlow.setdefault(h, {})[b] = ql
+                if w.n_clusters > 0:
+                    C, a = res.centroids[g], res.assign[g]
+                    E = eligible_clusters(a, C.shape[0], qe, w.window)
+                    s = cluster_scores(ql, C, E)
+                    S = topk_order(s, E, w.topk)
+                    if sel_override is not None:
+                        S = np.asarray(sel_override[h][b], dtype=np.int64)
+                    keys, vis = retrieval_key_set(rows, w.window, Bk, 0, clusters=S, assign=a,
+                                                  n_clusters=C.shape[0])
+                else:
+                    E = eligible_blocks(qe, w.window, w.force_block0, Bk)
+                    s = block_scores(ql, rows, res.klow[g], E, Bk) if E.size else np.zeros(0)
+                    S = topk_order(s, E, w.topk)
+                    if sel_override is not None:
+                        S = np.asarray(sel_override[h][b], dtype=np.int64)
+                    keys, vis = retrieval_key_set(rows, w.window, Bk, w.force_block0, blocks=S)
+                res.sel.setdefault(h, {})[b] = S
+                res.scored.setdefault(h, {})[b] = (E, s)
+                o = attend_rows(q, rows, K[:, g], V[:, g], keys, vis, sc)
+            else:
+                raise ValueError(f"unknown head kind {kind}")
+            O[off:off + rows.size, h] = o
+        off += rows.size
+
+    if with_out and w.n_out > 0:
+        Oo = np.zeros((w.n_out, Hq, D), dtype=np.float64)
+        for t in range(w.n_out):
+            p = N - w.n_out + t
+            qp = q_rows(p, p + 1)[0]
+            for h in heads:
+                g = head_group(h, Hq, Hkv)
+                Oo[t, h] = orthros_cross(qp[h], xa_scale[h], xa_offset[h], K[:, g], V[:, g], p, sc)
+        res.O_out = Oo
+    return res
