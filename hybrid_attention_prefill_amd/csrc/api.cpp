@@ -1,0 +1,394 @@
+// Host side of the C ABI declared in include/ha.h: argument checks (before
+// any HIP call), workspace layout, head packing and launch order.
+#include "ha.h"
+
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "common.h"
+
+namespace ha {
+namespace {
+
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+struct Heads {
+  std::vector<int> ret;       // retrieval heads, ascending
+  std::vector<int> ret_slot;  // [Hq] slot in ret or -1
+  bool any_band = false;
+};
+
+int check_desc(const ha_layer_desc* d, const int32_t* kinds, Heads* out) {
+  if (!d) return HA_ERR_ARG;
+  if (d->n_tokens < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1) return HA_ERR_ARG;
+  if (d->n_q_heads % d->n_kv_heads != 0) return HA_ERR_ARG;
+  if (d->head_dim < 1 || d->q_block < 1 || d->k_block < 1) return HA_ERR_ARG;
+  if (d->n_q_heads > kMaxHeads) return HA_ERR_UNSUPPORTED;
+  if (d->head_dim != kHeadDim) return HA_ERR_UNSUPPORTED;
+  if (d->q_block != kBlock || d->k_block != kBlock) return HA_ERR_UNSUPPORTED;
+  if (d->n_out < 0 || d->n_out > d->n_tokens) return HA_ERR_ARG;
+  if (d->n_out > 0 && d->n_q_heads / d->n_kv_heads > 16) return HA_ERR_UNSUPPORTED;
+  if (!kinds) return HA_ERR_ARG;
+  Heads h;
+  h.ret_slot.assign(d->n_q_heads, -1);
+  bool need_window = false, any_tri = false;
+  for (int i = 0; i < d->n_q_heads; ++i) {
+    const int k = kinds[i];
+    if (k < HA_SWA || k > HA_DENSE) return HA_ERR_ARG;
+    if (k == HA_RETRIEVAL) {
+      h.ret_slot[i] = (int)h.ret.size();
+      h.ret.push_back(i);
+    } else {
+      h.any_band = true;
+    }
+    if (k != HA_DENSE) need_window = true;
+    if (k == HA_TRIANGLE) any_tri = true;
+  }
+  if (need_window && d->window < 1) return HA_ERR_ARG;
+  if (any_tri && (d->sink < 0 || d->last_q < 0)) return HA_ERR_ARG;
+  if (!h.ret.empty()) {
+    if (d->rank < 1 || d->topk < 0) return HA_ERR_ARG;
+    if (d->force_block0 != 0 && d->force_block0 != 1) return HA_ERR_ARG;
+    if (d->rank != kRank) return HA_ERR_UNSUPPORTED;
+    if (d->topk > kMaxTopk) return HA_ERR_UNSUPPORTED;
+    if (d->n_clusters < 0) return HA_ERR_ARG;
+    if (d->n_clusters > 0) {
+      if (d->kmeans_iters < 1 || d->kmeans_stride < 1) return HA_ERR_ARG;
+      if ((int64_t)d->n_clusters * d->kmeans_stride > d->n_tokens) return HA_ERR_ARG;
+      return HA_ERR_UNSUPPORTED;  // cluster mode is not built in this version
+    } else {
+      const int n_kb = (d->n_tokens + kBlock - 1) / kBlock;
+      if (n_kb > kMaxSelCand) return HA_ERR_UNSUPPORTED;
+    }
+  }
+  if (out) *out = std::move(h);
+  return HA_OK;
+}
+
+inline int n_qb_of(const ha_layer_desc* d) { return (d->n_tokens + kBlock - 1) / kBlock; }
+inline int n_cross_chunks(const ha_layer_desc* d) { return (d->n_tokens + kCrossChunk - 1) / kCrossChunk; }
+
+struct Layout {
+  size_t qlow, klow, sel, cross, total;
+};
+
+Layout layout_of(const ha_layer_desc* d, const Heads& h) {
+  Layout L{};
+  size_t off = 0;
+  const size_t N = (size_t)d->n_tokens, Hret = h.ret.size();
+  L.qlow = off;
+  off += align_up(Hret * N * kRank * sizeof(float));
+  L.klow = off;
+  off += Hret ? align_up((size_t)d->n_kv_heads * N * kRank * sizeof(float)) : 0;
+  L.sel = off;
+  off += align_up(Hret * (size_t)n_qb_of(d) * (size_t)std::max(0, d->topk) * sizeof(int32_t));
+  L.cross = off;
+  off += align_up((size_t)d->n_out * d->n_q_heads * (size_t)n_cross_chunks(d) * (kHeadDim + 2) * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+inline float scale_c(const ha_layer_desc* d) {
+  const float sc = d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / sqrtf((float)d->head_dim);
+  return sc * 1.4426950408889634f;
+}
+
+inline int dev_status(hipError_t e) { return e == hipSuccess ? HA_OK : HA_ERR_DEVICE; }
+
+// Packs of up to 4 heads with one role and one KV head.
+void build_packs(const ha_layer_desc* d, const int32_t* kinds, int kind, const std::vector<int>& slot,
+                 PackTable* pt) {
+  const int G = d->n_q_heads / d->n_kv_heads;
+  pt->n = 0;
+  for (int g = 0; g < d->n_kv_heads; ++g) {
+    uint32_t w = 0, s = 0;
+    int cnt = 0;
+    for (int hh = 0; hh < G; ++hh) {
+      const int h = g * G + hh;
+      if (kinds[h] != kind) continue;
+      w |= (uint32_t)h << (8 * cnt);
+      s |= (uint32_t)(slot.empty() ? 0 : std::max(0, slot[h])) << (8 * cnt);
+      if (++cnt == 4) {
+        pt->heads[pt->n] = w;
+        pt->slots[pt->n] = s;
+        ++pt->n;
+        w = s = 0;
+        cnt = 0;
+      }
+    }
+    if (cnt) {
+      for (int x = cnt; x < 4; ++x) w |= 0xFFu << (8 * x);
+      pt->heads[pt->n] = w;
+      pt->slots[pt->n] = s;
+      ++pt->n;
+    }
+  }
+}
+
+AttnParams attn_params(const ha_layer_desc* d, const void* Q, const void* K, const void* V, float* O) {
+  AttnParams p{};
+  p.Q = static_cast<const uint16_t*>(Q);
+  p.K = static_cast<const uint16_t*>(K);
+  p.V = static_cast<const uint16_t*>(V);
+  p.O = O;
+  p.N = d->n_tokens;
+  p.Hq = d->n_q_heads;
+  p.Hkv = d->n_kv_heads;
+  p.G = d->n_q_heads / d->n_kv_heads;
+  p.c = scale_c(d);
+  p.window = d->window;
+  p.sink = d->sink;
+  p.dense_from = d->n_tokens - d->last_q;
+  p.n_qt = n_qb_of(d);
+  p.topk = d->topk;
+  p.force_block0 = d->force_block0;
+  return p;
+}
+
+int run_band(const ha_layer_desc* d, const int32_t* kinds, const void* Q, const void* K, const void* V,
+             float* O, hipStream_t s) {
+  AttnParams p = attn_params(d, Q, K, V, O);
+  static const int band_kinds[3] = {TRIANGLE, DENSE, SWA};
+  for (int kind : band_kinds) {
+    PackTable pt;
+    build_packs(d, kinds, kind, {}, &pt);
+    if (pt.n == 0) continue;
+    p.kind = kind;
+    const int st = dev_status(launch_attn_band(p, pt, s));
+    if (st != HA_OK) return st;
+  }
+  return HA_OK;
+}
+
+int run_project(const ha_layer_desc* d, const Heads& h, const void* Q, const void* K, const float* P,
+                float* qlow, float* klow, hipStream_t s) {
+  const int G = d->n_q_heads / d->n_kv_heads;
+  ProjParams pp{};
+  pp.N = d->n_tokens;
+  pp.P = P;
+  if (qlow && !h.ret.empty()) {
+    pp.X = static_cast<const uint16_t*>(Q);
+    pp.H = d->n_q_heads;
+    pp.out = qlow;
+    pp.n_entries = (int)h.ret.size();
+    for (int t = 0; t < pp.n_entries; ++t) {
+      pp.head[t] = h.ret[t];
+      pp.group[t] = h.ret[t] / G;
+    }
+    const int st = dev_status(launch_project(pp, s));
+    if (st != HA_OK) return st;
+  }
+  if (klow) {
+    pp.X = static_cast<const uint16_t*>(K);
+    pp.H = d->n_kv_heads;
+    pp.out = klow;
+    pp.n_entries = d->n_kv_heads;
+    for (int g = 0; g < pp.n_entries; ++g) {
+      pp.head[g] = g;
+      pp.group[g] = g;
+    }
+    const int st = dev_status(launch_project(pp, s));
+    if (st != HA_OK) return st;
+  }
+  return HA_OK;
+}
+
+int run_select_blocks(const ha_layer_desc* d, const Heads& h, const float* qlow, const float* klow,
+                      int32_t* sel, hipStream_t s) {
+  const int G = d->n_q_heads / d->n_kv_heads;
+  SelectParams sp{};
+  sp.qlow = qlow;
+  sp.klow = klow;
+  sp.sel = sel;
+  sp.N = d->n_tokens;
+  sp.n_qb = n_qb_of(d);
+  sp.window = d->window;
+  sp.topk = d->topk;
+  sp.force_block0 = d->force_block0;
+  sp.n_ret = (int)h.ret.size();
+  for (int t = 0; t < sp.n_ret; ++t) sp.group_of_ret[t] = h.ret[t] / G;
+  return dev_status(launch_select_blocks(sp, s));
+}
+
+int run_gather(const ha_layer_desc* d, const int32_t* kinds, const Heads& h, const void* Q, const void* K,
+               const void* V, const int32_t* sel, float* O, hipStream_t s) {
+  if (h.ret.empty()) return HA_OK;
+  AttnParams p = attn_params(d, Q, K, V, O);
+  p.kind = RETRIEVAL;
+  p.sel = sel;
+  PackTable pt;
+  build_packs(d, kinds, RETRIEVAL, h.ret_slot, &pt);
+  return dev_status(launch_attn_gather_blocks(p, pt, s));
+}
+
+int run_cross(const ha_layer_desc* d, const void* Q, const void* K, const void* V, const float* xs,
+              const float* xo, float* O_out, float* part, hipStream_t s) {
+  if (d->n_out == 0) return HA_OK;
+  CrossParams cp{};
+  cp.Q = static_cast<const uint16_t*>(Q);
+  cp.K = static_cast<const uint16_t*>(K);
+  cp.V = static_cast<const uint16_t*>(V);
+  cp.xs = xs;
+  cp.xo = xo;
+  cp.O_out = O_out;
+  cp.part = part;
+  cp.N = d->n_tokens;
+  cp.Hq = d->n_q_heads;
+  cp.Hkv = d->n_kv_heads;
+  cp.G = d->n_q_heads / d->n_kv_heads;
+  cp.n_out = d->n_out;
+  cp.n_chunks = n_cross_chunks(d);
+  cp.c = scale_c(d);
+  return dev_status(launch_cross(cp, s));
+}
+
+inline char* ws_at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+bool ws_ok(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return true;
+  if (!ws || ws_bytes < need) return false;
+  return (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) == 0;
+}
+
+}  // namespace
+}  // namespace ha
+
+using namespace ha;
+
+extern "C" {
+
+const char* ha_status_string(int status) {
+  switch (status) {
+    case HA_OK: return "HA_OK";
+    case HA_ERR_ARG: return "HA_ERR_ARG: invalid argument";
+    case HA_ERR_UNSUPPORTED: return "HA_ERR_UNSUPPORTED: configuration not supported by this build";
+    case HA_ERR_WORKSPACE: return "HA_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case HA_ERR_DEVICE: return "HA_ERR_DEVICE: HIP launch failed";
+    default: return "unknown ha_status";
+  }
+}
+
+int ha_version(void) { return HA_VERSION; }
+
+size_t ha_workspace_bytes(const ha_layer_desc* desc, const int32_t* head_kind) {
+  Heads h;
+  if (check_desc(desc, head_kind, &h) != HA_OK) return 0;
+  return layout_of(desc, h).total;
+}
+
+int ha_prefill(const ha_layer_desc* desc, const int32_t* head_kind, const void* Q, const void* K,
+               const void* V, const float* P_idx, const float* xa_scale, const float* xa_offset, float* O,
+               float* O_out, ha_aux* aux, void* workspace, size_t ws_bytes, void* stream) {
+  Heads h;
+  int st = check_desc(desc, head_kind, &h);
+  if (st != HA_OK) return st;
+  if (!Q || !K || !V || !O) return HA_ERR_ARG;
+  if (!h.ret.empty() && !P_idx) return HA_ERR_ARG;
+  if (desc->n_out > 0 && (!xa_scale || !xa_offset || !O_out)) return HA_ERR_ARG;
+  const Layout L = layout_of(desc, h);
+  if (!ws_ok(workspace, ws_bytes, L.total)) return HA_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  if (!h.ret.empty()) {
+    float* qlow = (aux && aux->qlow) ? aux->qlow : reinterpret_cast<float*>(ws_at(workspace, L.qlow));
+    float* klow = (aux && aux->klow) ? aux->klow : reinterpret_cast<float*>(ws_at(workspace, L.klow));
+    int32_t* sel = (aux && aux->sel) ? aux->sel : reinterpret_cast<int32_t*>(ws_at(workspace, L.sel));
+    st = run_project(desc, h, Q, K, P_idx, qlow, klow, s);
+    if (st != HA_OK) return st;
+    st = run_select_blocks(desc, h, qlow, klow, sel, s);
+    if (st != HA_OK) return st;
+    st = run_gather(desc, head_kind, h, Q, K, V, sel, O, s);
+    if (st != HA_OK) return st;
+  }
+  if (h.any_band) {
+    st = run_band(desc, head_kind, Q, K, V, O, s);
+    if (st != HA_OK) return st;
+  }
+  if (desc->n_out > 0) {
+    st = run_cross(desc, Q, K, V, xa_scale, xa_offset, O_out, reinterpret_cast<float*>(ws_at(workspace, L.cross)), s);
+    if (st != HA_OK) return st;
+  }
+  return HA_OK;
+}
+
+int ha_index_project(const ha_layer_desc* desc, const int32_t* head_kind, const void* Q, const void* K,
+                     const float* P_idx, float* qlow, float* klow, void* stream) {
+  Heads h;
+  int st = check_desc(desc, head_kind, &h);
+  if (st != HA_OK) return st;
+  if (h.ret.empty()) return HA_ERR_ARG;
+  if (!P_idx || !K || !klow || (qlow && !Q)) return HA_ERR_ARG;
+  return run_project(desc, h, Q, K, P_idx, qlow, klow, static_cast<hipStream_t>(stream));
+}
+
+int ha_select_blocks(const ha_layer_desc* desc, const int32_t* head_kind, const float* qlow, const float* klow,
+                     int32_t* sel, void* stream) {
+  Heads h;
+  int st = check_desc(desc, head_kind, &h);
+  if (st != HA_OK) return st;
+  if (h.ret.empty() || desc->n_clusters != 0) return HA_ERR_ARG;
+  if (!qlow || !klow || !sel) return HA_ERR_ARG;
+  return run_select_blocks(desc, h, qlow, klow, sel, static_cast<hipStream_t>(stream));
+}
+
+int ha_kmeans(const ha_layer_desc* desc, const float* klow, float* centroids, int32_t* assign, int32_t* csr_off,
+              int32_t* csr_mem, void* workspace, size_t ws_bytes, void* stream) {
+  (void)klow; (void)centroids; (void)assign; (void)csr_off; (void)csr_mem;
+  (void)workspace; (void)ws_bytes; (void)stream;
+  if (!desc) return HA_ERR_ARG;
+  return HA_ERR_UNSUPPORTED;
+}
+
+int ha_select_clusters(const ha_layer_desc* desc, const int32_t* head_kind, const float* qlow,
+                       const float* centroids, const int32_t* csr_off, const int32_t* csr_mem, int32_t* sel,
+                       void* workspace, size_t ws_bytes, void* stream) {
+  (void)head_kind; (void)qlow; (void)centroids; (void)csr_off; (void)csr_mem; (void)sel;
+  (void)workspace; (void)ws_bytes; (void)stream;
+  if (!desc) return HA_ERR_ARG;
+  return HA_ERR_UNSUPPORTED;
+}
+
+int ha_attn_band(const ha_layer_desc* desc, const int32_t* head_kind, const void* Q, const void* K, const void* V,
+                 float* O, void* workspace, size_t ws_bytes, void* stream) {
+  (void)workspace; (void)ws_bytes;
+  Heads h;
+  int st = check_desc(desc, head_kind, &h);
+  if (st != HA_OK) return st;
+  if (!Q || !K || !V || !O) return HA_ERR_ARG;
+  return run_band(desc, head_kind, Q, K, V, O, static_cast<hipStream_t>(stream));
+}
+
+int ha_attn_gather(const ha_layer_desc* desc, const int32_t* head_kind, const void* Q, const void* K,
+                   const void* V, const int32_t* sel, const int32_t* csr_off, const int32_t* csr_mem, float* O,
+                   void* workspace, size_t ws_bytes, void* stream) {
+  (void)workspace; (void)ws_bytes; (void)csr_off; (void)csr_mem;
+  Heads h;
+  int st = check_desc(desc, head_kind, &h);
+  if (st != HA_OK) return st;
+  if (h.ret.empty()) return HA_ERR_ARG;
+  if (!Q || !K || !V || !O || (desc->topk > 0 && !sel)) return HA_ERR_ARG;
+  return run_gather(desc, head_kind, h, Q, K, V, sel, O, static_cast<hipStream_t>(stream));
+}
+
+int ha_attn_cross(const ha_layer_desc* desc, const void* Q, const void* K, const void* V, const float* xa_scale,
+                  const float* xa_offset, float* O_out, void* workspace, size_t ws_bytes, void* stream) {
+  if (!desc) return HA_ERR_ARG;
+  if (desc->n_tokens < 1 || desc->n_q_heads < 1 || desc->n_kv_heads < 1 ||
+      desc->n_q_heads % desc->n_kv_heads != 0 || desc->n_out < 1 || desc->n_out > desc->n_tokens)
+    return HA_ERR_ARG;
+  if (desc->head_dim != kHeadDim) return desc->head_dim < 1 ? HA_ERR_ARG : HA_ERR_UNSUPPORTED;
+  if (desc->n_q_heads / desc->n_kv_heads > 16 || desc->n_q_heads > kMaxHeads) return HA_ERR_UNSUPPORTED;
+  if (!Q || !K || !V || !xa_scale || !xa_offset || !O_out) return HA_ERR_ARG;
+  const size_t need = align_up((size_t)desc->n_out * desc->n_q_heads * (size_t)n_cross_chunks(desc) *
+                               (kHeadDim + 2) * sizeof(float));
+  if (!ws_ok(workspace, ws_bytes, need)) return HA_ERR_WORKSPACE;
+  return run_cross(desc, Q, K, V, xa_scale, xa_offset, O_out, static_cast<float*>(workspace),
+                   static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,95 @@
+// Internal declarations shared by the host library and the HIP kernels.
+// Not part of the public interface (that is include/ha.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ha {
+
+constexpr int kHeadDim = 128;   // D
+constexpr int kRank = 16;       // r
+constexpr int kBlock = 64;      // q_block = k_block
+constexpr int kMaxHeads = 256;  // Hq limit (packs fit in a kernel argument)
+constexpr int kMaxTopk = 256;   // topk limit for the gather kernel's LDS tile list
+constexpr int kMaxSelCand = 16384;  // eligible blocks/clusters scored per query block in LDS
+
+enum Kind { SWA = 0, RETRIEVAL = 1, TRIANGLE = 2, DENSE = 3 };
+
+// A pack is up to 4 query heads of one KV head and one role that share their
+// key tiles; the 4 waves of a workgroup take one head each.  Head ids are
+// stored in bytes (0xFF = empty slot).
+struct PackTable {
+  int32_t n;
+  uint32_t heads[kMaxHeads];  // 4 head ids per pack, byte w = wave w's head
+  uint32_t slots[kMaxHeads];  // retrieval slot (row of sel) of each head, same packing
+};
+
+struct AttnParams {
+  const uint16_t* Q;   // bf16 [N, Hq, D]
+  const uint16_t* K;   // bf16 [N, Hkv, D]
+  const uint16_t* V;
+  float* O;            // fp32 [N, Hq, D]
+  int N, Hq, Hkv, G;   // G = Hq / Hkv
+  float c;             // softmax scale * log2(e)
+  int window, sink, dense_from;   // dense_from = N - last_q (TRIANGLE)
+  int kind;            // SWA, DENSE, TRIANGLE (band kernel) or RETRIEVAL (gather)
+  int n_qt;            // query tiles of 64 rows
+  // gather only
+  const int32_t* sel;  // [Hret, n_qb, topk]
+  int topk, force_block0;
+};
+
+// Host launchers (each returns a hipError_t from the launch).
+hipError_t launch_attn_band(const AttnParams& p, const PackTable& packs, hipStream_t s);
+hipError_t launch_attn_gather_blocks(const AttnParams& p, const PackTable& packs, hipStream_t s);
+
+struct ProjParams {
+  const uint16_t* X;   // bf16 [N, H, D]
+  int N, H;            // H = heads in X
+  const float* P;      // fp32 [Hkv, D, r]
+  float* out;          // [n_entries, N, r]
+  int n_entries;
+  int32_t head[kMaxHeads];   // head of X for each entry
+  int32_t group[kMaxHeads];  // projection group for each entry
+};
+hipError_t launch_project(const ProjParams& p, hipStream_t s);
+
+struct SelectParams {
+  const float* qlow;   // [Hret, N, r]
+  const float* klow;   // [Hkv, N, r]   (block mode)
+  const float* cent;   // [Hkv, M, r]   (cluster mode)
+  const int32_t* csr_off;  // [Hkv, M+1]
+  const int32_t* csr_mem;  // [Hkv, N]
+  int32_t* sel;        // [Hret, n_qb, topk]
+  int N, n_qb, window, topk, force_block0, M;
+  int n_ret;
+  int32_t group_of_ret[kMaxHeads];
+};
+hipError_t launch_select_blocks(const SelectParams& p, hipStream_t s);
+
+struct CrossParams {
+  const uint16_t* Q;
+  const uint16_t* K;
+  const uint16_t* V;
+  const float* xs;     // [Hq, D]
+  const float* xo;     // [Hq, D]
+  float* O_out;        // [n_out, Hq, D]
+  float* part;         // workspace partials [n_out, Hq, n_chunks, D + 2]
+  int N, Hq, Hkv, G, n_out, n_chunks;
+  float c;             // scale * log2(e)
+};
+constexpr int kCrossChunk = 1024;
+hipError_t launch_cross(const CrossParams& p, hipStream_t s);
+
+// XCD-aware remap of a linear workgroup id: workgroups are dealt round-robin
+// to the 8 XCDs; this makes consecutive logical ids land on the same XCD (and
+// so share its L2).  A bijection on [0, n).
+__device__ inline int xcd_remap(int bid, int n) {
+  const int per = n >> 3, rem = n & 7;
+  const int x = bid & 7, slot = bid >> 3;
+  return (x < rem) ? x * (per + 1) + slot : rem * (per + 1) + (x - rem) * per + slot;
+}
+
+}  // namespace ha

@@ -1,0 +1,188 @@
+/*
+ * ha.h -- head-wise hybrid attention prefill for AMD Instinct MI355X (gfx950).
+ *
+ * One attention layer's prefill over a long context, head by head:
+ *   - streaming heads: causal sliding-window attention (SWA);
+ *   - retrieval heads: a rank-16 low-rank indexer scores key blocks (or k-means
+ *     clusters of the low-rank keys), keeps the top-k per query block, and exact
+ *     softmax attention runs over the selected keys plus the local window;
+ *   - TriangleMix heads: sink keys + local band, dense attention for the last rows;
+ *   - dense heads: plain causal attention;
+ *   - Orthros output positions: full cross-attention of a scale-offset query.
+ *
+ * Sources (page title, passage):
+ *   "RTPurbo" post (tchannels.org, Анализ данных): most heads work locally, a
+ *     few retrieval heads reach far; a cheap 16-dim indexer scouts candidates
+ *     and exact attention runs on them in full dimension.
+ *   "RTPurboV2" article (th-motor.com): ~15% retrieval heads, the rest SWA
+ *     (window 8192 in deployment); projector D -> r = 16; K clustering in the
+ *     low-rank space; all-sparse mode when most heads are retrieval heads.
+ *   36kr interview "Agent 的注意力系统" (TriangleMix introduction): streaming
+ *     region + last Q-K region in deep layers; top-k over key blocks.
+ *   "一个 Attention,两种工作模式" (Orthros), "Prefilling" and design sections:
+ *     SWA for all tokens, full cross-attention for output positions, a light
+ *     scale-offset separating the two query roles.
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers unless marked (host).  All device buffers
+ *     are allocated and owned by the caller; the library never allocates,
+ *     frees or keeps a pointer past the call.
+ *   - Arguments are checked on the host before any HIP call; a call that
+ *     returns an error has enqueued nothing.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *     and is asynchronous: outputs are valid once the stream has completed.
+ *     No entry point synchronises.
+ *   - The library holds no global mutable state; concurrent calls are safe
+ *     as long as they do not share output or workspace buffers.
+ *   - Layouts are token-major and contiguous:
+ *       Q  bf16 [N, Hq, D]       K, V  bf16 [N, Hkv, D]
+ *       O  fp32 [N, Hq, D]       O_out fp32 [n_out, Hq, D]
+ *     Query head h reads KV head h / (Hq / Hkv).
+ *   - Supported now: head_dim 128, rank 16, q_block = k_block = 64.
+ *     Other values return HA_ERR_UNSUPPORTED.
+ */
+#ifndef HA_H_
+#define HA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HA_VERSION 1
+
+typedef enum {
+  HA_SWA = 0,        /* causal sliding window: keys i-w < j <= i */
+  HA_RETRIEVAL = 1,  /* indexer-selected blocks or clusters + window */
+  HA_TRIANGLE = 2,   /* j <= i and (j < sink or i-j < w or i >= N-last_q) */
+  HA_DENSE = 3       /* j <= i */
+} ha_head_kind;
+
+typedef enum {
+  HA_OK = 0,
+  HA_ERR_ARG = 1,          /* null pointer, inconsistent sizes, bad head kind */
+  HA_ERR_UNSUPPORTED = 2,  /* valid but not built: D != 128, r != 16, blocks != 64 */
+  HA_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than ha_workspace_bytes() */
+  HA_ERR_DEVICE = 4        /* a HIP launch or query failed */
+} ha_status;
+
+typedef struct {
+  int32_t n_tokens;      /* N >= 1 */
+  int32_t n_q_heads;     /* Hq, a multiple of Hkv */
+  int32_t n_kv_heads;    /* Hkv >= 1 */
+  int32_t head_dim;      /* D: 128 */
+  float softmax_scale;   /* <= 0 selects 1/sqrt(D) */
+  int32_t window;        /* w >= 1 for SWA / RETRIEVAL / TRIANGLE heads */
+  int32_t rank;          /* indexer rank r: 16 */
+  int32_t q_block;       /* query rows per selection: 64 */
+  int32_t k_block;       /* keys per selectable block: 64 */
+  int32_t topk;          /* blocks or clusters kept per query block, >= 0 */
+  int32_t force_block0;  /* 1: retrieval heads always see key block 0 */
+  int32_t n_clusters;    /* 0: block selection; M > 0: k-means cluster selection */
+  int32_t kmeans_iters;  /* Lloyd iterations (>= 1 when n_clusters > 0) */
+  int32_t kmeans_stride; /* initial centroid m = low-rank key m*stride; M*stride <= N */
+  int32_t sink;          /* TriangleMix: keys [0, sink) always visible */
+  int32_t last_q;        /* TriangleMix: rows >= N - last_q attend densely */
+  int32_t n_out;         /* Orthros: the last n_out rows also run cross-attention */
+} ha_layer_desc;
+
+/* Optional copies of the indexer's intermediate results (caller-owned device
+ * buffers; any field may be NULL).  Retrieval heads are numbered in
+ * increasing query-head order (Hret of them).  n_qb = ceil(N / q_block). */
+typedef struct {
+  int32_t* sel;        /* [Hret, n_qb, topk] ascending block/cluster ids, -1 padded */
+  float* qlow;         /* [Hret, N, r] low-rank queries */
+  float* klow;         /* [Hkv, N, r] low-rank keys */
+  float* centroids;    /* [Hkv, M, r] */
+  int32_t* assign;     /* [Hkv, N] cluster of each key */
+  int32_t* csr_off;    /* [Hkv, M+1] member offsets */
+  int32_t* csr_mem;    /* [Hkv, N] key positions grouped by cluster, ascending inside */
+} ha_aux;
+
+/* Human-readable name of a status code (static storage). */
+const char* ha_status_string(int status);
+
+/* HA_VERSION of the built library. */
+int ha_version(void);
+
+/* Bytes of device workspace any entry point below needs for this layer
+ * (the maximum over them).  Returns 0 when the descriptor is invalid.
+ * head_kind (host) [Hq]. */
+size_t ha_workspace_bytes(const ha_layer_desc* desc, const int32_t* head_kind);
+
+/* Whole-layer prefill.  Runs, on `stream`: the indexer projection and
+ * selection for retrieval heads (k-means first in cluster mode), the banded /
+ * dense / triangle kernels for the other heads, the gather kernel for the
+ * retrieval heads, and Orthros cross-attention for the last n_out rows.
+ *   head_kind  (host) [Hq] ha_head_kind values
+ *   P_idx      fp32 [Hkv, D, r] indexer projection; NULL iff no retrieval head
+ *   xa_scale, xa_offset  fp32 [Hq, D]; NULL iff n_out == 0
+ *   O          fp32 [N, Hq, D], every row of every head written
+ *   O_out      fp32 [n_out, Hq, D]; NULL iff n_out == 0
+ *   aux        optional (may be NULL), see ha_aux
+ *   workspace  >= ha_workspace_bytes(desc, head_kind) bytes, 256-byte aligned */
+int ha_prefill(const ha_layer_desc* desc, const int32_t* head_kind,
+               const void* Q, const void* K, const void* V, const float* P_idx,
+               const float* xa_scale, const float* xa_offset,
+               float* O, float* O_out, ha_aux* aux,
+               void* workspace, size_t ws_bytes, void* stream);
+
+/* Stage: low-rank projection (RTPurboV2, low-rank projector passage).
+ *   qlow[t] = Q[:, h_t, :] P[g(h_t)] for the t-th retrieval head h_t, [Hret, N, r]
+ *   klow[g] = K[:, g, :] P[g] for every KV head g, [Hkv, N, r]
+ * Accumulates in fp32 from bf16 inputs.  qlow may be NULL (keys only). */
+int ha_index_project(const ha_layer_desc* desc, const int32_t* head_kind,
+                     const void* Q, const void* K, const float* P_idx,
+                     float* qlow, float* klow, void* stream);
+
+/* Stage: block scoring + top-k (RTPurbo scout; TriangleMix interview top-k).
+ * For retrieval head t and query block b: eligible blocks c >= force_block0
+ * with c*k_block <= qe_b - window; score = max over causal (i, j) of
+ * qlow_i . klow_j; keeps the topk best by (score desc, block asc).
+ *   sel  int32 [Hret, n_qb, topk], ascending, -1 padded. */
+int ha_select_blocks(const ha_layer_desc* desc, const int32_t* head_kind,
+                     const float* qlow, const float* klow, int32_t* sel, void* stream);
+
+/* Stage: Lloyd k-means of klow per KV head (RTPurboV2 clustering passage).
+ * M = n_clusters, kmeans_iters iterations, C0_m = klow_{m*stride}; ties go to
+ * the lower centroid; an empty cluster keeps its centroid.  Deterministic:
+ * running with iters = t reproduces the state after t iterations.
+ *   klow [Hkv, N, r]; centroids [Hkv, M, r]; assign [Hkv, N];
+ *   csr_off [Hkv, M+1]; csr_mem [Hkv, N] (members of cluster m at
+ *   csr_mem[off[m] .. off[m+1]), ascending key position). */
+int ha_kmeans(const ha_layer_desc* desc, const float* klow, float* centroids,
+              int32_t* assign, int32_t* csr_off, int32_t* csr_mem,
+              void* workspace, size_t ws_bytes, void* stream);
+
+/* Stage: cluster scoring + top-k.  Eligible clusters have a member
+ * j <= qe_b - window; score = max over the block's rows of qlow_i . C_m. */
+int ha_select_clusters(const ha_layer_desc* desc, const int32_t* head_kind,
+                       const float* qlow, const float* centroids,
+                       const int32_t* csr_off, const int32_t* csr_mem,
+                       int32_t* sel, void* workspace, size_t ws_bytes, void* stream);
+
+/* Stage: SWA, dense and TriangleMix heads of head_kind (others untouched). */
+int ha_attn_band(const ha_layer_desc* desc, const int32_t* head_kind,
+                 const void* Q, const void* K, const void* V, float* O,
+                 void* workspace, size_t ws_bytes, void* stream);
+
+/* Stage: retrieval heads: window U selected keys (U key block 0 when forced).
+ * Block mode reads sel only; cluster mode also reads assign/csr.
+ *   csr_off, csr_mem: NULL in block mode. */
+int ha_attn_gather(const ha_layer_desc* desc, const int32_t* head_kind,
+                   const void* Q, const void* K, const void* V, const int32_t* sel,
+                   const int32_t* csr_off, const int32_t* csr_mem, float* O,
+                   void* workspace, size_t ws_bytes, void* stream);
+
+/* Stage: Orthros cross-attention for rows p in [N-n_out, N):
+ *   q' = q_p * xa_scale[h] + xa_offset[h] (fp32), attention over keys 0..p. */
+int ha_attn_cross(const ha_layer_desc* desc, const void* Q, const void* K, const void* V,
+                  const float* xa_scale, const float* xa_offset, float* O_out,
+                  void* workspace, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HA_H_ */

@@ -1,0 +1,85 @@
+"""GPU-side helpers for the parity tests: device copies of the seeded inputs,
+a run of the C-ABI path, and the comparison rules.
+
+Comparison rules (stated for bf16 inputs with fp32 accumulation):
+  outputs     max |gpu - oracle| <= 2e-2 and mean |gpu - oracle| <= 2e-3
+  low-rank    |gpu - oracle| <= 1e-5 * ||oracle row||_2 per row
+  selections  equal sets, except candidates whose oracle score is within
+              1e-3 * |tau| of the oracle's k-th best score tau (near ties)
+"""
+import numpy as np
+
+import hybrid_attention_prefill_amd as ha
+from synth import inputs as si
+
+OUT_MAX, OUT_MEAN = 2e-2, 2e-3
+LOWRANK_REL = 1e-5
+TIE_REL = 1e-3
+
+
+def dev_bf16(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def dev_f32(x):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+
+
+def run_gpu(w, li, return_aux=True):
+    """The whole layer through ha_prefill on the current stream."""
+    import torch
+    Q, K, V = dev_bf16(li.Q), dev_bf16(li.K), dev_bf16(li.V)
+    P = dev_f32(li.P) if li.P is not None else None
+    xs = dev_f32(li.xa_scale) if li.xa_scale is not None else None
+    xo = dev_f32(li.xa_offset) if li.xa_offset is not None else None
+    res = ha.hybrid_attn_prefill(
+        Q, K, V, w.head_kind, w.window, P, topk=w.topk, block=w.q_block, force_block0=w.force_block0,
+        n_clusters=w.n_clusters, kmeans_iters=w.kmeans_iters, kmeans_stride=w.kmeans_stride,
+        sink=w.sink, last_q=w.last_q, n_out=w.n_out, xa_scale=xs, xa_offset=xo,
+        return_aux=return_aux and bool(w.ret_heads))
+    torch.cuda.synchronize()
+    if not isinstance(res, tuple):
+        res = (res,)
+    O = res[0]
+    O_out = res[1] if w.n_out > 0 else None
+    aux = res[-1] if (return_aux and w.ret_heads) else None
+    return O, O_out, aux
+
+
+def assert_close_out(gpu, ref, what=""):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    err = np.abs(gpu - ref)
+    mx, mean = float(err.max()) if err.size else 0.0, float(err.mean()) if err.size else 0.0
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite output"
+    assert mx <= OUT_MAX and mean <= OUT_MEAN, f"{what}: max abs {mx:.3g}, mean abs {mean:.3g}"
+    return mx, mean
+
+
+def assert_lowrank(gpu, ref, what=""):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    nrm = np.linalg.norm(ref, axis=-1, keepdims=True)
+    bad = np.abs(gpu - ref) > LOWRANK_REL * np.maximum(nrm, 1e-30)
+    assert not bad.any(), f"{what}: {int(bad.sum())} low-rank entries off"
+
+
+def check_selection(gpu_sel, eligible, scores, k, what=""):
+    """gpu_sel: GPU row (ascending, -1 padded); eligible/scores: oracle's."""
+    g = [int(x) for x in gpu_sel if x >= 0]
+    assert g == sorted(g), f"{what}: selection not ascending"
+    assert len(set(g)) == len(g), f"{what}: duplicate ids"
+    kk = min(k, len(eligible))
+    assert len(g) == kk, f"{what}: {len(g)} selected, expected {kk}"
+    if kk == 0:
+        return 0
+    order = np.lexsort((eligible, -scores))
+    tau = scores[order[kk - 1]]
+    ref = set(int(x) for x in eligible[order[:kk]])
+    sc = dict(zip((int(x) for x in eligible), scores))
+    diff = ref.symmetric_difference(g)
+    for c in diff:
+        assert c in sc, f"{what}: block {c} not eligible"
+        assert abs(sc[c] - tau) <= TIE_REL * max(abs(tau), 1e-30), \
+            f"{what}: block {c} (score {sc[c]:.6g}) differs from the oracle outside the tie band (tau {tau:.6g})"
+    return len(diff)

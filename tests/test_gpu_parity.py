@@ -1,0 +1,104 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle, at sizes the
+oracle finishes in seconds: several tiles, ragged tails, edge windows."""
+import numpy as np
+import pytest
+
+import synth
+from synth.configs import Workload, HEAD_DENSE, HEAD_RETRIEVAL, HEAD_SWA, HEAD_TRIANGLE
+from oracle.prefill import layer_prefill
+from tests._util import oracle_arrays
+from tests import _gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _layer(kinds, N, Hkv=2, **kw):
+    return Workload(name="case", n_tokens=N, n_q_heads=len(kinds), n_kv_heads=Hkv, head_kind=tuple(kinds), **kw)
+
+
+def _compare(w, blocks=None, check_sel=True):
+    print(f"\n[case] {w.name} N={w.n_tokens} kinds={w.head_kind} w={w.window} k={w.topk}", flush=True)
+    li = synth.make_layer_inputs(w)
+    O, O_out, aux = _gpu.run_gpu(w, li)
+    q, K, V, P, xs, xo = oracle_arrays(w, li)
+    ref = layer_prefill(w, q, K, V, P, xs, xo, blocks=blocks)
+    Og = O.cpu().numpy()[ref.rows]
+    if w.ret_heads and check_sel:
+        sel = aux["sel"].cpu().numpy()
+        klow = aux["klow"].cpu().numpy()
+        for g, kl in ref.klow.items():
+            _gpu.assert_lowrank(klow[g], kl, f"klow[{g}]")
+        override = {}
+        for t, h in enumerate(w.ret_heads):
+            override[h] = {}
+            for b, (E, s) in ref.scored[h].items():
+                _gpu.check_selection(sel[t, b], E, s, w.topk, f"head {h} block {b}")
+                override[h][b] = np.array([x for x in sel[t, b] if x >= 0], dtype=np.int64)
+        # grade attention given the validated GPU selection
+        ref = layer_prefill(w, q, K, V, P, xs, xo, blocks=blocks, sel_override=override)
+    _gpu.assert_close_out(Og, ref.O, w.name)
+    if w.n_out:
+        _gpu.assert_close_out(O_out.cpu().numpy(), ref.O_out, w.name + " O_out")
+    return O, ref
+
+
+@pytest.mark.parametrize("N", [1, 63, 64, 65, 700])
+@pytest.mark.parametrize("window", [1, 7, 64, 100, 5000])
+def test_swa_heads(N, window):
+    _compare(_layer([HEAD_SWA] * 8, N, window=window))
+
+
+@pytest.mark.parametrize("N", [1, 130, 1000])
+def test_dense_heads(N):
+    _compare(_layer([HEAD_DENSE] * 4, N, Hkv=1))
+
+
+@pytest.mark.parametrize("N,sink,window,last", [(1000, 64, 128, 128), (1000, 3, 50, 37), (777, 100, 1, 0),
+                                                (500, 0, 64, 500), (256, 64, 2048, 128)])
+def test_triangle_heads(N, sink, window, last):
+    _compare(_layer([HEAD_TRIANGLE] * 4, N, window=window, sink=sink, last_q=last))
+
+
+def test_mixed_roles_one_layer():
+    kinds = [HEAD_SWA, HEAD_DENSE, HEAD_TRIANGLE, HEAD_SWA, HEAD_TRIANGLE, HEAD_DENSE, HEAD_SWA, HEAD_SWA]
+    _compare(_layer(kinds, 900, window=130, sink=10, last_q=70))
+
+
+def test_gqa_group_sizes():
+    _compare(_layer([HEAD_SWA] * 6, 300, Hkv=6, window=40))       # G = 1
+    _compare(_layer([HEAD_SWA] * 16, 300, Hkv=2, window=40))      # G = 8: two packs per KV head
+    _compare(_layer([HEAD_SWA] * 5, 300, Hkv=1, window=40))       # partial pack
+
+
+@pytest.mark.parametrize("N,window,topk,f0", [(1000, 100, 3, 0), (1000, 100, 3, 1), (1337, 64, 8, 1),
+                                              (700, 1, 2, 0), (640, 50, 0, 1), (640, 50, 100, 0),
+                                              (300, 5000, 4, 0)])
+def test_retrieval_block_mode(N, window, topk, f0):
+    kinds = [HEAD_RETRIEVAL, HEAD_SWA, HEAD_RETRIEVAL, HEAD_RETRIEVAL, HEAD_SWA, HEAD_RETRIEVAL, HEAD_RETRIEVAL,
+             HEAD_RETRIEVAL]
+    _compare(_layer(kinds, N, window=window, topk=topk, force_block0=f0))
+
+
+def test_tiny_hybrid_layer_full():
+    _compare(synth.WORKLOADS["tiny_hybrid_2k"])
+
+
+def test_planted_component_layer_reduced():
+    w = synth.configs.shrink(synth.WORKLOADS["qwen3_30b_a3b_32k"], 4096, window=1024)
+    _compare(w)
+
+
+@pytest.mark.parametrize("N,n_out", [(1, 1), (3000, 1), (2500, 3)])
+def test_orthros_cross(N, n_out):
+    w = _layer([HEAD_SWA] * 8, N, window=256, n_out=n_out)
+    _compare(w)
+
+
+def test_deterministic_rerun():
+    import torch
+    w = synth.WORKLOADS["tiny_hybrid_2k"]
+    li = synth.make_layer_inputs(w)
+    a = _gpu.run_gpu(w, li)
+    b = _gpu.run_gpu(w, li)
+    assert torch.equal(a[0], b[0])
+    assert torch.equal(a[2]["sel"], b[2]["sel"])
