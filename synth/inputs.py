@@ -60,11 +60,10 @@ def _threads() -> int:
     return max(1, min(16, n))
 
 
-def gen_rows(seed: int, tag: int, row_shape, r0: int, r1: int,
-             std: float = 1.0, mean: float = 0.0) -> np.ndarray:
-    """float32 normal draws for token rows [r0, r1) of a chunked tensor."""
-    row_shape = tuple(row_shape)
-    out = np.empty((r1 - r0,) + row_shape, dtype=np.float32)
+def _chunked(seed: int, tag: int, row_shape, r0: int, r1: int, out: np.ndarray, finish,
+             std: float = 1.0, mean: float = 0.0):
+    """Draw rows [r0, r1) chunk by chunk (threads), pass each float32 chunk
+    through ``finish(rows_lo, rows_hi, x) -> array`` and store it in ``out``."""
     if r1 <= r0:
         return out
     c0, c1 = r0 // CHUNK, (r1 - 1) // CHUNK
@@ -73,15 +72,14 @@ def gen_rows(seed: int, tag: int, row_shape, r0: int, r1: int,
         rng = np.random.default_rng([seed, tag, c])
         lo, hi = c * CHUNK, (c + 1) * CHUNK
         a, b = max(lo, r0), min(hi, r1)
-        if a == lo and b == hi:
-            blk = rng.standard_normal((CHUNK,) + row_shape, dtype=np.float32)
-        else:
-            blk = rng.standard_normal((CHUNK,) + row_shape, dtype=np.float32)[a - lo:b - lo]
+        blk = rng.standard_normal((CHUNK,) + tuple(row_shape), dtype=np.float32)
+        if a != lo or b != hi:
+            blk = blk[a - lo:b - lo]
         if std != 1.0:
             blk *= np.float32(std)
         if mean != 0.0:
             blk += np.float32(mean)
-        out[a - r0:b - r0] = blk
+        out[a - r0:b - r0] = finish(a, b, blk)
 
     cs = list(range(c0, c1 + 1))
     if len(cs) == 1:
@@ -90,6 +88,25 @@ def gen_rows(seed: int, tag: int, row_shape, r0: int, r1: int,
         with ThreadPoolExecutor(_threads()) as ex:
             list(ex.map(one, cs))
     return out
+
+
+def gen_rows(seed: int, tag: int, row_shape, r0: int, r1: int,
+             std: float = 1.0, mean: float = 0.0) -> np.ndarray:
+    """float32 normal draws for token rows [r0, r1) of a chunked tensor."""
+    out = np.empty((max(0, r1 - r0),) + tuple(row_shape), dtype=np.float32)
+    return _chunked(seed, tag, row_shape, r0, r1, out, lambda a, b, x: x, std, mean)
+
+
+def gen_rows_bf16(seed: int, tag: int, row_shape, r0: int, r1: int, plant=None) -> np.ndarray:
+    """Like gen_rows, rounded to bf16 bit patterns per chunk; ``plant(a, b, x)``
+    may modify the float32 rows [a, b) in place before rounding."""
+    out = np.empty((max(0, r1 - r0),) + tuple(row_shape), dtype=np.uint16)
+
+    def finish(a, b, x):
+        if plant is not None:
+            plant(a, b, x)
+        return bf16_round(x)
+    return _chunked(seed, tag, row_shape, r0, r1, out, finish)
 
 
 def gen_param(seed: int, tag: int, shape, std: float = 1.0, mean: float = 0.0) -> np.ndarray:
@@ -141,37 +158,40 @@ def needles(w: Workload) -> Optional[Needles]:
 
 def gen_q(w: Workload, r0: int = 0, r1: Optional[int] = None) -> np.ndarray:
     r1 = w.n_tokens if r1 is None else r1
-    x = gen_rows(w.seed, TAG_Q, (w.n_q_heads, w.head_dim), r0, r1)
     nd = needles(w)
-    if nd is not None:
-        for n in range(nd.q_row.size):
-            i = int(nd.q_row[n])
-            if r0 <= i < r1:
-                x[i - r0, nd.q_head[n]] = nd.vec[n]
-    return bf16_round(x)
+
+    def plant(a, b, x):
+        if nd is not None:
+            for n in range(nd.q_row.size):
+                i = int(nd.q_row[n])
+                if a <= i < b:
+                    x[i - a, nd.q_head[n]] = nd.vec[n]
+    return gen_rows_bf16(w.seed, TAG_Q, (w.n_q_heads, w.head_dim), r0, r1, plant)
 
 
 def gen_k(w: Workload, r0: int = 0, r1: Optional[int] = None) -> np.ndarray:
     r1 = w.n_tokens if r1 is None else r1
-    x = gen_rows(w.seed, TAG_K, (w.n_kv_heads, w.head_dim), r0, r1)
-    if w.recipe == "planted_lowfreq":
-        z, seg_topic = _topics(w)
-        seg = np.arange(r0, r1) // TOPIC_SEGMENT
-        for g in range(w.n_kv_heads):
-            add = 2.0 * z[g, seg_topic[g, seg]]            # [rows, 32]
-            x[:, g, LOWFREQ_DIMS] += add.astype(np.float32)
     nd = needles(w)
-    if nd is not None:
-        for n in range(nd.key_pos.size):
-            p = int(nd.key_pos[n])
-            if r0 <= p < r1:
-                x[p - r0, nd.kv_head[n]] = nd.vec[n]
-    return bf16_round(x)
+    topics = _topics(w) if w.recipe == "planted_lowfreq" else None
+
+    def plant(a, b, x):
+        if topics is not None:
+            z, seg_topic = topics
+            seg = np.arange(a, b) // TOPIC_SEGMENT
+            for g in range(w.n_kv_heads):
+                add = 2.0 * z[g, seg_topic[g, seg]]            # [rows, 32]
+                x[:, g, LOWFREQ_DIMS] += add.astype(np.float32)
+        if nd is not None:
+            for n in range(nd.key_pos.size):
+                p = int(nd.key_pos[n])
+                if a <= p < b:
+                    x[p - a, nd.kv_head[n]] = nd.vec[n]
+    return gen_rows_bf16(w.seed, TAG_K, (w.n_kv_heads, w.head_dim), r0, r1, plant)
 
 
 def gen_v(w: Workload, r0: int = 0, r1: Optional[int] = None) -> np.ndarray:
     r1 = w.n_tokens if r1 is None else r1
-    return bf16_round(gen_rows(w.seed, TAG_V, (w.n_kv_heads, w.head_dim), r0, r1))
+    return gen_rows_bf16(w.seed, TAG_V, (w.n_kv_heads, w.head_dim), r0, r1)
 
 
 def gen_proj(w: Workload) -> np.ndarray:

@@ -1,0 +1,78 @@
+"""Parity at the full workload sizes, in the launch configuration the benchmark
+times (one whole-layer call), checked on sampled query blocks the oracle can
+compute one by one: the first and last blocks, blocks around the window and
+triangle boundaries, and one seeded block per eighth of the sequence."""
+import numpy as np
+import pytest
+
+import synth
+from synth import inputs as si
+from oracle.prefill import layer_prefill
+from tests import _gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample_blocks(w, extra=()):
+    n = w.n_qb
+    rng = np.random.default_rng(1234)
+    strata = [int(rng.integers(s * n // 8, max(s * n // 8 + 1, (s + 1) * n // 8))) for s in range(8)]
+    edge = [0, 1, n - 2, n - 1]
+    if w.window:
+        edge += [min(n - 1, w.window // 64), min(n - 1, w.window // 64 + 1)]
+    return sorted(set(b for b in edge + strata + list(extra) if 0 <= b < n))
+
+
+def _run(name, heads=None, blocks=None):
+    w = synth.WORKLOADS[name]
+    print(f"\n[case] full-size {name}", flush=True)
+    li = synth.make_layer_inputs(w)
+    O, O_out, aux = _gpu.run_gpu(w, li)
+    blocks = _sample_blocks(w) if blocks is None else blocks
+    K, V = si.bf16_to_f64(li.K), si.bf16_to_f64(li.V)
+    P = None if li.P is None else li.P.astype(np.float64)
+    xs = None if li.xa_scale is None else li.xa_scale.astype(np.float64)
+    xo = None if li.xa_offset is None else li.xa_offset.astype(np.float64)
+
+    def q_rows(a, b):
+        return si.bf16_to_f64(li.Q[a:b])
+
+    ref = layer_prefill(w, q_rows, K, V, P, xs, xo, blocks=blocks, heads=heads)
+    if w.ret_heads:
+        sel = aux["sel"].cpu().numpy()
+        override = {}
+        n_diff = 0
+        for t, h in enumerate(w.ret_heads):
+            if heads is not None and h not in heads:
+                continue
+            override[h] = {}
+            for b, (E, s) in ref.scored[h].items():
+                n_diff += _gpu.check_selection(sel[t, b], E, s, w.topk, f"head {h} block {b}")
+                override[h][b] = np.array([x for x in sel[t, b] if x >= 0], dtype=np.int64)
+        print(f"selection differences inside the tie band: {n_diff}")
+        ref = layer_prefill(w, q_rows, K, V, P, xs, xo, blocks=blocks, heads=heads, sel_override=override)
+    Og = O.cpu().numpy()[ref.rows]
+    hs = list(range(w.n_q_heads)) if heads is None else list(heads)
+    mx, mean = _gpu.assert_close_out(Og[:, hs], ref.O[:, hs], name)
+    print(f"{name}: {len(blocks)} blocks x {len(hs)} heads, max abs {mx:.3e}, mean abs {mean:.3e}")
+    if w.n_out:
+        _gpu.assert_close_out(O_out.cpu().numpy()[:, hs], ref.O_out[:, hs], name + " cross")
+
+
+def test_qwen3_30b_layer_32k():
+    _run("qwen3_30b_a3b_32k")
+
+
+def test_trianglemix_layer_128k():
+    w = synth.WORKLOADS["trianglemix_llama8b_128k"]
+    _run("trianglemix_llama8b_128k", heads=list(range(0, 32, 3)),
+         blocks=_sample_blocks(w)[:6] + [w.n_qb - 2, w.n_qb - 1])
+
+
+def test_dense_layer_128k():
+    w = synth.WORKLOADS["dense_llama8b_128k"]
+    _run("dense_llama8b_128k", heads=[0, 5, 13, 31], blocks=[0, 3, 777, w.n_qb // 2, w.n_qb - 1])
+
+
+def test_orthros_layer_128k():
+    _run("orthros_8b_128k", heads=list(range(0, 32, 5)))
