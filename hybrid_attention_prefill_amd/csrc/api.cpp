@@ -60,7 +60,7 @@ int check_desc(const ha_layer_desc* d, const int32_t* kinds, Heads* out) {
     if (d->n_clusters > 0) {
       if (d->kmeans_iters < 1 || d->kmeans_stride < 1) return HA_ERR_ARG;
       if ((int64_t)d->n_clusters * d->kmeans_stride > d->n_tokens) return HA_ERR_ARG;
-      return HA_ERR_UNSUPPORTED;  // cluster mode is not built in this version
+      if (d->n_clusters > kMaxSelCand) return HA_ERR_UNSUPPORTED;
     } else {
       const int n_kb = (d->n_tokens + kBlock - 1) / kBlock;
       if (n_kb > kMaxSelCand) return HA_ERR_UNSUPPORTED;
@@ -74,7 +74,7 @@ inline int n_qb_of(const ha_layer_desc* d) { return (d->n_tokens + kBlock - 1) /
 inline int n_cross_chunks(const ha_layer_desc* d) { return (d->n_tokens + kCrossChunk - 1) / kCrossChunk; }
 
 struct Layout {
-  size_t qlow, klow, sel, cross, total;
+  size_t qlow, klow, sel, cent, assign, csr_off, csr_mem, km_scratch, cross, total;
 };
 
 Layout layout_of(const ha_layer_desc* d, const Heads& h) {
@@ -87,6 +87,17 @@ Layout layout_of(const ha_layer_desc* d, const Heads& h) {
   off += Hret ? align_up((size_t)d->n_kv_heads * N * kRank * sizeof(float)) : 0;
   L.sel = off;
   off += align_up(Hret * (size_t)n_qb_of(d) * (size_t)std::max(0, d->topk) * sizeof(int32_t));
+  const size_t M = (Hret && d->n_clusters > 0) ? (size_t)d->n_clusters : 0, Hkv = (size_t)d->n_kv_heads;
+  L.cent = off;
+  off += align_up(Hkv * M * kRank * sizeof(float));
+  L.assign = off;
+  off += M ? align_up(Hkv * N * sizeof(int32_t)) : 0;
+  L.csr_off = off;
+  off += M ? align_up(Hkv * (M + 1) * sizeof(int32_t)) : 0;
+  L.csr_mem = off;
+  off += M ? align_up(Hkv * N * sizeof(int32_t)) : 0;
+  L.km_scratch = off;
+  off += M ? align_up(kmeans_scratch_bytes(d->n_tokens, (int)M, d->n_kv_heads)) : 0;
   L.cross = off;
   off += align_up((size_t)d->n_out * d->n_q_heads * (size_t)n_cross_chunks(d) * (kHeadDim + 2) * sizeof(float));
   L.total = off;
@@ -216,14 +227,58 @@ int run_select_blocks(const ha_layer_desc* d, const Heads& h, const float* qlow,
 }
 
 int run_gather(const ha_layer_desc* d, const int32_t* kinds, const Heads& h, const void* Q, const void* K,
-               const void* V, const int32_t* sel, float* O, hipStream_t s) {
+               const void* V, const int32_t* sel, const int32_t* csr_off, const int32_t* csr_mem, float* O,
+               hipStream_t s) {
   if (h.ret.empty()) return HA_OK;
   AttnParams p = attn_params(d, Q, K, V, O);
   p.kind = RETRIEVAL;
   p.sel = sel;
   PackTable pt;
   build_packs(d, kinds, RETRIEVAL, h.ret_slot, &pt);
+  if (d->n_clusters > 0) {
+    p.csr_off = csr_off;
+    p.csr_mem = csr_mem;
+    p.M = d->n_clusters;
+    return dev_status(launch_attn_gather_clusters(p, pt, s));
+  }
   return dev_status(launch_attn_gather_blocks(p, pt, s));
+}
+
+int run_kmeans(const ha_layer_desc* d, const float* klow, float* cent, int32_t* assign, int32_t* csr_off,
+               int32_t* csr_mem, void* scratch, hipStream_t s) {
+  KmeansParams kp{};
+  kp.klow = klow;
+  kp.cent = cent;
+  kp.assign = assign;
+  kp.csr_off = csr_off;
+  kp.csr_mem = csr_mem;
+  kp.N = d->n_tokens;
+  kp.M = d->n_clusters;
+  kp.stride = d->kmeans_stride;
+  kp.hist = static_cast<int32_t*>(scratch);
+  const size_t n_chunks_m = kmeans_scratch_bytes(d->n_tokens, d->n_clusters, d->n_kv_heads) / sizeof(int32_t) -
+                            (size_t)d->n_kv_heads * d->n_clusters;
+  kp.count = kp.hist + n_chunks_m;
+  return dev_status(launch_kmeans(kp, d->n_kv_heads, d->kmeans_iters, s));
+}
+
+int run_select_clusters(const ha_layer_desc* d, const Heads& h, const float* qlow, const float* cent,
+                        const int32_t* csr_off, const int32_t* csr_mem, int32_t* sel, hipStream_t s) {
+  const int G = d->n_q_heads / d->n_kv_heads;
+  SelectParams sp{};
+  sp.qlow = qlow;
+  sp.cent = cent;
+  sp.csr_off = csr_off;
+  sp.csr_mem = csr_mem;
+  sp.sel = sel;
+  sp.N = d->n_tokens;
+  sp.n_qb = n_qb_of(d);
+  sp.window = d->window;
+  sp.topk = d->topk;
+  sp.M = d->n_clusters;
+  sp.n_ret = (int)h.ret.size();
+  for (int t = 0; t < sp.n_ret; ++t) sp.group_of_ret[t] = h.ret[t] / G;
+  return dev_status(launch_select_clusters(sp, s));
 }
 
 int run_cross(const ha_layer_desc* d, const void* Q, const void* K, const void* V, const float* xs,
@@ -300,9 +355,24 @@ int ha_prefill(const ha_layer_desc* desc, const int32_t* head_kind, const void* 
     int32_t* sel = (aux && aux->sel) ? aux->sel : reinterpret_cast<int32_t*>(ws_at(workspace, L.sel));
     st = run_project(desc, h, Q, K, P_idx, qlow, klow, s);
     if (st != HA_OK) return st;
-    st = run_select_blocks(desc, h, qlow, klow, sel, s);
-    if (st != HA_OK) return st;
-    st = run_gather(desc, head_kind, h, Q, K, V, sel, O, s);
+    const int32_t* off = nullptr;
+    const int32_t* mem = nullptr;
+    if (desc->n_clusters > 0) {
+      float* cent = (aux && aux->centroids) ? aux->centroids : reinterpret_cast<float*>(ws_at(workspace, L.cent));
+      int32_t* asg = (aux && aux->assign) ? aux->assign : reinterpret_cast<int32_t*>(ws_at(workspace, L.assign));
+      int32_t* co = (aux && aux->csr_off) ? aux->csr_off : reinterpret_cast<int32_t*>(ws_at(workspace, L.csr_off));
+      int32_t* cm = (aux && aux->csr_mem) ? aux->csr_mem : reinterpret_cast<int32_t*>(ws_at(workspace, L.csr_mem));
+      st = run_kmeans(desc, klow, cent, asg, co, cm, ws_at(workspace, L.km_scratch), s);
+      if (st != HA_OK) return st;
+      st = run_select_clusters(desc, h, qlow, cent, co, cm, sel, s);
+      if (st != HA_OK) return st;
+      off = co;
+      mem = cm;
+    } else {
+      st = run_select_blocks(desc, h, qlow, klow, sel, s);
+      if (st != HA_OK) return st;
+    }
+    st = run_gather(desc, head_kind, h, Q, K, V, sel, off, mem, O, s);
     if (st != HA_OK) return st;
   }
   if (h.any_band) {
@@ -338,19 +408,29 @@ int ha_select_blocks(const ha_layer_desc* desc, const int32_t* head_kind, const 
 
 int ha_kmeans(const ha_layer_desc* desc, const float* klow, float* centroids, int32_t* assign, int32_t* csr_off,
               int32_t* csr_mem, void* workspace, size_t ws_bytes, void* stream) {
-  (void)klow; (void)centroids; (void)assign; (void)csr_off; (void)csr_mem;
-  (void)workspace; (void)ws_bytes; (void)stream;
   if (!desc) return HA_ERR_ARG;
-  return HA_ERR_UNSUPPORTED;
+  const ha_layer_desc* d = desc;
+  if (d->n_tokens < 1 || d->n_kv_heads < 1 || d->n_clusters < 1 || d->kmeans_iters < 1 || d->kmeans_stride < 1)
+    return HA_ERR_ARG;
+  if ((int64_t)d->n_clusters * d->kmeans_stride > d->n_tokens) return HA_ERR_ARG;
+  if (d->rank != kRank) return d->rank < 1 ? HA_ERR_ARG : HA_ERR_UNSUPPORTED;
+  if (d->n_clusters > kMaxSelCand) return HA_ERR_UNSUPPORTED;
+  if (!klow || !centroids || !assign || !csr_off || !csr_mem) return HA_ERR_ARG;
+  if (!ws_ok(workspace, ws_bytes, align_up(kmeans_scratch_bytes(d->n_tokens, d->n_clusters, d->n_kv_heads))))
+    return HA_ERR_WORKSPACE;
+  return run_kmeans(d, klow, centroids, assign, csr_off, csr_mem, workspace, static_cast<hipStream_t>(stream));
 }
 
 int ha_select_clusters(const ha_layer_desc* desc, const int32_t* head_kind, const float* qlow,
                        const float* centroids, const int32_t* csr_off, const int32_t* csr_mem, int32_t* sel,
                        void* workspace, size_t ws_bytes, void* stream) {
-  (void)head_kind; (void)qlow; (void)centroids; (void)csr_off; (void)csr_mem; (void)sel;
-  (void)workspace; (void)ws_bytes; (void)stream;
-  if (!desc) return HA_ERR_ARG;
-  return HA_ERR_UNSUPPORTED;
+  (void)workspace; (void)ws_bytes;
+  Heads h;
+  int st = check_desc(desc, head_kind, &h);
+  if (st != HA_OK) return st;
+  if (h.ret.empty() || desc->n_clusters < 1) return HA_ERR_ARG;
+  if (!qlow || !centroids || !csr_off || !csr_mem || !sel) return HA_ERR_ARG;
+  return run_select_clusters(desc, h, qlow, centroids, csr_off, csr_mem, sel, static_cast<hipStream_t>(stream));
 }
 
 int ha_attn_band(const ha_layer_desc* desc, const int32_t* head_kind, const void* Q, const void* K, const void* V,
@@ -366,13 +446,14 @@ int ha_attn_band(const ha_layer_desc* desc, const int32_t* head_kind, const void
 int ha_attn_gather(const ha_layer_desc* desc, const int32_t* head_kind, const void* Q, const void* K,
                    const void* V, const int32_t* sel, const int32_t* csr_off, const int32_t* csr_mem, float* O,
                    void* workspace, size_t ws_bytes, void* stream) {
-  (void)workspace; (void)ws_bytes; (void)csr_off; (void)csr_mem;
+  (void)workspace; (void)ws_bytes;
   Heads h;
   int st = check_desc(desc, head_kind, &h);
   if (st != HA_OK) return st;
   if (h.ret.empty()) return HA_ERR_ARG;
   if (!Q || !K || !V || !O || (desc->topk > 0 && !sel)) return HA_ERR_ARG;
-  return run_gather(desc, head_kind, h, Q, K, V, sel, O, static_cast<hipStream_t>(stream));
+  if (desc->n_clusters > 0 && (!csr_off || !csr_mem)) return HA_ERR_ARG;
+  return run_gather(desc, head_kind, h, Q, K, V, sel, csr_off, csr_mem, O, static_cast<hipStream_t>(stream));
 }
 
 int ha_attn_cross(const ha_layer_desc* desc, const void* Q, const void* K, const void* V, const float* xa_scale,

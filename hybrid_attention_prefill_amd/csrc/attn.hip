@@ -36,6 +36,8 @@ constexpr int VSTR = BK + 8;         // V^T row stride in LDS (bf16): 144 B
 constexpr int K_ELEMS = BK * KSTR;
 constexpr int V_ELEMS = D * VSTR;
 constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;   // 35840 B per buffer
+constexpr int Q_ELEMS = 64 * KSTR;             // one wave's 64 query rows (17408 B)
+constexpr int SMEM_ELEMS = 2 * BUF_ELEMS + 4 * Q_ELEMS;
 constexpr int NT = 256;
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kMInit = -1e30f;     // finite start for the running max
@@ -55,23 +57,41 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 
 // Global -> registers for one 64-key tile of K and V (KV head g).
-// K: 1024 chunks of 16 B, chunk id -> (key = id/16, d = (id%16)*8), coalesced rows.
-// V: thread -> 4 consecutive keys x 8 consecutive d (transposed on the LDS store).
+// K: 1024 chunks of 16 B, chunk id = c*256 + tid -> (key slot c*16 + tid/16,
+// d = (tid%16)*8): coalesced rows.  V: thread -> key slots 4*(tid%16) + x,
+// d = 8*(tid/16) .. +8 (transposed on the LDS store).  rows[0..3] are the key
+// rows of the K slots, rows[4..7] those of the V slots; -1 = zero fill.
 __device__ __forceinline__ void tile_load(TileRegs& r, const uint16_t* __restrict__ K,
-                                          const uint16_t* __restrict__ V, int k0, int N,
+                                          const uint16_t* __restrict__ V, const int (&rows)[8],
                                           size_t rs, int g, int tid) {
   const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const int id = c * NT + tid;
-    const int key = k0 + (id >> 4);
-    r.k[c] = (key < N) ? *reinterpret_cast<const u32x4*>(K + (size_t)key * rs + g * D + (id & 15) * 8) : z;
+    const int key = rows[c];
+    r.k[c] = (key >= 0) ? *reinterpret_cast<const u32x4*>(K + (size_t)key * rs + g * D + (tid & 15) * 8) : z;
   }
-  const int kg = tid & 15, dc = tid >> 4;
+  const int dc = tid >> 4;
 #pragma unroll
   for (int x = 0; x < 4; ++x) {
-    const int key = k0 + kg * 4 + x;
-    r.v[x] = (key < N) ? *reinterpret_cast<const u32x4*>(V + (size_t)key * rs + g * D + dc * 8) : z;
+    const int key = rows[4 + x];
+    r.v[x] = (key >= 0) ? *reinterpret_cast<const u32x4*>(V + (size_t)key * rs + g * D + dc * 8) : z;
+  }
+}
+
+// Key slots this thread loads: K slots c*16 + tid/16, V slots 4*(tid%16) + x.
+__device__ __forceinline__ int k_slot(int c, int tid) { return c * 16 + (tid >> 4); }
+__device__ __forceinline__ int v_slot(int x, int tid) { return (tid & 15) * 4 + x; }
+
+__device__ __forceinline__ void contiguous_rows(int (&rows)[8], int k0, int N, int tid) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int key = k0 + k_slot(c, tid);
+    rows[c] = key < N ? key : -1;
+  }
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int key = k0 + v_slot(x, tid);
+    rows[4 + x] = key < N ? key : -1;
   }
 }
 
@@ -122,28 +142,40 @@ __device__ __forceinline__ bool tile_full(const MaskSpec& ms, int q0, int k0) {
 
 // One 64-key tile against the wave's 64 query rows, as two 32-key halves
 // (each half is one online-softmax step; this keeps 32 score registers live).
-__device__ __forceinline__ void tile_compute(const uint16_t* __restrict__ buf, const bf16x8 (&qf)[2][8],
-                                             WaveAcc& acc, int lane, int q0, int k0,
-                                             const MaskSpec& ms, float c) {
+// GATHER: the tile's keys are arbitrary positions kpos[0..64) (-1 = empty
+// slot); otherwise keys k0 .. k0+63.
+template <bool GATHER>
+__device__ __forceinline__ void tile_compute(const uint16_t* __restrict__ buf, const uint16_t* __restrict__ Qs,
+                                             const int* __restrict__ kpos, WaveAcc& acc, int lane, int q0,
+                                             int k0, const MaskSpec& ms, float c) {
   const uint16_t* Ks = buf;
   const uint16_t* Vt = buf + K_ELEMS;
   const int lr = lane & 31, lh = lane >> 5;
-  const bool full = tile_full(ms, q0, k0);
+  const bool full = !GATHER && tile_full(ms, q0, k0);
 
+  // S^T = K Q^T for the 64 x 64 tile: [key half][query half]
+  f32x16 s[2][2];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    f32x16 s[2];
+  for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[qb][e] = 0.f;
+      for (int e = 0; e < 16; ++e) s[kb][qb][e] = 0.f;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+  for (int t = 0; t < 8; ++t) {
+    const bf16x8 q0f = *reinterpret_cast<const bf16x8*>(Qs + lr * KSTR + t * 16 + lh * 8);
+    const bf16x8 q1f = *reinterpret_cast<const bf16x8*>(Qs + (32 + lr) * KSTR + t * 16 + lh * 8);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
       const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + (kb * 32 + lr) * KSTR + t * 16 + lh * 8);
-      s[0] = mfma(kf, qf[0][t], s[0]);
-      s[1] = mfma(kf, qf[1][t], s[1]);
+      s[kb][0] = mfma(kf, q0f, s[kb][0]);
+      s[kb][1] = mfma(kf, q1f, s[kb][1]);
     }
+  }
 
+  // each 32-key half is one online-softmax step followed by its PV k-steps
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
     if (!full) {
       const int jb = k0 + kb * 32 + lh * 4;
 #pragma unroll
@@ -152,10 +184,12 @@ __device__ __forceinline__ void tile_compute(const uint16_t* __restrict__ buf, c
         const bool dense_row = i >= ms.dense_from;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int j = jb + (e >> 2) * 8 + (e & 3);
+          const int slot = kb * 32 + lh * 4 + (e >> 2) * 8 + (e & 3);
+          const int j = GATHER ? kpos[slot] : jb + (e >> 2) * 8 + (e & 3);
           const int d = i - j;
-          const bool vis = (d >= ms.a) && (d < ms.b || j < ms.sink || dense_row);
-          if (!vis) s[qb][e] = kNegInf;
+          bool vis = (d >= ms.a) && (d < ms.b || j < ms.sink || dense_row);
+          if (GATHER) vis = vis && j >= 0;
+          if (!vis) s[kb][qb][e] = kNegInf;
         }
       }
     }
@@ -165,7 +199,7 @@ __device__ __forceinline__ void tile_compute(const uint16_t* __restrict__ buf, c
     for (int qb = 0; qb < 2; ++qb) {
       float mx = kNegInf;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[qb][e]);
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][qb][e]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float mnew = fmaxf(acc.m[qb], mx);
       const float alpha = exp2f((acc.m[qb] - mnew) * c);
@@ -174,8 +208,8 @@ __device__ __forceinline__ void tile_compute(const uint16_t* __restrict__ buf, c
       float sum = 0.f;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float pv = exp2f(fmaf(s[qb][e], c, nb));
-        s[qb][e] = pv;
+        const float pv = exp2f(fmaf(s[kb][qb][e], c, nb));
+        s[kb][qb][e] = pv;
         sum += pv;
       }
       acc.l[qb] = acc.l[qb] * alpha + sum;
@@ -186,7 +220,7 @@ __device__ __forceinline__ void tile_compute(const uint16_t* __restrict__ buf, c
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pf[qb][h2][e] = (__bf16)s[qb][h2 * 8 + e];
+        for (int e = 0; e < 8; ++e) pf[qb][h2][e] = (__bf16)s[kb][qb][h2 * 8 + e];
     }
 
 #pragma unroll
@@ -202,21 +236,17 @@ __device__ __forceinline__ void tile_compute(const uint16_t* __restrict__ buf, c
   }
 }
 
-__device__ __forceinline__ void load_q(bf16x8 (&qf)[2][8], const uint16_t* __restrict__ Q, int N, int Hq,
-                                       int h, int q0, int lane) {
-  const int lr = lane & 31, lh = lane >> 5;
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int i = q0 + qb * 32 + lr;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      if (i < N) {
-        qf[qb][t] = *reinterpret_cast<const bf16x8*>(Q + ((size_t)i * Hq + h) * D + t * 16 + lh * 8);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qf[qb][t][e] = (__bf16)0.f;
-      }
-    }
+// The wave's 64 query rows -> LDS (rows >= N are zero).
+__device__ __forceinline__ void load_q_lds(uint16_t* Qs, const uint16_t* __restrict__ Q, int N, int Hq, int h,
+                                           int q0, int lane) {
+#pragma unroll 4
+  for (int c = 0; c < 16; ++c) {
+    const int id = c * 64 + lane;        // 1024 chunks of 16 B
+    const int row = id >> 4, dc = id & 15;
+    const int i = q0 + row;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (i < N) v = *reinterpret_cast<const u32x4*>(Q + ((size_t)i * Hq + h) * D + dc * 8);
+    *reinterpret_cast<u32x4*>(Qs + row * KSTR + dc * 8) = v;
   }
 }
 
@@ -256,42 +286,82 @@ __device__ __forceinline__ void store_o(const WaveAcc& acc, float* __restrict__ 
   }
 }
 
-// Shared pipeline: T tiles, tile idx -> (k0, mask, whether this wave computes it).
-template <class TileInfo>
-__device__ __forceinline__ void run_tiles(const AttnParams& p, uint16_t* smem, int T, int g, int h,
-                                          bool active, int q0, TileInfo&& info) {
-  const int tid = threadIdx.x, lane = tid & 63;
+struct TileDesc {
+  int k0;          // first key (contiguous tiles)
+  MaskSpec ms;
+  bool on;         // this wave computes the tile
+  bool gather;     // keys are looked up; positions in the row ring
+};
+
+// Shared pipeline over T tiles.  info(idx) describes tile idx.  For gathered
+// tiles, lookup(idx, slot) returns the key row of a slot (-1 = empty); the 64
+// slots of tile t+2 are looked up by threads 0..63 while tile t is computed
+// and tile t+1 is in flight, and parked in a 3-entry LDS ring (rows[3][64]),
+// which also serves as the key positions of the tile for masking.
+template <bool ALL_GATHER = false, class Info, class Lookup>
+__device__ __forceinline__ void run_tiles(const AttnParams& p, uint16_t* smem, int (*rows)[BK], int T, int g,
+                                          int h, bool active, int q0, Info&& info, Lookup&& lookup) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const size_t rs = (size_t)p.Hkv * D;
-  bf16x8 qf[2][8];
+  uint16_t* Qs = smem + 2 * BUF_ELEMS + wave * Q_ELEMS;
   WaveAcc acc;
   acc_init(acc);
-  if (active) load_q(qf, p.Q, p.N, p.Hq, h, q0, lane);
+  if (active) load_q_lds(Qs, p.Q, p.N, p.Hq, h, q0, lane);
 
+  auto rows_for = [&](int idx, const TileDesc& d, int(&rr)[8]) {
+    if (ALL_GATHER) {
+      const int* ring = rows[idx % 3];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) rr[c] = ring[k_slot(c, tid)];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) rr[4 + x] = ring[v_slot(x, tid)];
+    } else {
+      contiguous_rows(rr, d.k0, p.N, tid);
+    }
+  };
+  if (ALL_GATHER && tid < BK) {
+    if (T > 0) rows[0][tid] = lookup(0, tid);
+    if (T > 1) rows[1][tid] = lookup(1, tid);
+  }
+  __syncthreads();
   TileRegs r;
-  int k0;
-  MaskSpec ms;
-  bool on;
-  info(0, k0, ms, on);
-  tile_load(r, p.K, p.V, k0, p.N, rs, g, tid);
-  tile_store(r, smem, tid);
+  TileDesc cur = info(0);
+  {
+    int rr[8];
+    rows_for(0, cur, rr);
+    tile_load(r, p.K, p.V, rr, rs, g, tid);
+    tile_store(r, smem, tid);
+  }
   __syncthreads();
   for (int t = 0; t < T; ++t) {
-    const int cur_k0 = k0;
-    const MaskSpec cur_ms = ms;
-    const bool cur_on = on;
-    if (t + 1 < T) {
-      info(t + 1, k0, ms, on);
-      tile_load(r, p.K, p.V, k0, p.N, rs, g, tid);
+    TileDesc nxt = cur;
+    int pending = -1;
+    const bool have_next = t + 1 < T;
+    if (have_next) {
+      nxt = info(t + 1);
+      int rr[8];
+      rows_for(t + 1, nxt, rr);
+      tile_load(r, p.K, p.V, rr, rs, g, tid);
     }
-    if (active && cur_on) tile_compute(smem + (t & 1) * BUF_ELEMS, qf, acc, lane, q0, cur_k0, cur_ms, p.c);
-    if (t + 1 < T) tile_store(r, smem + ((t + 1) & 1) * BUF_ELEMS, tid);
+    const bool prep = ALL_GATHER && t + 2 < T && tid < BK;
+    if (prep) pending = lookup(t + 2, tid);
+    if (active && cur.on) {
+      const uint16_t* buf = smem + (t & 1) * BUF_ELEMS;
+      if (ALL_GATHER)
+        tile_compute<true>(buf, Qs, rows[t % 3], acc, lane, q0, cur.k0, cur.ms, p.c);
+      else
+        tile_compute<false>(buf, Qs, nullptr, acc, lane, q0, cur.k0, cur.ms, p.c);
+    }
+    if (have_next) tile_store(r, smem + ((t + 1) & 1) * BUF_ELEMS, tid);
+    if (prep) rows[(t + 2) % 3][tid] = pending;
+    cur = nxt;
     __syncthreads();
   }
   if (active) store_o(acc, p.O, p.N, p.Hq, h, q0, lane);
 }
 
 __global__ __launch_bounds__(NT, 1) void attn_band_kernel(AttnParams p, PackTable packs) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * BUF_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM_ELEMS];
   const int wave = threadIdx.x >> 6;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
   const int pk = lid / p.n_qt;
@@ -319,11 +389,10 @@ __global__ __launch_bounds__(NT, 1) void attn_band_kernel(AttnParams p, PackTabl
     }
   }
   const int T = st + (hi_t - bl + 1);
-  run_tiles(p, smem, T, g, h, active, q0, [&](int idx, int& k0, MaskSpec& m, bool& on) {
-    k0 = (idx < st ? idx : bl + idx - st) * BK;
-    m = ms;
-    on = true;
-  });
+  auto k0_of = [&](int idx) { return (idx < st ? idx : bl + idx - st) * BK; };
+  run_tiles(
+      p, smem, nullptr, T, g, h, active, q0,
+      [&](int idx) { return TileDesc{k0_of(idx), ms, true, false}; }, [](int, int) { return -1; });
 }
 
 // Retrieval heads, block mode: tiles = forced block 0 + the union of the pack's
@@ -331,7 +400,7 @@ __global__ __launch_bounds__(NT, 1) void attn_band_kernel(AttnParams p, PackTabl
 // A selected block contributes only keys outside the window (j <= i - w), the
 // window tiles only keys inside it, so every key of the union is counted once.
 __global__ __launch_bounds__(NT, 1) void attn_gather_blocks_kernel(AttnParams p, PackTable packs) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * BUF_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM_ELEMS];
   __shared__ int32_t sel_s[4][kMaxTopk];
   __shared__ int32_t list_s[4 * kMaxTopk + 1];   // (block << 4) | wave mask
   __shared__ int32_t n_list;
@@ -388,18 +457,119 @@ __global__ __launch_bounds__(NT, 1) void attn_gather_blocks_kernel(AttnParams p,
   const int T = nl + (hi_t - bl + 1);
   const MaskSpec win = {0, p.window, 0, INT_MAX};
   const MaskSpec out = {p.window, INT_MAX, 0, INT_MAX};
-  run_tiles(p, smem, T, g, h, active, q0, [&](int idx, int& k0, MaskSpec& m, bool& on) {
-    if (idx < nl) {
-      const int e = list_s[idx];
-      k0 = (e >> 4) * BK;
-      m = out;
-      on = (e >> wave) & 1;
-    } else {
-      k0 = (bl + idx - nl) * BK;
-      m = win;
-      on = true;
+  auto k0_of = [&](int idx) { return idx < nl ? (list_s[idx] >> 4) * BK : (bl + idx - nl) * BK; };
+  run_tiles(
+      p, smem, nullptr, T, g, h, active, q0,
+      [&](int idx) {
+        if (idx < nl) return TileDesc{k0_of(idx), out, ((list_s[idx] >> wave) & 1) != 0, false};
+        return TileDesc{k0_of(idx), win, true, false};
+      },
+      [](int, int) { return -1; });
+}
+
+// Retrieval heads, cluster mode: tiles = the window tiles (shared by the
+// pack) followed, head by head, by the members of that head's selected
+// clusters that some row of the block may see (j <= qe - window), 64 per tile
+// in (cluster, position) order; only the owning wave computes those tiles.
+// A member contributes only to rows with j <= i - w (outside the window).
+__global__ __launch_bounds__(NT, 1) void attn_gather_clusters_kernel(AttnParams p, PackTable packs) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM_ELEMS];
+  __shared__ int ring_s[3][BK];
+  __shared__ int lo_s[4][kMaxTopk];
+  __shared__ int pre_s[4][kMaxTopk + 1];
+  __shared__ int ntile_s[4];
+
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int pk = lid / p.n_qt;
+  const int qt = p.n_qt - 1 - (lid % p.n_qt);
+  const uint32_t pw = packs.heads[pk];
+  const uint32_t sw = packs.slots[pk];
+  const int h = (pw >> (8 * wave)) & 0xFF;
+  const bool active = h != 0xFF;
+  const int g = (int)(pw & 0xFF) / p.G;
+  const int q0 = qt * BK;
+  const int lim = min(p.N, q0 + BK) - 1 - p.window;   // members j <= lim can be visible
+  const int32_t* off = p.csr_off + (size_t)g * (p.M + 1);
+  const int32_t* mem = p.csr_mem + (size_t)g * p.N;
+
+  // member counts of every selected cluster (binary search for j <= lim)
+  for (int x = tid; x < 4 * p.topk; x += NT) {
+    const int w = x / p.topk, e = x % p.topk;
+    const int hw = (pw >> (8 * w)) & 0xFF;
+    int lo = 0, cnt = 0;
+    if (hw != 0xFF && lim >= 0) {
+      const int slot = (sw >> (8 * w)) & 0xFF;
+      const int m = p.sel[((size_t)slot * p.n_qt + qt) * p.topk + e];
+      if (m >= 0 && m < p.M) {
+        lo = off[m];
+        int a = lo, b = off[m + 1];
+        while (a < b) {
+          const int mid = (a + b) >> 1;
+          if (mem[mid] <= lim) a = mid + 1;
+          else b = mid;
+        }
+        cnt = a - lo;
+      }
     }
-  });
+    lo_s[w][e] = lo;
+    pre_s[w][e + 1] = cnt;
+  }
+  __syncthreads();
+  if (tid < 4) {
+    int run = 0;
+    pre_s[tid][0] = 0;
+    for (int e = 0; e < p.topk; ++e) {
+      run += pre_s[tid][e + 1];
+      pre_s[tid][e + 1] = run;
+    }
+    ntile_s[tid] = (run + BK - 1) / BK;
+  }
+  __syncthreads();
+  const int hi_t = min(p.N - 1, q0 + 63) >> 6;
+  const int bl = max(0, q0 - p.window + 1) >> 6;
+  const int nwin = hi_t - bl + 1;
+  const int nt0 = ntile_s[0], nt1 = ntile_s[1], nt2 = ntile_s[2], nt3 = ntile_s[3];
+  const int T = nwin + nt0 + nt1 + nt2 + nt3;
+  const MaskSpec win = {0, p.window, 0, INT_MAX};
+  const MaskSpec out = {p.window, INT_MAX, 0, INT_MAX};
+  auto owner = [&](int idx, int& lt) {
+    int x = idx - nwin;
+    if (x < nt0) { lt = x; return 0; }
+    x -= nt0;
+    if (x < nt1) { lt = x; return 1; }
+    x -= nt1;
+    if (x < nt2) { lt = x; return 2; }
+    lt = x - nt2;
+    return 3;
+  };
+  // every tile goes through the lookup path (window tiles too), so the
+  // kernel holds a single instantiation of the tile computation
+  run_tiles<true>(
+      p, smem, ring_s, T, g, h, active, q0,
+      [&](int idx) {
+        if (idx < nwin) return TileDesc{(bl + idx) * BK, win, true, true};
+        int lt;
+        const int w = owner(idx, lt);
+        return TileDesc{0, out, w == wave, true};
+      },
+      [&](int idx, int slot) {
+        if (idx < nwin) {
+          const int j = (bl + idx) * BK + slot;
+          return j < p.N ? j : -1;
+        }
+        int lt;
+        const int w = owner(idx, lt);
+        const int f = lt * BK + slot;
+        if (f >= pre_s[w][p.topk]) return -1;
+        int a = 0, b = p.topk;          // largest e with pre[e] <= f
+        while (b - a > 1) {
+          const int mid = (a + b) >> 1;
+          if (pre_s[w][mid] <= f) a = mid;
+          else b = mid;
+        }
+        return (int)mem[lo_s[w][a] + (f - pre_s[w][a])];
+      });
 }
 
 }  // namespace
@@ -415,6 +585,13 @@ hipError_t launch_attn_gather_blocks(const AttnParams& p, const PackTable& packs
   const int nwg = packs.n * p.n_qt;
   if (nwg == 0) return hipSuccess;
   hipLaunchKernelGGL(attn_gather_blocks_kernel, dim3(nwg), dim3(NT), 0, s, p, packs);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_gather_clusters(const AttnParams& p, const PackTable& packs, hipStream_t s) {
+  const int nwg = packs.n * p.n_qt;
+  if (nwg == 0) return hipSuccess;
+  hipLaunchKernelGGL(attn_gather_clusters_kernel, dim3(nwg), dim3(NT), 0, s, p, packs);
   return hipGetLastError();
 }
 

@@ -37,13 +37,17 @@ struct AttnParams {
   int kind;            // SWA, DENSE, TRIANGLE (band kernel) or RETRIEVAL (gather)
   int n_qt;            // query tiles of 64 rows
   // gather only
-  const int32_t* sel;  // [Hret, n_qb, topk]
+  const int32_t* sel;      // [Hret, n_qb, topk]
   int topk, force_block0;
+  const int32_t* csr_off;  // cluster mode: [Hkv, M+1]
+  const int32_t* csr_mem;  // cluster mode: [Hkv, N]
+  int M;
 };
 
 // Host launchers (each returns a hipError_t from the launch).
 hipError_t launch_attn_band(const AttnParams& p, const PackTable& packs, hipStream_t s);
 hipError_t launch_attn_gather_blocks(const AttnParams& p, const PackTable& packs, hipStream_t s);
+hipError_t launch_attn_gather_clusters(const AttnParams& p, const PackTable& packs, hipStream_t s);
 
 struct ProjParams {
   const uint16_t* X;   // bf16 [N, H, D]
@@ -68,6 +72,20 @@ struct SelectParams {
   int32_t group_of_ret[kMaxHeads];
 };
 hipError_t launch_select_blocks(const SelectParams& p, hipStream_t s);
+
+struct KmeansParams {
+  const float* klow;   // [Hkv, N, r]
+  float* cent;         // [Hkv, M, r]
+  int32_t* assign;     // [Hkv, N]
+  int32_t* csr_off;    // [Hkv, M+1]
+  int32_t* csr_mem;    // [Hkv, N]
+  int32_t* hist;       // scratch [Hkv, n_chunks, M]
+  int32_t* count;      // scratch [Hkv, M]
+  int N, M, stride, n_chunks;
+};
+size_t kmeans_scratch_bytes(int N, int M, int Hkv);
+hipError_t launch_kmeans(KmeansParams p, int Hkv, int iters, hipStream_t s);
+hipError_t launch_select_clusters(const SelectParams& p, hipStream_t s);
 
 struct CrossParams {
   const uint16_t* Q;

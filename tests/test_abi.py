@@ -102,6 +102,15 @@ def test_prefill_cluster_argument_checks():
     assert _prefill(_desc(topk=4, n_clusters=100, kmeans_iters=2, kmeans_stride=20), kinds) == ha.HA_ERR_ARG
     # iterations must be >= 1
     assert _prefill(_desc(topk=4, n_clusters=10, kmeans_iters=0, kmeans_stride=2), kinds) == ha.HA_ERR_ARG
+    # more clusters than the selection kernel scores in LDS
+    big = _desc(n_tokens=1 << 20, topk=4, n_clusters=20000, kmeans_iters=1, kmeans_stride=2)
+    assert _prefill(big, kinds) == ha.HA_ERR_UNSUPPORTED
+    L = ha.lib()
+    d = _desc(topk=4, n_clusters=10, kmeans_iters=2, kmeans_stride=2)
+    assert L.ha_kmeans(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == ha.HA_ERR_ARG
+    assert L.ha_kmeans(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == ha.HA_ERR_WORKSPACE
+    assert L.ha_select_clusters(ctypes.byref(d), ha._kinds(kinds), FAKE, FAKE, None, FAKE, FAKE, None, 0,
+                                None) == ha.HA_ERR_ARG
 
 
 def test_prefill_orthros_argument_checks():

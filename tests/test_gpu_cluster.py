@@ -1,0 +1,175 @@
+"""Cluster mode (k-means of the low-rank keys) on the GPU against the oracle.
+
+Staged, because fp32 and fp64 Lloyd trajectories may part at near-ties:
+  1. assignment of iteration t: the oracle's argmin over the GPU's centroids
+     of iteration t-1 must equal the GPU's, except where the exact distances
+     to the two centroids differ by <= 1e-5 (|k|^2 + |C|^2);
+  2. update: the oracle's means of the GPU's assignment match the GPU's
+     centroids within 1e-4;
+  3. CSR: bit-exact (members of each cluster in ascending position);
+  4. selection: tie band as in block mode; output graded with the GPU's
+     validated clusters and selection.
+"""
+import numpy as np
+import pytest
+import torch
+
+import hybrid_attention_prefill_amd as ha
+import synth
+from synth import inputs as si
+from oracle.kmeans import assign_step, update_step, sq_dist
+from oracle.indexer import cluster_scores, eligible_clusters
+from oracle.prefill import layer_prefill
+from tests import _gpu
+
+pytestmark = pytest.mark.gpu
+KM_REL = 1e-5
+CENT_ABS = 1e-4
+
+
+def _kmeans_gpu(w, klow, iters):
+    Hkv, N, M = w.n_kv_heads, w.n_tokens, w.n_clusters
+    d = ha.make_desc(N, w.n_q_heads, Hkv, w.head_dim, window=w.window, topk=w.topk, n_clusters=M,
+                     kmeans_iters=iters, kmeans_stride=w.kmeans_stride)
+    cent = torch.empty((Hkv, M, 16), dtype=torch.float32, device="cuda")
+    asg = torch.empty((Hkv, N), dtype=torch.int32, device="cuda")
+    off = torch.empty((Hkv, M + 1), dtype=torch.int32, device="cuda")
+    mem = torch.empty((Hkv, N), dtype=torch.int32, device="cuda")
+    ws = torch.empty(ha.ha_workspace_bytes(d, w.head_kind), dtype=torch.uint8, device="cuda")
+    ha.ha_kmeans(d, klow, cent, asg, off, mem, ws)
+    torch.cuda.synchronize()
+    return cent.cpu().numpy(), asg.cpu().numpy(), off.cpu().numpy(), mem.cpu().numpy()
+
+
+def check_assign(X, C, gpu_a, keys, what):
+    """Oracle argmin over the given centroids vs the GPU's, for the listed keys."""
+    X = X[keys].astype(np.float64)
+    C = C.astype(np.float64)
+    ora = assign_step(X, C)
+    ga = gpu_a[keys].astype(np.int64)
+    bad = np.nonzero(ora != ga)[0]
+    for t in bad:
+        dg = sq_dist(X[t:t + 1], C[ga[t]:ga[t] + 1])[0]
+        do = sq_dist(X[t:t + 1], C[ora[t]:ora[t] + 1])[0]
+        band = KM_REL * (np.dot(X[t], X[t]) + max(np.dot(C[ga[t]], C[ga[t]]), np.dot(C[ora[t]], C[ora[t]])))
+        assert abs(dg - do) <= band, f"{what}: key {keys[t]} GPU cluster {ga[t]} vs oracle {ora[t]} ({dg} vs {do})"
+    return bad.size
+
+
+def check_csr(a, off, mem, M, what):
+    N = a.size
+    cnt = np.bincount(a, minlength=M)
+    np.testing.assert_array_equal(off, np.r_[0, np.cumsum(cnt)], err_msg=what)
+    expect = np.lexsort((np.arange(N), a))       # by cluster, then position
+    np.testing.assert_array_equal(mem, expect, err_msg=what)
+
+
+def _kmeans_staged(w, li, iters, key_sample=None):
+    Q, K = _gpu.dev_bf16(li.Q) if li.Q is not None else None, _gpu.dev_bf16(li.K)
+    P = _gpu.dev_f32(li.P)
+    d = ha.make_desc(w.n_tokens, w.n_q_heads, w.n_kv_heads, w.head_dim, window=w.window, topk=w.topk)
+    klow = torch.empty((w.n_kv_heads, w.n_tokens, 16), dtype=torch.float32, device="cuda")
+    ha.ha_index_project(d, w.head_kind, None, K, P, None, klow)
+    torch.cuda.synchronize()
+    X = klow.cpu().numpy()
+    prev = None
+    for t in range(1, iters + 1):
+        C, a, off, mem = _kmeans_gpu(w, klow, t)
+        for g in range(w.n_kv_heads):
+            Cp = X[g][np.arange(w.n_clusters) * w.kmeans_stride] if prev is None else prev[0][g]
+            keys = np.arange(w.n_tokens) if key_sample is None else key_sample
+            nb = check_assign(X[g], Cp, a[g], keys, f"iter {t} kv {g}")
+            ref = update_step(X[g].astype(np.float64), a[g].astype(np.int64), Cp.astype(np.float64))
+            assert np.max(np.abs(ref - C[g])) <= CENT_ABS, f"iter {t} kv {g}: centroid update off"
+            check_csr(a[g], off[g], mem[g], w.n_clusters, f"iter {t} kv {g}")
+            print(f"iter {t} kv {g}: {nb} near-tie assignment differences")
+        prev = (C, a)
+    return X, prev
+
+
+def test_kmeans_small_every_iteration():
+    w = synth.configs.shrink(synth.WORKLOADS["allsparse_1m"], 8192, n_clusters=128, window=512, n_needles=4)
+    print(f"\n[case] kmeans N={w.n_tokens} M={w.n_clusters}", flush=True)
+    li = synth.make_layer_inputs(w, with_q=False)
+    _kmeans_staged(w, li, 4)
+
+
+def test_kmeans_degenerate_every_key_a_cluster():
+    w = synth.configs.shrink(synth.WORKLOADS["allsparse_1m"], 512, n_clusters=512, window=64, n_needles=0)
+    w = w.with_(kmeans_stride=1)
+    print(f"\n[case] kmeans identity N={w.n_tokens}", flush=True)
+    li = synth.make_layer_inputs(w, with_q=False)
+    X, (C, a) = _kmeans_staged(w, li, 2)
+    for g in range(w.n_kv_heads):
+        np.testing.assert_array_equal(a[g], np.arange(512))
+        np.testing.assert_array_equal(C[g], X[g])
+
+
+def test_kmeans_ragged_chunks_and_empty_clusters():
+    # N not a multiple of the histogram chunk; duplicated keys make some
+    # clusters empty after the first assignment (lowest-index rule).
+    w = synth.configs.shrink(synth.WORKLOADS["allsparse_1m"], 9000, n_clusters=300, window=256, n_needles=0)
+    w = w.with_(kmeans_stride=30)
+    print(f"\n[case] kmeans ragged N={w.n_tokens}", flush=True)
+    li = synth.make_layer_inputs(w, with_q=False)
+    li.K[30] = li.K[0]     # centroid seeds 0 and 1 coincide
+    _kmeans_staged(w, li, 3)
+
+
+def _layer_cluster(w, blocks=None):
+    print(f"\n[case] cluster layer {w.name} N={w.n_tokens} M={w.n_clusters} k={w.topk} w={w.window}", flush=True)
+    li = synth.make_layer_inputs(w)
+    O, _, aux = _gpu.run_gpu(w, li)
+    q_rows = lambda a, b: si.bf16_to_f64(li.Q[a:b])
+    K, V, P = si.bf16_to_f64(li.K), si.bf16_to_f64(li.V), li.P.astype(np.float64)
+    C = aux["centroids"].cpu().numpy()
+    asg = aux["assign"].cpu().numpy()
+    off = aux["csr_off"].cpu().numpy()
+    mem = aux["csr_mem"].cpu().numpy()
+    sel = aux["sel"].cpu().numpy()
+    for g in range(w.n_kv_heads):
+        check_csr(asg[g], off[g], mem[g], w.n_clusters, f"kv {g}")
+        # final centroids are the means of the final assignment
+        ref = update_step(aux["klow"][g].cpu().numpy().astype(np.float64), asg[g].astype(np.int64),
+                          C[g].astype(np.float64))
+        assert np.max(np.abs(ref - C[g])) <= CENT_ABS
+    km = {g: (C[g], asg[g]) for g in range(w.n_kv_heads)}
+    blocks = list(range(w.n_qb)) if blocks is None else blocks
+    ref = layer_prefill(w, q_rows, K, V, P, blocks=blocks, kmeans_override=km)
+    override = {}
+    nd = 0
+    for t, h in enumerate(w.ret_heads):
+        override[h] = {}
+        for b, (E, s) in ref.scored[h].items():
+            nd += _gpu.check_selection(sel[t, b], E, s, w.topk, f"head {h} block {b}")
+            override[h][b] = np.array([x for x in sel[t, b] if x >= 0], dtype=np.int64)
+    print(f"selection near-tie differences: {nd}")
+    ref = layer_prefill(w, q_rows, K, V, P, blocks=blocks, kmeans_override=km, sel_override=override)
+    mx, mean = _gpu.assert_close_out(O.cpu().numpy()[ref.rows], ref.O, w.name)
+    print(f"max abs {mx:.3e}, mean abs {mean:.3e}")
+    return li, O, ref
+
+
+@pytest.mark.parametrize("N,M,window,topk", [(4096, 64, 256, 4), (3000, 50, 100, 8), (5000, 128, 64, 0),
+                                             (2048, 32, 4096, 3), (2048, 128, 200, 200)])
+def test_cluster_layer_small(N, M, window, topk):
+    base = synth.WORKLOADS["allsparse_1m"]
+    w = synth.configs.shrink(base, N, n_clusters=M, window=window, n_needles=2)
+    w = w.with_(kmeans_stride=N // M if N // M >= 1 else 1, topk=topk, kmeans_iters=3)
+    _layer_cluster(w)
+
+
+def test_cluster_layer_mixed_with_swa_heads():
+    base = synth.WORKLOADS["allsparse_1m"]
+    kinds = tuple(1 if h % 3 == 0 else 0 for h in range(16))
+    w = synth.configs.shrink(base, 6000, n_clusters=96, window=300, n_needles=2)
+    w = w.with_(head_kind=kinds, kmeans_stride=62, topk=6, kmeans_iters=2)
+    _layer_cluster(w)
+
+
+def test_cluster_layer_reduced_allsparse_needles_found():
+    base = synth.WORKLOADS["allsparse_1m"]
+    w = synth.configs.shrink(base, 32768, n_clusters=512, window=1024, n_needles=16)
+    nd = si.needles(w)
+    blocks = sorted(set(int(r) // 64 for r in nd.q_row))[:12]
+    li, O, ref = _layer_cluster(w, blocks=blocks)
