@@ -83,7 +83,40 @@ def pairs_retrieval_blocks(N, w, sel_rows, f0, Bk=64, Bq=64):
     return total
 
 
-def layer_work(w, sel=None):
+def pairs_retrieval_clusters(N, w, sel_rows, csr_off, csr_mem, Bq=64):
+    """Pairs of one retrieval head in cluster mode: window + members j <= i-w
+    of the selected clusters, from the CSR (members ascending per cluster).
+    For rows [qs, qe] of a block and a cluster with C(x) = #members <= x and
+    S(x) = sum of members <= x:
+      pairs = n*C(qs-w) + (qe-w+1)*(C(qe-w) - C(qs-w)) - (S(qe-w) - S(qs-w))."""
+    total = pairs_swa(N, w)
+    n_qb, k = sel_rows.shape
+    M = csr_off.size - 1
+    clus = np.repeat(np.arange(M, dtype=np.int64), np.diff(csr_off))
+    keyv = clus * (N + 1) + csr_mem.astype(np.int64)          # ascending
+    csum = np.r_[0, np.cumsum(csr_mem.astype(np.int64))]
+    b = np.repeat(np.arange(n_qb, dtype=np.int64), k)
+    m = sel_rows.reshape(-1).astype(np.int64)
+    ok = m >= 0
+    b, m = b[ok], m[ok]
+    qs = b * Bq
+    qe = np.minimum(N, qs + Bq) - 1
+    n = qe - qs + 1
+
+    def CS(x):
+        xx = np.maximum(x, -1)
+        pos = np.searchsorted(keyv, m * (N + 1) + xx, side="right")
+        lo = csr_off[m]
+        pos = np.maximum(pos, lo)
+        return pos - lo, csum[pos] - csum[lo]
+
+    c1, s1 = CS(qs - w)
+    c2, s2 = CS(qe - w)
+    total += int((n * c1 + (qe - w + 1) * (c2 - c1) - (s2 - s1)).sum())
+    return total
+
+
+def layer_work(w, sel=None, csr=None):
     """(actual attention pairs, dense-equivalent pairs) summed over heads."""
     N = w.n_tokens
     act = 0
@@ -96,7 +129,11 @@ def layer_work(w, sel=None):
             act += pairs_triangle(N, w.sink, w.window, w.last_q)
         else:
             t = w.ret_heads.index(h)
-            act += pairs_retrieval_blocks(N, w.window, sel[t], w.force_block0)
+            if w.n_clusters:
+                g = h // (w.n_q_heads // w.n_kv_heads)
+                act += pairs_retrieval_clusters(N, w.window, sel[t], csr[0][g], csr[1][g])
+            else:
+                act += pairs_retrieval_blocks(N, w.window, sel[t], w.force_block0)
     act += w.n_out * w.n_q_heads * N
     return act, w.n_q_heads * pairs_dense(N)
 
@@ -303,11 +340,9 @@ def main():
     tot_act = tot_dense = 0.0
     for L in layers:
         w = L.w
-        sel = L.sel.cpu().numpy() if w.ret_heads and not w.n_clusters else None
-        if w.n_clusters:
-            act, dense = None, w.n_q_heads * pairs_dense(w.n_tokens)
-        else:
-            act, dense = layer_work(w, sel)
+        sel = L.sel.cpu().numpy() if w.ret_heads else None
+        csr = (L.csr_off.cpu().numpy(), L.csr_mem.cpu().numpy()) if w.n_clusters else None
+        act, dense = layer_work(w, sel, csr)
         ms = float(sum(stage_ms[t] for t, (LL, _, _) in enumerate(plan) if LL is L))
         stg = {name: round(float(stage_ms[t]), 4) for t, (LL, name, _) in enumerate(plan) if LL is L}
         fl_act = None if act is None else 4.0 * w.head_dim * act

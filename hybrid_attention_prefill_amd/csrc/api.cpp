@@ -61,6 +61,7 @@ int check_desc(const ha_layer_desc* d, const int32_t* kinds, Heads* out) {
       if (d->kmeans_iters < 1 || d->kmeans_stride < 1) return HA_ERR_ARG;
       if ((int64_t)d->n_clusters * d->kmeans_stride > d->n_tokens) return HA_ERR_ARG;
       if (d->n_clusters > kMaxSelCand) return HA_ERR_UNSUPPORTED;
+      if (d->force_block0) return HA_ERR_UNSUPPORTED;   // block 0 is a block-mode rule
     } else {
       const int n_kb = (d->n_tokens + kBlock - 1) / kBlock;
       if (n_kb > kMaxSelCand) return HA_ERR_UNSUPPORTED;
@@ -74,7 +75,7 @@ inline int n_qb_of(const ha_layer_desc* d) { return (d->n_tokens + kBlock - 1) /
 inline int n_cross_chunks(const ha_layer_desc* d) { return (d->n_tokens + kCrossChunk - 1) / kCrossChunk; }
 
 struct Layout {
-  size_t qlow, klow, sel, cent, assign, csr_off, csr_mem, km_scratch, cross, total;
+  size_t qlow, klow, sel, lse, cent, assign, csr_off, csr_mem, km_scratch, cross, total;
 };
 
 Layout layout_of(const ha_layer_desc* d, const Heads& h) {
@@ -87,6 +88,8 @@ Layout layout_of(const ha_layer_desc* d, const Heads& h) {
   off += Hret ? align_up((size_t)d->n_kv_heads * N * kRank * sizeof(float)) : 0;
   L.sel = off;
   off += align_up(Hret * (size_t)n_qb_of(d) * (size_t)std::max(0, d->topk) * sizeof(int32_t));
+  L.lse = off;
+  off += align_up(Hret * N * sizeof(float));
   const size_t M = (Hret && d->n_clusters > 0) ? (size_t)d->n_clusters : 0, Hkv = (size_t)d->n_kv_heads;
   L.cent = off;
   off += align_up(Hkv * M * kRank * sizeof(float));
@@ -97,7 +100,9 @@ Layout layout_of(const ha_layer_desc* d, const Heads& h) {
   L.csr_mem = off;
   off += M ? align_up(Hkv * N * sizeof(int32_t)) : 0;
   L.km_scratch = off;
-  off += M ? align_up(kmeans_scratch_bytes(d->n_tokens, (int)M, d->n_kv_heads)) : 0;
+  off += M ? align_up(std::max(kmeans_scratch_bytes(d->n_tokens, (int)M, d->n_kv_heads),
+                               select_clusters_scratch_bytes((int)M, d->n_kv_heads)))
+           : 0;
   L.cross = off;
   off += align_up((size_t)d->n_out * d->n_q_heads * (size_t)n_cross_chunks(d) * (kHeadDim + 2) * sizeof(float));
   L.total = off;
@@ -226,22 +231,30 @@ int run_select_blocks(const ha_layer_desc* d, const Heads& h, const float* qlow,
   return dev_status(launch_select_blocks(sp, s));
 }
 
+// Retrieval heads: the window part through the banded kernel (which also
+// leaves each row's log2-sum-exp), then the selected keys, merged in.
 int run_gather(const ha_layer_desc* d, const int32_t* kinds, const Heads& h, const void* Q, const void* K,
                const void* V, const int32_t* sel, const int32_t* csr_off, const int32_t* csr_mem, float* O,
-               hipStream_t s) {
+               float* lse, hipStream_t s) {
   if (h.ret.empty()) return HA_OK;
   AttnParams p = attn_params(d, Q, K, V, O);
-  p.kind = RETRIEVAL;
-  p.sel = sel;
+  p.kind = SWA;
+  p.lse = lse;
   PackTable pt;
   build_packs(d, kinds, RETRIEVAL, h.ret_slot, &pt);
+  int st = dev_status(launch_attn_band(p, pt, s));
+  if (st != HA_OK) return st;
+  p.kind = RETRIEVAL;
+  p.sel = sel;
   if (d->n_clusters > 0) {
     p.csr_off = csr_off;
     p.csr_mem = csr_mem;
     p.M = d->n_clusters;
-    return dev_status(launch_attn_gather_clusters(p, pt, s));
   }
-  return dev_status(launch_attn_gather_blocks(p, pt, s));
+  SelList sl;
+  sl.n_ret = (int)h.ret.size();
+  for (int t = 0; t < sl.n_ret; ++t) sl.head[t] = h.ret[t];
+  return dev_status(launch_attn_selected(p, sl, s));
 }
 
 int run_kmeans(const ha_layer_desc* d, const float* klow, float* cent, int32_t* assign, int32_t* csr_off,
@@ -255,15 +268,21 @@ int run_kmeans(const ha_layer_desc* d, const float* klow, float* cent, int32_t* 
   kp.N = d->n_tokens;
   kp.M = d->n_clusters;
   kp.stride = d->kmeans_stride;
+  const size_t Hkv = (size_t)d->n_kv_heads, M = (size_t)d->n_clusters;
+  const size_t n_chunks = ((size_t)d->n_tokens + 8191) / 8192;
   kp.hist = static_cast<int32_t*>(scratch);
-  const size_t n_chunks_m = kmeans_scratch_bytes(d->n_tokens, d->n_clusters, d->n_kv_heads) / sizeof(int32_t) -
-                            (size_t)d->n_kv_heads * d->n_clusters;
-  kp.count = kp.hist + n_chunks_m;
+  kp.count = kp.hist + Hkv * n_chunks * M;
+  kp.c_norm = reinterpret_cast<float*>(kp.count + Hkv * M);
+  // 16-byte vector loads read the split centroids: start them on an aligned address
+  kp.c_hi = reinterpret_cast<__bf16*>(align_up(reinterpret_cast<uintptr_t>(kp.c_norm + Hkv * M)));
+  kp.c_mid = kp.c_hi + Hkv * M * kRank;
+  kp.c_lo = kp.c_mid + Hkv * M * kRank;
   return dev_status(launch_kmeans(kp, d->n_kv_heads, d->kmeans_iters, s));
 }
 
 int run_select_clusters(const ha_layer_desc* d, const Heads& h, const float* qlow, const float* cent,
-                        const int32_t* csr_off, const int32_t* csr_mem, int32_t* sel, hipStream_t s) {
+                        const int32_t* csr_off, const int32_t* csr_mem, int32_t* sel, void* scratch,
+                        hipStream_t s) {
   const int G = d->n_q_heads / d->n_kv_heads;
   SelectParams sp{};
   sp.qlow = qlow;
@@ -278,7 +297,11 @@ int run_select_clusters(const ha_layer_desc* d, const Heads& h, const float* qlo
   sp.M = d->n_clusters;
   sp.n_ret = (int)h.ret.size();
   for (int t = 0; t < sp.n_ret; ++t) sp.group_of_ret[t] = h.ret[t] / G;
-  return dev_status(launch_select_clusters(sp, s));
+  const size_t nparts = (size_t)d->n_kv_heads * d->n_clusters * kRank;
+  sp.c_hi = static_cast<__bf16*>(scratch);
+  sp.c_lo = sp.c_hi + nparts;
+  sp.first_mem = reinterpret_cast<int32_t*>(sp.c_lo + nparts);
+  return dev_status(launch_select_clusters(sp, d->n_kv_heads, s));
 }
 
 int run_cross(const ha_layer_desc* d, const void* Q, const void* K, const void* V, const float* xs,
@@ -364,7 +387,7 @@ int ha_prefill(const ha_layer_desc* desc, const int32_t* head_kind, const void* 
       int32_t* cm = (aux && aux->csr_mem) ? aux->csr_mem : reinterpret_cast<int32_t*>(ws_at(workspace, L.csr_mem));
       st = run_kmeans(desc, klow, cent, asg, co, cm, ws_at(workspace, L.km_scratch), s);
       if (st != HA_OK) return st;
-      st = run_select_clusters(desc, h, qlow, cent, co, cm, sel, s);
+      st = run_select_clusters(desc, h, qlow, cent, co, cm, sel, ws_at(workspace, L.km_scratch), s);
       if (st != HA_OK) return st;
       off = co;
       mem = cm;
@@ -372,7 +395,8 @@ int ha_prefill(const ha_layer_desc* desc, const int32_t* head_kind, const void* 
       st = run_select_blocks(desc, h, qlow, klow, sel, s);
       if (st != HA_OK) return st;
     }
-    st = run_gather(desc, head_kind, h, Q, K, V, sel, off, mem, O, s);
+    st = run_gather(desc, head_kind, h, Q, K, V, sel, off, mem, O, reinterpret_cast<float*>(ws_at(workspace, L.lse)),
+                    s);
     if (st != HA_OK) return st;
   }
   if (h.any_band) {
@@ -424,13 +448,15 @@ int ha_kmeans(const ha_layer_desc* desc, const float* klow, float* centroids, in
 int ha_select_clusters(const ha_layer_desc* desc, const int32_t* head_kind, const float* qlow,
                        const float* centroids, const int32_t* csr_off, const int32_t* csr_mem, int32_t* sel,
                        void* workspace, size_t ws_bytes, void* stream) {
-  (void)workspace; (void)ws_bytes;
   Heads h;
   int st = check_desc(desc, head_kind, &h);
   if (st != HA_OK) return st;
   if (h.ret.empty() || desc->n_clusters < 1) return HA_ERR_ARG;
   if (!qlow || !centroids || !csr_off || !csr_mem || !sel) return HA_ERR_ARG;
-  return run_select_clusters(desc, h, qlow, centroids, csr_off, csr_mem, sel, static_cast<hipStream_t>(stream));
+  if (!ws_ok(workspace, ws_bytes, align_up(select_clusters_scratch_bytes(desc->n_clusters, desc->n_kv_heads))))
+    return HA_ERR_WORKSPACE;
+  return run_select_clusters(desc, h, qlow, centroids, csr_off, csr_mem, sel, workspace,
+                             static_cast<hipStream_t>(stream));
 }
 
 int ha_attn_band(const ha_layer_desc* desc, const int32_t* head_kind, const void* Q, const void* K, const void* V,
@@ -446,14 +472,16 @@ int ha_attn_band(const ha_layer_desc* desc, const int32_t* head_kind, const void
 int ha_attn_gather(const ha_layer_desc* desc, const int32_t* head_kind, const void* Q, const void* K,
                    const void* V, const int32_t* sel, const int32_t* csr_off, const int32_t* csr_mem, float* O,
                    void* workspace, size_t ws_bytes, void* stream) {
-  (void)workspace; (void)ws_bytes;
   Heads h;
   int st = check_desc(desc, head_kind, &h);
   if (st != HA_OK) return st;
   if (h.ret.empty()) return HA_ERR_ARG;
   if (!Q || !K || !V || !O || (desc->topk > 0 && !sel)) return HA_ERR_ARG;
   if (desc->n_clusters > 0 && (!csr_off || !csr_mem)) return HA_ERR_ARG;
-  return run_gather(desc, head_kind, h, Q, K, V, sel, csr_off, csr_mem, O, static_cast<hipStream_t>(stream));
+  const size_t need = align_up(h.ret.size() * (size_t)desc->n_tokens * sizeof(float));
+  if (!ws_ok(workspace, ws_bytes, need)) return HA_ERR_WORKSPACE;
+  return run_gather(desc, head_kind, h, Q, K, V, sel, csr_off, csr_mem, O, static_cast<float*>(workspace),
+                    static_cast<hipStream_t>(stream));
 }
 
 int ha_attn_cross(const ha_layer_desc* desc, const void* Q, const void* K, const void* V, const float* xa_scale,

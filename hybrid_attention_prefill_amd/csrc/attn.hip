@@ -1,5 +1,6 @@
-// Flash attention for gfx950: banded / dense / TriangleMix heads and
-// retrieval heads (window + indexer-selected key blocks).
+// Flash attention for gfx950: banded / dense / TriangleMix heads, and the
+// local-window part of retrieval heads (with a per-row log2-sum-exp so the
+// selected-key part can be merged in afterwards).
 //
 // The attention itself is exact softmax over each query's key set (RTPurbo
 // post: exact attention on the selected candidates in full dimension; the
@@ -41,6 +42,7 @@ constexpr int SMEM_ELEMS = 2 * BUF_ELEMS + 4 * Q_ELEMS;
 constexpr int NT = 256;
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kMInit = -1e30f;     // finite start for the running max
+constexpr float kSlack = 8.f;        // log2 headroom before the reference max moves
 
 // visible(i, j) = j <= i - a  &&  (i - j < b  ||  j < sink  ||  i >= dense_from)
 struct MaskSpec {
@@ -142,16 +144,14 @@ __device__ __forceinline__ bool tile_full(const MaskSpec& ms, int q0, int k0) {
 
 // One 64-key tile against the wave's 64 query rows, as two 32-key halves
 // (each half is one online-softmax step; this keeps 32 score registers live).
-// GATHER: the tile's keys are arbitrary positions kpos[0..64) (-1 = empty
-// slot); otherwise keys k0 .. k0+63.
-template <bool GATHER>
+// The tile's keys are k0 .. k0+63.
 __device__ __forceinline__ void tile_compute(const uint16_t* __restrict__ buf, const uint16_t* __restrict__ Qs,
-                                             const int* __restrict__ kpos, WaveAcc& acc, int lane, int q0,
-                                             int k0, const MaskSpec& ms, float c) {
+                                             WaveAcc& acc, int lane, int q0, int k0, const MaskSpec& ms,
+                                             float c) {
   const uint16_t* Ks = buf;
   const uint16_t* Vt = buf + K_ELEMS;
   const int lr = lane & 31, lh = lane >> 5;
-  const bool full = !GATHER && tile_full(ms, q0, k0);
+  const bool full = tile_full(ms, q0, k0);
 
   // S^T = K Q^T for the 64 x 64 tile: [key half][query half]
   f32x16 s[2][2];
@@ -182,18 +182,20 @@ __device__ __forceinline__ void tile_compute(const uint16_t* __restrict__ buf, c
       for (int qb = 0; qb < 2; ++qb) {
         const int i = q0 + qb * 32 + lr;
         const bool dense_row = i >= ms.dense_from;
+        const int dd = i - jb;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int slot = kb * 32 + lh * 4 + (e >> 2) * 8 + (e & 3);
-          const int j = GATHER ? kpos[slot] : jb + (e >> 2) * 8 + (e & 3);
-          const int d = i - j;
-          bool vis = (d >= ms.a) && (d < ms.b || j < ms.sink || dense_row);
-          if (GATHER) vis = vis && j >= 0;
-          if (!vis) s[kb][qb][e] = kNegInf;
+          const int off = (e >> 2) * 8 + (e & 3);
+          const int d = dd - off;
+          const bool vis = (d >= ms.a) & ((d < ms.b) | (jb + off < ms.sink) | dense_row);
+          s[kb][qb][e] = vis ? s[kb][qb][e] : kNegInf;
         }
       }
     }
 
+    // Online softmax with a lazily moved reference max: the exponent base m
+    // only changes when a row max exceeds it by more than kSlack (log2
+    // units), so P <= 2^kSlack and the accumulator rescale is rare.
     bf16x8 pf[2][2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -201,22 +203,23 @@ __device__ __forceinline__ void tile_compute(const uint16_t* __restrict__ buf, c
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][qb][e]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(acc.m[qb], mx);
-      const float alpha = exp2f((acc.m[qb] - mnew) * c);
-      acc.m[qb] = mnew;
-      const float nb = -mnew * c;
-      float sum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float pv = exp2f(fmaf(s[kb][qb][e], c, nb));
-        s[kb][qb][e] = pv;
-        sum += pv;
-      }
-      acc.l[qb] = acc.l[qb] * alpha + sum;
-      if (__any(alpha != 1.f)) {
+      if (__any((mx - acc.m[qb]) * c > kSlack)) {
+        const float mnew = fmaxf(acc.m[qb], mx);
+        const float alpha = __builtin_amdgcn_exp2f((acc.m[qb] - mnew) * c);
+        acc.m[qb] = mnew;
+        acc.l[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < 4; ++db) acc.o[qb][db] *= alpha;
       }
+      const float nb = -acc.m[qb] * c;
+      float sum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][e], c, nb));
+        s[kb][qb][e] = pv;
+        sum += pv;
+      }
+      acc.l[qb] += sum;
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
@@ -262,8 +265,8 @@ __device__ __forceinline__ void acc_init(WaveAcc& acc) {
   }
 }
 
-__device__ __forceinline__ void store_o(const WaveAcc& acc, float* __restrict__ O, int N, int Hq, int h,
-                                        int q0, int lane) {
+__device__ __forceinline__ void store_o(const WaveAcc& acc, float* __restrict__ O, float* __restrict__ lse,
+                                        int slot, int N, int Hq, int h, int q0, int lane, float c) {
   const int lr = lane & 31, lh = lane >> 5;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
@@ -271,6 +274,7 @@ __device__ __forceinline__ void store_o(const WaveAcc& acc, float* __restrict__ 
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const int i = q0 + qb * 32 + lr;
     if (i >= N) continue;
+    if (lse != nullptr && lh == 0) lse[(size_t)slot * N + i] = acc.m[qb] * c + __log2f(lt);
     float* row = O + ((size_t)i * Hq + h) * D;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -286,21 +290,11 @@ __device__ __forceinline__ void store_o(const WaveAcc& acc, float* __restrict__ 
   }
 }
 
-struct TileDesc {
-  int k0;          // first key (contiguous tiles)
-  MaskSpec ms;
-  bool on;         // this wave computes the tile
-  bool gather;     // keys are looked up; positions in the row ring
-};
-
-// Shared pipeline over T tiles.  info(idx) describes tile idx.  For gathered
-// tiles, lookup(idx, slot) returns the key row of a slot (-1 = empty); the 64
-// slots of tile t+2 are looked up by threads 0..63 while tile t is computed
-// and tile t+1 is in flight, and parked in a 3-entry LDS ring (rows[3][64]),
-// which also serves as the key positions of the tile for masking.
-template <bool ALL_GATHER = false, class Info, class Lookup>
-__device__ __forceinline__ void run_tiles(const AttnParams& p, uint16_t* smem, int (*rows)[BK], int T, int g,
-                                          int h, bool active, int q0, Info&& info, Lookup&& lookup) {
+// Shared pipeline over T tiles; k0_of(idx) is the first key of tile idx.
+// Tile t+1 is in flight (registers) while tile t is computed from LDS.
+template <class K0Of>
+__device__ __forceinline__ void run_tiles(const AttnParams& p, uint16_t* smem, int T, int g, int h, int slot,
+                                          bool active, int q0, const MaskSpec& ms, K0Of&& k0_of) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const size_t rs = (size_t)p.Hkv * D;
   uint16_t* Qs = smem + 2 * BUF_ELEMS + wave * Q_ELEMS;
@@ -308,56 +302,25 @@ __device__ __forceinline__ void run_tiles(const AttnParams& p, uint16_t* smem, i
   acc_init(acc);
   if (active) load_q_lds(Qs, p.Q, p.N, p.Hq, h, q0, lane);
 
-  auto rows_for = [&](int idx, const TileDesc& d, int(&rr)[8]) {
-    if (ALL_GATHER) {
-      const int* ring = rows[idx % 3];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) rr[c] = ring[k_slot(c, tid)];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) rr[4 + x] = ring[v_slot(x, tid)];
-    } else {
-      contiguous_rows(rr, d.k0, p.N, tid);
-    }
-  };
-  if (ALL_GATHER && tid < BK) {
-    if (T > 0) rows[0][tid] = lookup(0, tid);
-    if (T > 1) rows[1][tid] = lookup(1, tid);
-  }
-  __syncthreads();
   TileRegs r;
-  TileDesc cur = info(0);
-  {
-    int rr[8];
-    rows_for(0, cur, rr);
-    tile_load(r, p.K, p.V, rr, rs, g, tid);
-    tile_store(r, smem, tid);
-  }
+  int rows[8];
+  int k0 = k0_of(0);
+  contiguous_rows(rows, k0, p.N, tid);
+  tile_load(r, p.K, p.V, rows, rs, g, tid);
+  tile_store(r, smem, tid);
   __syncthreads();
   for (int t = 0; t < T; ++t) {
-    TileDesc nxt = cur;
-    int pending = -1;
-    const bool have_next = t + 1 < T;
-    if (have_next) {
-      nxt = info(t + 1);
-      int rr[8];
-      rows_for(t + 1, nxt, rr);
-      tile_load(r, p.K, p.V, rr, rs, g, tid);
+    const int cur = k0;
+    if (t + 1 < T) {
+      k0 = k0_of(t + 1);
+      contiguous_rows(rows, k0, p.N, tid);
+      tile_load(r, p.K, p.V, rows, rs, g, tid);
     }
-    const bool prep = ALL_GATHER && t + 2 < T && tid < BK;
-    if (prep) pending = lookup(t + 2, tid);
-    if (active && cur.on) {
-      const uint16_t* buf = smem + (t & 1) * BUF_ELEMS;
-      if (ALL_GATHER)
-        tile_compute<true>(buf, Qs, rows[t % 3], acc, lane, q0, cur.k0, cur.ms, p.c);
-      else
-        tile_compute<false>(buf, Qs, nullptr, acc, lane, q0, cur.k0, cur.ms, p.c);
-    }
-    if (have_next) tile_store(r, smem + ((t + 1) & 1) * BUF_ELEMS, tid);
-    if (prep) rows[(t + 2) % 3][tid] = pending;
-    cur = nxt;
+    if (active) tile_compute(smem + (t & 1) * BUF_ELEMS, Qs, acc, lane, q0, cur, ms, p.c);
+    if (t + 1 < T) tile_store(r, smem + ((t + 1) & 1) * BUF_ELEMS, tid);
     __syncthreads();
   }
-  if (active) store_o(acc, p.O, p.N, p.Hq, h, q0, lane);
+  if (active) store_o(acc, p.O, p.lse, slot, p.N, p.Hq, h, q0, lane, p.c);
 }
 
 __global__ __launch_bounds__(NT, 1) void attn_band_kernel(AttnParams p, PackTable packs) {
@@ -389,187 +352,9 @@ __global__ __launch_bounds__(NT, 1) void attn_band_kernel(AttnParams p, PackTabl
     }
   }
   const int T = st + (hi_t - bl + 1);
-  auto k0_of = [&](int idx) { return (idx < st ? idx : bl + idx - st) * BK; };
-  run_tiles(
-      p, smem, nullptr, T, g, h, active, q0,
-      [&](int idx) { return TileDesc{k0_of(idx), ms, true, false}; }, [](int, int) { return -1; });
-}
-
-// Retrieval heads, block mode: tiles = forced block 0 + the union of the pack's
-// selected blocks (each wave computes only its own) + the window tiles.
-// A selected block contributes only keys outside the window (j <= i - w), the
-// window tiles only keys inside it, so every key of the union is counted once.
-__global__ __launch_bounds__(NT, 1) void attn_gather_blocks_kernel(AttnParams p, PackTable packs) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM_ELEMS];
-  __shared__ int32_t sel_s[4][kMaxTopk];
-  __shared__ int32_t list_s[4 * kMaxTopk + 1];   // (block << 4) | wave mask
-  __shared__ int32_t n_list;
-
-  const int tid = threadIdx.x, wave = tid >> 6;
-  const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int pk = lid / p.n_qt;
-  const int qt = p.n_qt - 1 - (lid % p.n_qt);
-  const uint32_t pw = packs.heads[pk];
-  const uint32_t sw = packs.slots[pk];
-  const int h = (pw >> (8 * wave)) & 0xFF;
-  const bool active = h != 0xFF;
-  const int g = (int)(pw & 0xFF) / p.G;
-  const int q0 = qt * BK;
-  const int n_kb = (p.N + BK - 1) / BK;
-
-  for (int x = tid; x < 4 * p.topk; x += NT) {
-    const int w = x / p.topk, e = x % p.topk;
-    const int hw = (pw >> (8 * w)) & 0xFF;
-    int v = -1;
-    if (hw != 0xFF) {
-      const int slot = (sw >> (8 * w)) & 0xFF;
-      v = p.sel[((size_t)slot * p.n_qt + qt) * p.topk + e];
-      if (v < 0 || v >= n_kb || (p.force_block0 && v == 0)) v = -1;
-    }
-    sel_s[w][e] = v;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int n = 0;
-    if (p.force_block0) list_s[n++] = (0 << 4) | 0xF;
-    int cur[4] = {0, 0, 0, 0};
-    for (;;) {
-      int best = INT_MAX;
-      for (int w = 0; w < 4; ++w) {
-        while (cur[w] < p.topk && sel_s[w][cur[w]] < 0) ++cur[w];
-        if (cur[w] < p.topk) best = min(best, sel_s[w][cur[w]]);
-      }
-      if (best == INT_MAX) break;
-      int mask = 0;
-      for (int w = 0; w < 4; ++w)
-        if (cur[w] < p.topk && sel_s[w][cur[w]] == best) {
-          mask |= 1 << w;
-          ++cur[w];
-        }
-      list_s[n++] = (best << 4) | mask;
-    }
-    n_list = n;
-  }
-  __syncthreads();
-  const int nl = n_list;
-  const int hi_t = min(p.N - 1, q0 + 63) >> 6;
-  const int bl = max(0, q0 - p.window + 1) >> 6;
-  const int T = nl + (hi_t - bl + 1);
-  const MaskSpec win = {0, p.window, 0, INT_MAX};
-  const MaskSpec out = {p.window, INT_MAX, 0, INT_MAX};
-  auto k0_of = [&](int idx) { return idx < nl ? (list_s[idx] >> 4) * BK : (bl + idx - nl) * BK; };
-  run_tiles(
-      p, smem, nullptr, T, g, h, active, q0,
-      [&](int idx) {
-        if (idx < nl) return TileDesc{k0_of(idx), out, ((list_s[idx] >> wave) & 1) != 0, false};
-        return TileDesc{k0_of(idx), win, true, false};
-      },
-      [](int, int) { return -1; });
-}
-
-// Retrieval heads, cluster mode: tiles = the window tiles (shared by the
-// pack) followed, head by head, by the members of that head's selected
-// clusters that some row of the block may see (j <= qe - window), 64 per tile
-// in (cluster, position) order; only the owning wave computes those tiles.
-// A member contributes only to rows with j <= i - w (outside the window).
-__global__ __launch_bounds__(NT, 1) void attn_gather_clusters_kernel(AttnParams p, PackTable packs) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM_ELEMS];
-  __shared__ int ring_s[3][BK];
-  __shared__ int lo_s[4][kMaxTopk];
-  __shared__ int pre_s[4][kMaxTopk + 1];
-  __shared__ int ntile_s[4];
-
-  const int tid = threadIdx.x, wave = tid >> 6;
-  const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int pk = lid / p.n_qt;
-  const int qt = p.n_qt - 1 - (lid % p.n_qt);
-  const uint32_t pw = packs.heads[pk];
-  const uint32_t sw = packs.slots[pk];
-  const int h = (pw >> (8 * wave)) & 0xFF;
-  const bool active = h != 0xFF;
-  const int g = (int)(pw & 0xFF) / p.G;
-  const int q0 = qt * BK;
-  const int lim = min(p.N, q0 + BK) - 1 - p.window;   // members j <= lim can be visible
-  const int32_t* off = p.csr_off + (size_t)g * (p.M + 1);
-  const int32_t* mem = p.csr_mem + (size_t)g * p.N;
-
-  // member counts of every selected cluster (binary search for j <= lim)
-  for (int x = tid; x < 4 * p.topk; x += NT) {
-    const int w = x / p.topk, e = x % p.topk;
-    const int hw = (pw >> (8 * w)) & 0xFF;
-    int lo = 0, cnt = 0;
-    if (hw != 0xFF && lim >= 0) {
-      const int slot = (sw >> (8 * w)) & 0xFF;
-      const int m = p.sel[((size_t)slot * p.n_qt + qt) * p.topk + e];
-      if (m >= 0 && m < p.M) {
-        lo = off[m];
-        int a = lo, b = off[m + 1];
-        while (a < b) {
-          const int mid = (a + b) >> 1;
-          if (mem[mid] <= lim) a = mid + 1;
-          else b = mid;
-        }
-        cnt = a - lo;
-      }
-    }
-    lo_s[w][e] = lo;
-    pre_s[w][e + 1] = cnt;
-  }
-  __syncthreads();
-  if (tid < 4) {
-    int run = 0;
-    pre_s[tid][0] = 0;
-    for (int e = 0; e < p.topk; ++e) {
-      run += pre_s[tid][e + 1];
-      pre_s[tid][e + 1] = run;
-    }
-    ntile_s[tid] = (run + BK - 1) / BK;
-  }
-  __syncthreads();
-  const int hi_t = min(p.N - 1, q0 + 63) >> 6;
-  const int bl = max(0, q0 - p.window + 1) >> 6;
-  const int nwin = hi_t - bl + 1;
-  const int nt0 = ntile_s[0], nt1 = ntile_s[1], nt2 = ntile_s[2], nt3 = ntile_s[3];
-  const int T = nwin + nt0 + nt1 + nt2 + nt3;
-  const MaskSpec win = {0, p.window, 0, INT_MAX};
-  const MaskSpec out = {p.window, INT_MAX, 0, INT_MAX};
-  auto owner = [&](int idx, int& lt) {
-    int x = idx - nwin;
-    if (x < nt0) { lt = x; return 0; }
-    x -= nt0;
-    if (x < nt1) { lt = x; return 1; }
-    x -= nt1;
-    if (x < nt2) { lt = x; return 2; }
-    lt = x - nt2;
-    return 3;
-  };
-  // every tile goes through the lookup path (window tiles too), so the
-  // kernel holds a single instantiation of the tile computation
-  run_tiles<true>(
-      p, smem, ring_s, T, g, h, active, q0,
-      [&](int idx) {
-        if (idx < nwin) return TileDesc{(bl + idx) * BK, win, true, true};
-        int lt;
-        const int w = owner(idx, lt);
-        return TileDesc{0, out, w == wave, true};
-      },
-      [&](int idx, int slot) {
-        if (idx < nwin) {
-          const int j = (bl + idx) * BK + slot;
-          return j < p.N ? j : -1;
-        }
-        int lt;
-        const int w = owner(idx, lt);
-        const int f = lt * BK + slot;
-        if (f >= pre_s[w][p.topk]) return -1;
-        int a = 0, b = p.topk;          // largest e with pre[e] <= f
-        while (b - a > 1) {
-          const int mid = (a + b) >> 1;
-          if (pre_s[w][mid] <= f) a = mid;
-          else b = mid;
-        }
-        return (int)mem[lo_s[w][a] + (f - pre_s[w][a])];
-      });
+  const int slot = (packs.slots[pk] >> (8 * wave)) & 0xFF;
+  run_tiles(p, smem, T, g, h, slot, active, q0, ms,
+            [&](int idx) { return (idx < st ? idx : bl + idx - st) * BK; });
 }
 
 }  // namespace
@@ -578,20 +363,6 @@ hipError_t launch_attn_band(const AttnParams& p, const PackTable& packs, hipStre
   const int nwg = packs.n * p.n_qt;
   if (nwg == 0) return hipSuccess;
   hipLaunchKernelGGL(attn_band_kernel, dim3(nwg), dim3(NT), 0, s, p, packs);
-  return hipGetLastError();
-}
-
-hipError_t launch_attn_gather_blocks(const AttnParams& p, const PackTable& packs, hipStream_t s) {
-  const int nwg = packs.n * p.n_qt;
-  if (nwg == 0) return hipSuccess;
-  hipLaunchKernelGGL(attn_gather_blocks_kernel, dim3(nwg), dim3(NT), 0, s, p, packs);
-  return hipGetLastError();
-}
-
-hipError_t launch_attn_gather_clusters(const AttnParams& p, const PackTable& packs, hipStream_t s) {
-  const int nwg = packs.n * p.n_qt;
-  if (nwg == 0) return hipSuccess;
-  hipLaunchKernelGGL(attn_gather_clusters_kernel, dim3(nwg), dim3(NT), 0, s, p, packs);
   return hipGetLastError();
 }
 

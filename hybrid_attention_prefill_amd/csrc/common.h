@@ -12,7 +12,7 @@ constexpr int kHeadDim = 128;   // D
 constexpr int kRank = 16;       // r
 constexpr int kBlock = 64;      // q_block = k_block
 constexpr int kMaxHeads = 256;  // Hq limit (packs fit in a kernel argument)
-constexpr int kMaxTopk = 256;   // topk limit for the gather kernel's LDS tile list
+constexpr int kMaxTopk = 255;   // topk limit (the selected-key kernel keeps topk + 1 entries)
 constexpr int kMaxSelCand = 16384;  // eligible blocks/clusters scored per query block in LDS
 
 enum Kind { SWA = 0, RETRIEVAL = 1, TRIANGLE = 2, DENSE = 3 };
@@ -41,13 +41,19 @@ struct AttnParams {
   int topk, force_block0;
   const int32_t* csr_off;  // cluster mode: [Hkv, M+1]
   const int32_t* csr_mem;  // cluster mode: [Hkv, N]
-  int M;
+  int M;                   // 0 = block mode
+  float* lse;              // [Hret, N] log2-sum-exp of the window part (retrieval heads)
+};
+
+// Retrieval heads handled by the selected-key kernel (slot t = row of sel / lse).
+struct SelList {
+  int32_t n_ret;
+  int32_t head[kMaxHeads];
 };
 
 // Host launchers (each returns a hipError_t from the launch).
 hipError_t launch_attn_band(const AttnParams& p, const PackTable& packs, hipStream_t s);
-hipError_t launch_attn_gather_blocks(const AttnParams& p, const PackTable& packs, hipStream_t s);
-hipError_t launch_attn_gather_clusters(const AttnParams& p, const PackTable& packs, hipStream_t s);
+hipError_t launch_attn_selected(const AttnParams& p, const SelList& sl, hipStream_t s);
 
 struct ProjParams {
   const uint16_t* X;   // bf16 [N, H, D]
@@ -67,6 +73,9 @@ struct SelectParams {
   const int32_t* csr_off;  // [Hkv, M+1]
   const int32_t* csr_mem;  // [Hkv, N]
   int32_t* sel;        // [Hret, n_qb, topk]
+  __bf16* c_hi;        // cluster mode scratch: [Hkv, M, r] split centroids
+  __bf16* c_lo;
+  int32_t* first_mem;  // [Hkv, M] smallest member position (INT_MAX if empty)
   int N, n_qb, window, topk, force_block0, M;
   int n_ret;
   int32_t group_of_ret[kMaxHeads];
@@ -81,11 +90,16 @@ struct KmeansParams {
   int32_t* csr_mem;    // [Hkv, N]
   int32_t* hist;       // scratch [Hkv, n_chunks, M]
   int32_t* count;      // scratch [Hkv, M]
+  __bf16* c_hi;        // scratch [Hkv, M, r]: centroids split in three bf16 parts
+  __bf16* c_mid;
+  __bf16* c_lo;
+  float* c_norm;       // scratch [Hkv, M]
   int N, M, stride, n_chunks;
 };
 size_t kmeans_scratch_bytes(int N, int M, int Hkv);
 hipError_t launch_kmeans(KmeansParams p, int Hkv, int iters, hipStream_t s);
-hipError_t launch_select_clusters(const SelectParams& p, hipStream_t s);
+hipError_t launch_select_clusters(const SelectParams& p, int Hkv, hipStream_t s);
+size_t select_clusters_scratch_bytes(int M, int Hkv);
 
 struct CrossParams {
   const uint16_t* Q;

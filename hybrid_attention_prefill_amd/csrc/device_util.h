@@ -8,6 +8,30 @@ namespace dev {
 
 constexpr int kNT = 256;
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// fp32 x = hi + lo (+ rest) with hi, lo bf16: hi = rn(x), lo = rn(x - hi).
+// Products of split operands reproduce fp32 dot products to ~1e-5 relative
+// with three MFMA passes (hi*hi + hi*lo + lo*hi).
+__device__ __forceinline__ void split2(float x, __bf16& hi, __bf16& lo) {
+  hi = (__bf16)x;
+  lo = (__bf16)(x - (float)hi);
+}
+
+// Three bf16 parts: x = hi + mid + lo to ~2^-24 relative; six MFMA passes
+// (hi*hi, hi*mid, mid*hi, mid*mid, hi*lo, lo*hi) give fp32-accurate dots.
+__device__ __forceinline__ void split3(float x, __bf16& hi, __bf16& mid, __bf16& lo) {
+  hi = (__bf16)x;
+  const float r = x - (float)hi;
+  mid = (__bf16)r;
+  lo = (__bf16)(r - (float)mid);
+}
+
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {

@@ -1,0 +1,310 @@
+// Retrieval heads: attention over the indexer-selected keys outside the local
+// window, merged into the window result.
+//
+// RTPurbo post: the 16-dim indexer picks candidate keys from the past
+// context, then exact softmax attention runs on that small set in full head
+// dimension, next to the head's local window.  The key set of row i is
+//   window(i) U {j <= i - w : j in a selected key block / selected cluster}
+// (U key block 0 when forced).  The window part is computed by the banded
+// kernel, which also leaves the row's log2-sum-exp; this kernel computes the
+// selected part for one (retrieval head, 64-row query block) and merges:
+//   O = (O_win 2^lse_win + O_sel 2^lse_sel) / (2^lse_win + 2^lse_sel).
+//
+// The selected part reads scattered K/V rows (HBM-bound).  A workgroup takes
+// one (head, block): its 4 waves own 16 query rows each and share every
+// 64-key tile staged in LDS (v_mfma_f32_16x16x32_bf16, fp32 online softmax).
+// Key rows of tile t+2 are looked up (CSR members or block keys) while tile t
+// is computed and tile t+1 is in flight; two workgroups fit on a CU.
+#include "common.h"
+#include "device_util.h"
+
+#include <limits.h>
+
+namespace ha {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int D = kHeadDim;
+constexpr int BK = 64;
+constexpr int NT = 256;
+constexpr int KSTR = D + 8;
+constexpr int VSTR = BK + 8;
+constexpr int K_ELEMS = BK * KSTR;
+constexpr int V_ELEMS = D * VSTR;
+constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kMInit = -1e30f;
+constexpr float kSlack = 8.f;
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Key u (0..31) of a 32-key PV k-step sits at this V^T position: lane group
+// g = lane/16 feeds B slot e' with key (e'/4)*16 + 4g + e'%4 (the S^T layout
+// of two 16-key blocks), and reads 8 contiguous positions 8g .. 8g+7.
+__device__ __forceinline__ int vt_pos(int u) { return 8 * ((u & 15) >> 2) + 4 * (u >> 4) + (u & 3); }
+
+struct TileRegs {
+  u32x4 k[4];
+  u32x4 v[4];
+};
+
+// K slots c*16 + tid/16 (16-B chunk tid%16); V slots 4*(tid%16) + x (d chunk tid/16)
+__device__ __forceinline__ int k_slot(int c, int tid) { return c * 16 + (tid >> 4); }
+__device__ __forceinline__ int v_slot(int x, int tid) { return (tid & 15) * 4 + x; }
+
+__device__ __forceinline__ void tile_load(TileRegs& r, const uint16_t* __restrict__ K,
+                                          const uint16_t* __restrict__ V, const int* ring, size_t rs, int g,
+                                          int tid) {
+  const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int key = ring[k_slot(c, tid)];
+    r.k[c] = key >= 0 ? *reinterpret_cast<const u32x4*>(K + (size_t)key * rs + g * D + (tid & 15) * 8) : z;
+  }
+  const int dc = tid >> 4;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int key = ring[v_slot(x, tid)];
+    r.v[x] = key >= 0 ? *reinterpret_cast<const u32x4*>(V + (size_t)key * rs + g * D + dc * 8) : z;
+  }
+}
+
+__device__ __forceinline__ void tile_store(const TileRegs& r, uint16_t* buf, int tid) {
+  uint16_t* Ks = buf;
+  uint16_t* Vt = buf + K_ELEMS;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int id = c * NT + tid;
+    *reinterpret_cast<u32x4*>(Ks + (id >> 4) * KSTR + (id & 15) * 8) = r.k[c];
+  }
+  const int kg = tid & 15, dc = tid >> 4;
+  const int pos = 32 * (kg >> 3) + vt_pos((kg * 4) & 31);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t a0 = r.v[0][w], a1 = r.v[1][w], a2 = r.v[2][w], a3 = r.v[3][w];
+    u32x2 ev, od;
+    ev[0] = (a0 & 0xFFFFu) | (a1 << 16);
+    ev[1] = (a2 & 0xFFFFu) | (a3 << 16);
+    od[0] = (a0 >> 16) | (a1 & 0xFFFF0000u);
+    od[1] = (a2 >> 16) | (a3 & 0xFFFF0000u);
+    *reinterpret_cast<u32x2*>(Vt + (dc * 8 + 2 * w) * VSTR + pos) = ev;
+    *reinterpret_cast<u32x2*>(Vt + (dc * 8 + 2 * w + 1) * VSTR + pos) = od;
+  }
+}
+
+struct Acc {
+  f32x4 o[8];   // O^T: d block db -> rows d = 16 db + 4 (lane/16) + e, column = the lane's query
+  float m, l;   // running max (raw scores) and this lane's partial sum
+};
+
+// One 64-key tile against the wave's 16 query rows.  Key j of slot s is
+// visible to row i iff j >= 0 and j <= i - w (outside the window).
+__device__ __forceinline__ void tile_compute(const uint16_t* __restrict__ buf, const int* __restrict__ kpos,
+                                             const bf16x8 (&qf)[4], Acc& acc, int lane, int i, int w, float c) {
+  const uint16_t* Ks = buf;
+  const uint16_t* Vt = buf + K_ELEMS;
+  const int lq = lane & 15, lg = lane >> 4;
+  f32x4 s[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + (kb * 16 + lq) * KSTR + ks * 32 + lg * 8);
+      s[kb] = mfma16(kf, qf[ks], s[kb]);
+    }
+  }
+  float mx = kNegInf;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const int4 jv = *reinterpret_cast<const int4*>(kpos + kb * 16 + lg * 4);
+    const int js[4] = {jv.x, jv.y, jv.z, jv.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool vis = (js[e] >= 0) & (i - js[e] >= w);
+      s[kb][e] = vis ? s[kb][e] : kNegInf;
+      mx = fmaxf(mx, s[kb][e]);
+    }
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  // lazily moved reference max (see the banded kernel): rescale only when a
+  // row max exceeds it by more than kSlack in log2 units
+  if (__any((mx - acc.m) * c > kSlack)) {
+    const float mnew = fmaxf(acc.m, mx);
+    const float alpha = __builtin_amdgcn_exp2f((acc.m - mnew) * c);
+    acc.m = mnew;
+    acc.l *= alpha;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) acc.o[db] *= alpha;
+  }
+  const float nb = -acc.m * c;
+  float sum = 0.f;
+  bf16x8 pf[2];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][e], c, nb));
+      sum += pv;
+      pf[kb >> 1][(kb & 1) * 4 + e] = (__bf16)pv;
+    }
+  acc.l += sum;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const bf16x8 vf = *reinterpret_cast<const bf16x8*>(Vt + (db * 16 + lq) * VSTR + ks * 32 + lg * 8);
+      acc.o[db] = mfma16(vf, pf[ks], acc.o[db]);
+    }
+}
+
+__global__ __launch_bounds__(NT, 2) void attn_selected_kernel(AttnParams p, SelList sl) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * BUF_ELEMS];
+  __shared__ __attribute__((aligned(16))) int ring[3][BK];
+  __shared__ int ent[kMaxTopk + 1];     // block id (block mode) or CSR start (cluster mode)
+  __shared__ int pre[kMaxTopk + 2];     // prefix of visible key counts per entry
+  __shared__ int tmp4[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int b = lid / sl.n_ret, t = lid % sl.n_ret;
+  const int h = sl.head[t];
+  const int g = h / p.G;
+  const int q0 = b * BK;
+  const int lim = min(p.N, q0 + BK) - 1 - p.window;   // keys j <= lim can be visible
+  const int n_kb = (p.N + BK - 1) / BK;
+  const int32_t* mem = p.csr_mem ? p.csr_mem + (size_t)g * p.N : nullptr;
+
+  // entries: forced block 0 + the selection; count of keys j <= lim in each
+  const int ne = p.topk + (p.force_block0 ? 1 : 0);
+  int cnt = 0, start = 0;
+  if (tid < ne && lim >= 0) {
+    if (p.force_block0 && tid == 0) {
+      start = 0;
+      cnt = min(BK, lim + 1);
+    } else {
+      const int e = tid - (p.force_block0 ? 1 : 0);
+      const int v = p.sel[((size_t)t * p.n_qt + b) * p.topk + e];
+      if (p.M > 0) {
+        if (v >= 0 && v < p.M) {
+          const int32_t* off = p.csr_off + (size_t)g * (p.M + 1);
+          const int lo = off[v];
+          int a = lo, bb = off[v + 1];
+          while (a < bb) {
+            const int mid = (a + bb) >> 1;
+            if (mem[mid] <= lim) a = mid + 1;
+            else bb = mid;
+          }
+          start = lo;
+          cnt = a - lo;
+        }
+      } else if (v >= 0 && v < n_kb && !(p.force_block0 && v == 0)) {
+        start = v;
+        cnt = max(0, min(BK, lim - v * BK + 1));
+      }
+    }
+  }
+  int total;
+  const int excl = dev::block_excl_scan(cnt, tmp4, &total);
+  if (tid < ne) {
+    ent[tid] = start;
+    pre[tid] = excl;
+  }
+  if (tid == 0) pre[ne] = total;
+  __syncthreads();
+  const int T = (total + BK - 1) / BK;
+  if (T == 0) return;
+
+  // key row of slot s of tile idx (flat index f = 64 idx + s over the entries)
+  auto lookup = [&](int idx, int s) -> int {
+    const int f = idx * BK + s;
+    if (f >= total) return -1;
+    int a = 0, bb = ne;              // largest e with pre[e] <= f
+    while (bb - a > 1) {
+      const int mid = (a + bb) >> 1;
+      if (pre[mid] <= f) a = mid;
+      else bb = mid;
+    }
+    const int r = f - pre[a];
+    if (p.M > 0) return (int)mem[ent[a] + r];
+    return ent[a] * BK + r;
+  };
+
+  const int lq = lane & 15, lg = lane >> 4;
+  const int i = q0 + wave * 16 + lq;          // this lane's query row
+  bf16x8 qf[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    if (i < p.N) {
+      qf[ks] = *reinterpret_cast<const bf16x8*>(p.Q + ((size_t)i * p.Hq + h) * D + ks * 32 + lg * 8);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)0.f;
+    }
+  }
+  Acc acc;
+  acc.m = kMInit;
+  acc.l = 0.f;
+#pragma unroll
+  for (int db = 0; db < 8; ++db) acc.o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const size_t rs = (size_t)p.Hkv * D;
+  if (tid < BK) {
+    ring[0][tid] = lookup(0, tid);
+    if (T > 1) ring[1][tid] = lookup(1, tid);
+  }
+  __syncthreads();
+  TileRegs r;
+  tile_load(r, p.K, p.V, ring[0], rs, g, tid);
+  tile_store(r, smem, tid);
+  __syncthreads();
+  for (int tt = 0; tt < T; ++tt) {
+    int pending = -1;
+    if (tt + 1 < T) tile_load(r, p.K, p.V, ring[(tt + 1) % 3], rs, g, tid);
+    const bool prep = tt + 2 < T && tid < BK;
+    if (prep) pending = lookup(tt + 2, tid);
+    tile_compute(smem + (tt & 1) * BUF_ELEMS, ring[tt % 3], qf, acc, lane, i, p.window, p.c);
+    if (tt + 1 < T) tile_store(r, smem + ((tt + 1) & 1) * BUF_ELEMS, tid);
+    if (prep) ring[(tt + 2) % 3][tid] = pending;
+    __syncthreads();
+  }
+
+  // merge with the window result of the row
+  float lt = acc.l + __shfl_xor(acc.l, 16);
+  lt += __shfl_xor(lt, 32);
+  if (i >= p.N || !(lt > 0.f)) return;
+  const float lse_s = acc.m * p.c + __log2f(lt);
+  const float lse_w = p.lse[(size_t)t * p.N + i];
+  const float M = fmaxf(lse_s, lse_w);
+  const float ws = exp2f(lse_s - M), ww = exp2f(lse_w - M);
+  const float inv = 1.f / (ws + ww);
+  const float fs = ws * inv / lt, fw = ww * inv;
+  float* row = p.O + ((size_t)i * p.Hq + h) * D;
+#pragma unroll
+  for (int db = 0; db < 8; ++db) {
+    float4* dst = reinterpret_cast<float4*>(row + db * 16 + lg * 4);
+    float4 v = *dst;
+    v.x = fmaf(v.x, fw, acc.o[db][0] * fs);
+    v.y = fmaf(v.y, fw, acc.o[db][1] * fs);
+    v.z = fmaf(v.z, fw, acc.o[db][2] * fs);
+    v.w = fmaf(v.w, fw, acc.o[db][3] * fs);
+    *dst = v;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_selected(const AttnParams& p, const SelList& sl, hipStream_t s) {
+  const int nwg = sl.n_ret * p.n_qt;
+  if (nwg == 0 || (p.topk == 0 && !p.force_block0)) return hipSuccess;
+  hipLaunchKernelGGL(attn_selected_kernel, dim3(nwg), dim3(NT), 0, s, p, sl);
+  return hipGetLastError();
+}
+
+}  // namespace ha

@@ -28,41 +28,70 @@ constexpr int NT = 256;
 // Projection: one 16-lane group per row; lane part p holds d in [8p, 8p+8),
 // computes 16 partial outputs, then a 4-step reduce-scatter leaves output r
 // in lane r of the group.  HBM-bound: 256 B read, 64 B written per row.
-__global__ __launch_bounds__(NT) void project_kernel(ProjParams p) {
-  __shared__ float Ps[D * R];
+// Projection on MFMA: a wave takes 16 rows at a time; X[16 x 128] (bf16,
+// exact) times P[128 x 16] with P split into three bf16 parts, so the three
+// products per k-step reproduce the fp32 result (v_mfma_f32_16x16x32_bf16,
+// A = X rows, B = P slice).  Lane l feeds row l%16 / column l%16 with
+// k = 8 (l/16) .. +8 of each 32-wide k-step and ends with rows 4 (l/16) + e
+// of output column l%16.  A workgroup walks a contiguous range of rows of
+// one entry; two row groups are in flight per iteration.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16(dev::bf16x8 a, dev::bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__global__ __launch_bounds__(NT) void project_kernel(ProjParams p, int rows_per_wg) {
   const int e = blockIdx.y;
   const int grp = p.group[e], head = p.head[e];
-  for (int x = threadIdx.x; x < D * R; x += NT) Ps[x] = p.P[(size_t)grp * D * R + x];
-  __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int part = lane & 15;
-  const int i = blockIdx.x * 16 + wave * 4 + (lane >> 4);
-  float acc[R];
+  const int lq = lane & 15, lg = lane >> 4;
+  dev::bf16x8 ph[4], pm[4], pl[4];
+  {
+    const float* src = p.P + (size_t)grp * D * R;
 #pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = 0.f;
-  if (i < p.N) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(p.X + ((size_t)i * p.H + head) * D + part * 8);
-    const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-    for (int dd = 0; dd < 8; ++dd) {
-      const uint32_t bits = (dd & 1) ? (w4[dd >> 1] & 0xFFFF0000u) : (w4[dd >> 1] << 16);
-      const float x = __uint_as_float(bits);
-      const float* prow = Ps + (part * 8 + dd) * R;
+      for (int x = 0; x < 8; ++x) {
+        __bf16 h, m, l;
+        dev::split3(src[(ks * 32 + lg * 8 + x) * R + lq], h, m, l);
+        ph[ks][x] = h;
+        pm[ks][x] = m;
+        pl[ks][x] = l;
+      }
+  }
+  const int r0 = blockIdx.x * rows_per_wg, r1 = min(p.N, r0 + rows_per_wg);
+  for (int base = r0 + wave * 32; base < r1; base += 128) {
+    dev::bf16x8 xa[2][4];
 #pragma unroll
-      for (int r = 0; r < R; ++r) acc[r] = fmaf(x, prow[r], acc[r]);
+    for (int u = 0; u < 2; ++u) {
+      const int i = base + u * 16 + lq;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        if (i < r1) {
+          xa[u][ks] = *reinterpret_cast<const dev::bf16x8*>(p.X + ((size_t)i * p.H + head) * D + ks * 32 + lg * 8);
+        } else {
+#pragma unroll
+          for (int x = 0; x < 8; ++x) xa[u][ks][x] = (__bf16)0.f;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        acc = mfma16(xa[u][ks], pl[ks], acc);
+        acc = mfma16(xa[u][ks], pm[ks], acc);
+        acc = mfma16(xa[u][ks], ph[ks], acc);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = base + u * 16 + lg * 4 + q;
+        if (i < r1) p.out[((size_t)e * p.N + i) * R + lq] = acc[q];
+      }
     }
   }
-#pragma unroll
-  for (int step = 8; step >= 1; step >>= 1) {
-    const bool hi = (lane & step) != 0;
-#pragma unroll
-    for (int j = 0; j < step; ++j) {
-      const float keep = hi ? acc[step + j] : acc[j];
-      const float give = hi ? acc[j] : acc[step + j];
-      acc[j] = keep + __shfl_xor(give, step);
-    }
-  }
-  if (i < p.N) p.out[((size_t)e * p.N + i) * R + part] = acc[0];
 }
 
 // One workgroup per (retrieval head, query block).  Wave w scores the
@@ -123,7 +152,11 @@ __global__ __launch_bounds__(NT) void select_blocks_kernel(SelectParams p) {
 
 hipError_t launch_project(const ProjParams& p, hipStream_t s) {
   if (p.n_entries == 0 || p.N == 0) return hipSuccess;
-  hipLaunchKernelGGL(project_kernel, dim3((p.N + 15) / 16, p.n_entries), dim3(NT), 0, s, p);
+  // about 2048 workgroups in total, each over a multiple of 16 rows
+  const int target = max(1, 2048 / p.n_entries);
+  int per = (p.N + target - 1) / target;
+  per = max(16, (per + 15) / 16 * 16);
+  hipLaunchKernelGGL(project_kernel, dim3((p.N + per - 1) / per, p.n_entries), dim3(NT), 0, s, p, per);
   return hipGetLastError();
 }
 

@@ -36,49 +36,116 @@ __global__ __launch_bounds__(NT) void km_init_kernel(KmeansParams p) {
   p.cent[((size_t)g * p.M + m) * R + r] = p.klow[((size_t)g * p.N + (size_t)m * p.stride) * R + r];
 }
 
-__global__ __launch_bounds__(NT) void km_assign_kernel(KmeansParams p) {
-  __shared__ float cs[kCTile * R];
-  __shared__ float cn[kCTile];
+// Per iteration: centroids split into three bf16 parts and their squared
+// norms, for the MFMA distance pass.
+__global__ __launch_bounds__(NT) void km_prep_kernel(KmeansParams p) {
   const int g = blockIdx.y;
-  const int j = blockIdx.x * NT + threadIdx.x;
-  const bool ok = j < p.N;
-  float k[R];
-  {
-    const float* kp = p.klow + ((size_t)g * p.N + (ok ? j : 0)) * R;
+  const int m = blockIdx.x * NT + threadIdx.x;
+  if (m >= p.M) return;
+  const size_t o = ((size_t)g * p.M + m) * R;
+  const float* c = p.cent + o;
+  float nrm = 0.f;
 #pragma unroll
-    for (int r = 0; r < R; r += 4) {
-      const float4 v = *reinterpret_cast<const float4*>(kp + r);
-      k[r] = v.x; k[r + 1] = v.y; k[r + 2] = v.z; k[r + 3] = v.w;
+  for (int r = 0; r < R; ++r) {
+    const float v = c[r];
+    nrm = fmaf(v, v, nrm);
+    dev::split3(v, p.c_hi[o + r], p.c_mid[o + r], p.c_lo[o + r]);
+  }
+  p.c_norm[(size_t)g * p.M + m] = nrm;
+}
+
+// Assignment: each wave owns 64 keys (two 32-key column blocks).  For every
+// tile of 32 centroids, S^T[m][j] = C_m . k_j comes from six bf16 MFMA passes
+// over the split operands (fp32-accurate), then d = |C_m|^2 - 2 S^T (the
+// |k_j|^2 term does not change the argmin).  A lane holds one key and 16 of
+// the tile's centroids in increasing order, so a strict "<" keeps the lowest
+// index; the two lane halves are merged with the same rule at the end.
+__global__ __launch_bounds__(NT) void km_assign_kernel(KmeansParams p) {
+  const int g = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, lr = lane & 31, lh = lane >> 5;
+  const int j0 = (blockIdx.x * 4 + wave) * 64;
+  if (j0 >= p.N) return;
+  dev::bf16x8 kh[2], km[2], kl[2];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int j = min(p.N - 1, j0 + kt * 32 + lr);
+    const float* kp = p.klow + ((size_t)g * p.N + j) * R + lh * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      __bf16 h, m, l;
+      dev::split3(kp[e], h, m, l);
+      kh[kt][e] = h;
+      km[kt][e] = m;
+      kl[kt][e] = l;
     }
   }
-  float best = __builtin_inff();
-  int arg = 0;
-  const float* C = p.cent + (size_t)g * p.M * R;
-  for (int m0 = 0; m0 < p.M; m0 += kCTile) {
-    const int nm = min(kCTile, p.M - m0);
-    __syncthreads();
-    for (int x = threadIdx.x; x < nm * R; x += NT) cs[x] = C[(size_t)m0 * R + x];
-    __syncthreads();
-    for (int x = threadIdx.x; x < nm; x += NT) {
-      float s = 0.f;
+  float best[2] = {__builtin_inff(), __builtin_inff()};
+  int arg[2] = {0, 0};
+  const __bf16* ch = p.c_hi + (size_t)g * p.M * R;
+  const __bf16* cm = p.c_mid + (size_t)g * p.M * R;
+  const __bf16* cl = p.c_lo + (size_t)g * p.M * R;
+  const float* cn = p.c_norm + (size_t)g * p.M;
+  const int n_tiles = (p.M + 31) / 32;
+  // operands of tile x+1 are loaded while tile x is computed
+  auto ld = [&](int x, dev::bf16x8& ah, dev::bf16x8& am, dev::bf16x8& al, float (&nr)[16]) {
+    const int m0 = x * 32;
+    const int ma = min(p.M - 1, m0 + lr);
+    ah = *reinterpret_cast<const dev::bf16x8*>(ch + (size_t)ma * R + lh * 8);
+    am = *reinterpret_cast<const dev::bf16x8*>(cm + (size_t)ma * R + lh * 8);
+    al = *reinterpret_cast<const dev::bf16x8*>(cl + (size_t)ma * R + lh * 8);
 #pragma unroll
-      for (int r = 0; r < R; ++r) s = fmaf(cs[x * R + r], cs[x * R + r], s);
-      cn[x] = s;
+    for (int q = 0; q < 4; ++q) {
+      const int mrow = m0 + lh * 4 + q * 8;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) nr[q * 4 + e] = (mrow + e < p.M) ? cn[mrow + e] : __builtin_inff();
     }
-    __syncthreads();
-    for (int mm = 0; mm < nm; ++mm) {
-      const float* c = cs + mm * R;
-      float dot = 0.f;
+  };
+  dev::bf16x8 nah, nam, nal;
+  float nnr[16];
+  ld(0, nah, nam, nal, nnr);
+  for (int x = 0; x < n_tiles; ++x) {
+    const dev::bf16x8 ah = nah, am = nam, al = nal;
+    float nr[16];
 #pragma unroll
-      for (int r = 0; r < R; ++r) dot = fmaf(k[r], c[r], dot);
-      const float d = fmaf(-2.f, dot, cn[mm]);
-      if (d < best) {
-        best = d;
-        arg = m0 + mm;
+    for (int e = 0; e < 16; ++e) nr[e] = nnr[e];
+    if (x + 1 < n_tiles) ld(x + 1, nah, nam, nal, nnr);
+    const int m0 = x * 32;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      dev::f32x16 acc = {};
+      acc = dev::mfma32(al, kh[kt], acc);
+      acc = dev::mfma32(ah, kl[kt], acc);
+      acc = dev::mfma32(am, km[kt], acc);
+      acc = dev::mfma32(am, kh[kt], acc);
+      acc = dev::mfma32(ah, km[kt], acc);
+      acc = dev::mfma32(ah, kh[kt], acc);
+      float d[16];
+      float tmin = __builtin_inff();
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        d[e] = fmaf(-2.f, acc[e], nr[e]);
+        tmin = fminf(tmin, d[e]);
+      }
+      // the per-element argmin update only runs when some lane improves
+      if (__any(tmin < best[kt])) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          if (d[e] < best[kt]) {
+            best[kt] = d[e];
+            arg[kt] = m0 + lh * 4 + (e >> 2) * 8 + (e & 3);
+          }
+        }
       }
     }
   }
-  if (ok) p.assign[(size_t)g * p.N + j] = arg;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const float ob = __shfl_xor(best[kt], 32);
+    const int oa = __shfl_xor(arg[kt], 32);
+    if (ob < best[kt] || (ob == best[kt] && oa < arg[kt])) arg[kt] = oa;
+    const int j = j0 + kt * 32 + lr;
+    if (lh == 0 && j < p.N) p.assign[(size_t)g * p.N + j] = arg[kt];
+  }
 }
 
 // per-chunk cluster histogram -> hist[g][chunk][m]
@@ -191,47 +258,97 @@ __global__ __launch_bounds__(NT) void km_update_kernel(KmeansParams p) {
 // first CSR member is the smallest position); score = max over the query
 // block's rows of qlow_i . C_m; the topk best by (score desc, cluster asc).
 
+// Per layer, once: centroids split into bf16 hi/lo parts and the first
+// (smallest) member position of every cluster (INT_MAX when empty).
+__global__ __launch_bounds__(NT) void cluster_prep_kernel(SelectParams p) {
+  const int g = blockIdx.y;
+  const int m = blockIdx.x * NT + threadIdx.x;
+  if (m >= p.M) return;
+  const float* c = p.cent + ((size_t)g * p.M + m) * R;
+  __bf16* hi = p.c_hi + ((size_t)g * p.M + m) * R;
+  __bf16* lo = p.c_lo + ((size_t)g * p.M + m) * R;
+#pragma unroll
+  for (int r = 0; r < R; ++r) dev::split2(c[r], hi[r], lo[r]);
+  const int32_t* off = p.csr_off + (size_t)g * (p.M + 1);
+  const int lo_i = off[m], hi_i = off[m + 1];
+  p.first_mem[(size_t)g * p.M + m] = hi_i > lo_i ? p.csr_mem[(size_t)g * p.N + lo_i] : INT_MAX;
+}
+
+// One workgroup per (retrieval head, query block).  S[i][m] = qlow_i . C_m on
+// MFMA (32 rows x 32 centroids per instruction, k = r = 16), split operands;
+// a lane ends with 16 rows of one centroid, so the row max is a lane-local
+// reduction plus one exchange with lane ^ 32.  Wave w takes centroid tiles
+// w, w+4, ...
 __global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
   __shared__ uint32_t keys[kMaxSelCand];
-  __shared__ float qs[kBlock * R];
   __shared__ int hist[256];
   __shared__ int tmp4[4];
   __shared__ int bcast[2];
   const int b = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, lr = lane & 31, lh = lane >> 5;
   const int g = p.group_of_ret[t];
   const int qs0 = b * kBlock;
   const int nrow = min(kBlock, p.N - qs0);
   const int lim = qs0 + nrow - 1 - p.window;
   int32_t* out = p.sel + ((size_t)t * p.n_qb + b) * p.topk;
   if (p.topk == 0) return;
-  for (int x = tid; x < nrow * R; x += NT) qs[x] = p.qlow[((size_t)t * p.N + qs0) * R + x];
-  __syncthreads();
-  const int32_t* off = p.csr_off + (size_t)g * (p.M + 1);
-  const int32_t* mem = p.csr_mem + (size_t)g * p.N;
-  const float* C = p.cent + (size_t)g * p.M * R;
-  int n_el = 0;
-  for (int m = tid; m < p.M; m += NT) {
-    const int lo = off[m], hi = off[m + 1];
-    const bool el = lim >= 0 && hi > lo && mem[lo] <= lim;
-    uint32_t key = 0u;
-    if (el) {
-      float c[R];
+
+  dev::bf16x8 qh[2], ql[2];
 #pragma unroll
-      for (int r = 0; r < R; r += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(C + (size_t)m * R + r);
-        c[r] = v.x; c[r + 1] = v.y; c[r + 2] = v.z; c[r + 3] = v.w;
-      }
-      float mx = -__builtin_inff();
-      for (int i = 0; i < nrow; ++i) {
-        float dot = 0.f;
+  for (int rt = 0; rt < 2; ++rt) {
+    const int i = rt * 32 + lr;
+    const float* qp = p.qlow + ((size_t)t * p.N + qs0 + min(i, nrow - 1)) * R + lh * 8;
 #pragma unroll
-        for (int r = 0; r < R; ++r) dot = fmaf(qs[i * R + r], c[r], dot);
-        mx = fmaxf(mx, dot);
-      }
-      key = dev::order_key(mx);
-      ++n_el;
+    for (int e = 0; e < 8; ++e) {
+      const float v = i < nrow ? qp[e] : 0.f;
+      __bf16 h, l;
+      dev::split2(v, h, l);
+      qh[rt][e] = h;
+      ql[rt][e] = l;
     }
-    keys[m] = key;
+  }
+  const __bf16* chi = p.c_hi + (size_t)g * p.M * R;
+  const __bf16* clo = p.c_lo + (size_t)g * p.M * R;
+  const int32_t* fm = p.first_mem + (size_t)g * p.M;
+  const bool ragged = nrow < kBlock;
+  int n_el = 0;
+  const int n_tiles = (p.M + 31) / 32;
+  // operands of the next tile are loaded while the current one is computed
+  auto ld = [&](int x, dev::bf16x8& bh, dev::bf16x8& bl, int& f) {
+    const int m = min(p.M - 1, x * 32 + lr);
+    bh = *reinterpret_cast<const dev::bf16x8*>(chi + (size_t)m * R + lh * 8);
+    bl = *reinterpret_cast<const dev::bf16x8*>(clo + (size_t)m * R + lh * 8);
+    f = fm[m];
+  };
+  dev::bf16x8 nbh, nbl;
+  int nf = INT_MAX;
+  if (wave < n_tiles) ld(wave, nbh, nbl, nf);
+  for (int x = wave; x < n_tiles; x += 4) {
+    const dev::bf16x8 bh = nbh, bl = nbl;
+    const int fmm = nf;
+    if (x + 4 < n_tiles) ld(x + 4, nbh, nbl, nf);
+    const int m = x * 32 + lr;
+    const bool mok = m < p.M;
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      dev::f32x16 acc = {};
+      acc = dev::mfma32(ql[rt], bh, acc);
+      acc = dev::mfma32(qh[rt], bl, acc);
+      acc = dev::mfma32(qh[rt], bh, acc);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = rt * 32 + lh * 4 + (e >> 2) * 8 + (e & 3);
+        const float v = (ragged && row >= nrow) ? -__builtin_inff() : acc[e];
+        mx = fmaxf(mx, v);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (lh == 0 && mok) {
+      const bool el = lim >= 0 && fmm <= lim;
+      keys[m] = el ? dev::order_key(mx) : 0u;
+      n_el += el;
+    }
   }
   int nE;
   dev::block_excl_scan(n_el, tmp4, &nE);
@@ -245,7 +362,8 @@ __global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
 
 size_t kmeans_scratch_bytes(int N, int M, int Hkv) {
   const size_t n_chunks = (size_t)(N + kChunk - 1) / kChunk;
-  return (size_t)Hkv * n_chunks * M * sizeof(int32_t) + (size_t)Hkv * M * sizeof(int32_t);
+  return (size_t)Hkv * n_chunks * M * sizeof(int32_t) + (size_t)Hkv * M * sizeof(int32_t) +
+         (size_t)Hkv * M * (3 * R * sizeof(__bf16) + sizeof(float)) + 256;
 }
 
 hipError_t launch_kmeans(KmeansParams p, int Hkv, int iters, hipStream_t s) {
@@ -253,6 +371,7 @@ hipError_t launch_kmeans(KmeansParams p, int Hkv, int iters, hipStream_t s) {
   hipLaunchKernelGGL(km_init_kernel, dim3((p.M * R + NT - 1) / NT, Hkv), dim3(NT), 0, s, p);
   hipError_t e = hipGetLastError();
   for (int it = 0; it < iters && e == hipSuccess; ++it) {
+    hipLaunchKernelGGL(km_prep_kernel, dim3((p.M + NT - 1) / NT, Hkv), dim3(NT), 0, s, p);
     hipLaunchKernelGGL(km_assign_kernel, dim3((p.N + NT - 1) / NT, Hkv), dim3(NT), 0, s, p);
     hipLaunchKernelGGL(km_hist_kernel, dim3(p.n_chunks, Hkv), dim3(NT), 0, s, p);
     hipLaunchKernelGGL(km_colscan_kernel, dim3((p.M + NT - 1) / NT, Hkv), dim3(NT), 0, s, p);
@@ -264,10 +383,15 @@ hipError_t launch_kmeans(KmeansParams p, int Hkv, int iters, hipStream_t s) {
   return e;
 }
 
-hipError_t launch_select_clusters(const SelectParams& p, hipStream_t s) {
+hipError_t launch_select_clusters(const SelectParams& p, int Hkv, hipStream_t s) {
   if (p.n_ret == 0 || p.n_qb == 0) return hipSuccess;
+  hipLaunchKernelGGL(cluster_prep_kernel, dim3((p.M + NT - 1) / NT, Hkv), dim3(NT), 0, s, p);
   hipLaunchKernelGGL(select_clusters_kernel, dim3(p.n_qb, p.n_ret), dim3(NT), 0, s, p);
   return hipGetLastError();
+}
+
+size_t select_clusters_scratch_bytes(int M, int Hkv) {
+  return (size_t)Hkv * M * (2 * R * sizeof(__bf16) + sizeof(int32_t));
 }
 
 }  // namespace ha

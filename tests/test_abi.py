@@ -105,6 +105,9 @@ def test_prefill_cluster_argument_checks():
     # more clusters than the selection kernel scores in LDS
     big = _desc(n_tokens=1 << 20, topk=4, n_clusters=20000, kmeans_iters=1, kmeans_stride=2)
     assert _prefill(big, kinds) == ha.HA_ERR_UNSUPPORTED
+    # block 0 is a block-mode rule
+    assert _prefill(_desc(topk=4, n_clusters=10, kmeans_iters=2, kmeans_stride=2, force_block0=1),
+                    kinds) == ha.HA_ERR_UNSUPPORTED
     L = ha.lib()
     d = _desc(topk=4, n_clusters=10, kmeans_iters=2, kmeans_stride=2)
     assert L.ha_kmeans(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == ha.HA_ERR_ARG
