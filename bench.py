@@ -38,11 +38,29 @@ METRIC = "hybrid-attn prefill ms/layer + TFLOP/s (% MFMA peak) at 128K and 1M to
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 DEFAULT_SUITE = ["qwen3_30b_a3b_32k", "trianglemix_llama8b_128k", "dense_llama8b_128k",
-                 "orthros_8b_128k"]
-# traffic measured with rocprofv3 --pmc (FETCH_SIZE, WRITE_SIZE) for the
-# dominant kernel, KiB per dispatch, scaled by the copy-kernel factor;
-# filled in from profiles/ when the counters were taken on the current kernel.
-TRAFFIC = {}
+                 "orthros_8b_128k", "allsparse_1m"]
+COPY_CAL_BYTES = 1 << 30
+# HBM bytes per launch measured with rocprofv3 --pmc (FETCH_SIZE, WRITE_SIZE,
+# KiB per dispatch, scaled by the same counters on a plain 1 GiB copy); valid
+# only while the kernel source is the one the counters were taken on.
+TRAFFIC = {
+    ("dense_llama8b_128k", "attn_band"): {
+        "bytes": 20693634840, "source": "hybrid_attention_prefill_amd/csrc/attn.hip",
+        "sha256_prefix": "f2df3ccb0ccedba7"},
+}
+
+
+def traffic_for(workload, stage):
+    import hashlib
+    t = TRAFFIC.get((workload, stage))
+    if t is None:
+        return None
+    try:
+        with open(os.path.join(ROOT, t["source"]), "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    return t["bytes"] if sha.startswith(t["sha256_prefix"]) else None
 
 
 # ---------------------------------------------------------------------------
@@ -285,6 +303,8 @@ def main():
     ap.add_argument("--workloads", type=str, default=",".join(DEFAULT_SUITE))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run one plain device copy of 1 GiB (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -301,6 +321,14 @@ def main():
     import synth
     ha.lib()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calibrate_copy:
+        src = torch.empty(COPY_CAL_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("copy calibration: 1 GiB device-to-device copy done")
     names = [n for n in args.workloads.split(",") if n]
     cache = {}
     layers = []
@@ -372,7 +400,7 @@ def main():
             act = per_layer[w.name]["attn_pairs"] - sum(
                 pairs_swa(w.n_tokens, w.window) for k in w.head_kind if k == 0)
         achieved = 4.0 * w.head_dim * act / (stage_ms[best] * 1e-3) / 1e12
-        tr = TRAFFIC.get((w.name, sname))
+        tr = traffic_for(w.name, sname)
         roof = {"kernel": f"{sname} ({w.name})", "bound": "mfma", "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": tr, "avg_ms": round(float(stage_ms[best]), 4),
