@@ -138,6 +138,7 @@ def layer_prefill(w, q_rows: Callable[[int, int], np.ndarray], K: np.ndarray, V:
                 C, a, _ = lloyd(res.klow[g], w.n_clusters, w.kmeans_stride, w.kmeans_iters)
             res.centroids[g], res.assign[g] = C, a
 
+    eligible_memo = {}   # (KV head, block) -> eligible clusters (shared by the group's heads)
     off = 0
     for b in blocks:
         r0, r1 = b * Bq, min(N, (b + 1) * Bq)
@@ -168,7 +169,9 @@ def layer_prefill(w, q_rows: Callable[[int, int], np.ndarray], K: np.ndarray, V:
                 res.qlow.setdefault(h, {})[b] = ql
                 if w.n_clusters > 0:
                     C, a = res.centroids[g], res.assign[g]
-                    E = eligible_clusters(a, C.shape[0], qe, w.window)
+                    if (g, b) not in eligible_memo:
+                        eligible_memo[(g, b)] = eligible_clusters(a, C.shape[0], qe, w.window)
+                    E = eligible_memo[(g, b)]
                     s = cluster_scores(ql, C, E)
                     S = topk_order(s, E, w.topk)
                     if sel_override is not None:

@@ -76,3 +76,70 @@ def test_dense_layer_128k():
 
 def test_orthros_layer_128k():
     _run("orthros_8b_128k", heads=list(range(0, 32, 5)))
+
+
+def test_allsparse_layer_1m():
+    """1M tokens, all 16 heads retrieval, 16384 clusters: 64 sampled query
+    blocks (one per 1/64 stratum), every head; k-means checked at its last
+    iteration against the GPU's centroids of the iteration before."""
+    import torch
+    import hybrid_attention_prefill_amd as ha
+    from oracle.kmeans import assign_step, update_step, sq_dist
+    w = synth.WORKLOADS["allsparse_1m"]
+    print(f"\n[case] full-size {w.name}", flush=True)
+    li = synth.make_layer_inputs(w)
+    O, _, aux = _gpu.run_gpu(w, li)
+    klow = aux["klow"]
+    C = aux["centroids"].cpu().numpy()
+    asg = aux["assign"].cpu().numpy()
+    off = aux["csr_off"].cpu().numpy()
+    mem = aux["csr_mem"].cpu().numpy()
+    sel = aux["sel"].cpu().numpy()
+    # centroids after iters-1 iterations (the run is deterministic)
+    d = ha.make_desc(w.n_tokens, w.n_q_heads, w.n_kv_heads, 128, window=w.window, topk=w.topk,
+                     n_clusters=w.n_clusters, kmeans_iters=w.kmeans_iters - 1, kmeans_stride=w.kmeans_stride)
+    Cp = torch.empty_like(aux["centroids"])
+    a2 = torch.empty_like(aux["assign"])
+    o2 = torch.empty_like(aux["csr_off"])
+    m2 = torch.empty_like(aux["csr_mem"])
+    ws = torch.empty(ha.ha_workspace_bytes(d, w.head_kind), dtype=torch.uint8, device="cuda")
+    ha.ha_kmeans(d, klow, Cp, a2, o2, m2, ws)
+    torch.cuda.synchronize()
+    Cp = Cp.cpu().numpy()
+    X = klow.cpu().numpy()
+    rng = np.random.default_rng(77)
+    for g in range(w.n_kv_heads):
+        keys = np.sort(rng.choice(w.n_tokens, 4096, replace=False))
+        Xg = X[g][keys].astype(np.float64)
+        ora = assign_step(Xg, Cp[g])
+        ga = asg[g][keys].astype(np.int64)
+        for t in np.nonzero(ora != ga)[0]:
+            dg = sq_dist(Xg[t:t + 1], Cp[g][ga[t]:ga[t] + 1].astype(np.float64))[0]
+            do = sq_dist(Xg[t:t + 1], Cp[g][ora[t]:ora[t] + 1].astype(np.float64))[0]
+            band = 1e-5 * (Xg[t] @ Xg[t] + max(Cp[g][ga[t]] @ Cp[g][ga[t]], Cp[g][ora[t]] @ Cp[g][ora[t]]))
+            assert abs(dg - do) <= band
+        ref_c = update_step(X[g].astype(np.float64), asg[g].astype(np.int64), Cp[g].astype(np.float64))
+        assert np.max(np.abs(ref_c - C[g])) <= 1e-4
+        cnt = np.bincount(asg[g], minlength=w.n_clusters)
+        np.testing.assert_array_equal(off[g], np.r_[0, np.cumsum(cnt)])
+        np.testing.assert_array_equal(mem[g], np.lexsort((np.arange(w.n_tokens), asg[g])))
+    print("k-means: last iteration, update and CSR verified", flush=True)
+    n = w.n_qb
+    blocks = sorted({int(np.random.default_rng(5).integers(s * n // 64, (s + 1) * n // 64)) for s in range(64)})
+    nd = si.needles(w)
+    blocks = sorted(set(blocks) | {int(r) // 64 for r in nd.q_row[:4]})
+    K, V = si.bf16_to_f64(li.K), si.bf16_to_f64(li.V)
+    P = li.P.astype(np.float64)
+    q_rows = lambda a, b: si.bf16_to_f64(li.Q[a:b])
+    km = {g: (C[g], asg[g]) for g in range(w.n_kv_heads)}
+    ref = layer_prefill(w, q_rows, K, V, P, blocks=blocks, kmeans_override=km)
+    override, n_diff = {}, 0
+    for t, h in enumerate(w.ret_heads):
+        override[h] = {}
+        for b, (E, s) in ref.scored[h].items():
+            n_diff += _gpu.check_selection(sel[t, b], E, s, w.topk, f"head {h} block {b}")
+            override[h][b] = np.array([x for x in sel[t, b] if x >= 0], dtype=np.int64)
+    print(f"selection near-tie differences: {n_diff}", flush=True)
+    ref = layer_prefill(w, q_rows, K, V, P, blocks=blocks, kmeans_override=km, sel_override=override)
+    mx, mean = _gpu.assert_close_out(O.cpu().numpy()[ref.rows], ref.O, w.name)
+    print(f"allsparse_1m: {len(blocks)} blocks x 16 heads, max abs {mx:.3e}, mean abs {mean:.3e}")
