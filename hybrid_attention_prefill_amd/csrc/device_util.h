@@ -63,12 +63,20 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+constexpr int kHistCopies = 8;            // histogram replicas (cuts same-bin atomic conflicts)
+constexpr int kHistStride = 257;          // words between replicas (different banks)
+constexpr int kHistWords = kHistCopies * kHistStride;
+
 // Exact top-k over keys[0..n) (order-preserving uint32 images of the scores),
 // larger key first, lower index first among equal keys.  Writes the chosen
 // indices + id_base in ascending order to out[0..k), -1 in out[k..topk).
+// Radix select on 8-bit digits: per pass, a histogram of the keys that match
+// the digits found so far (8 lane-strided replicas, so lanes with equal
+// digits mostly hit different words), then one wave finds the digit where
+// the count from the top reaches k.  hist needs kHistWords ints.
 __device__ inline void topk_select(const uint32_t* keys, int n, int k, int topk, int id_base, int32_t* out,
-                            int* hist, int* tmp4, int* bcast) {
-  const int tid = threadIdx.x;
+                                   int* hist, int* tmp4, int* bcast) {
+  const int tid = threadIdx.x, lane = tid & 63;
   if (k > n) k = n;
   if (k <= 0) {
     for (int x = tid; x < topk; x += kNT) out[x] = -1;
@@ -76,25 +84,50 @@ __device__ inline void topk_select(const uint32_t* keys, int n, int k, int topk,
   }
   uint32_t prefix = 0, pmask = 0;
   int need = k;
+  int* myhist = hist + (lane & (kHistCopies - 1)) * kHistStride;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    hist[tid] = 0;
+    for (int x = tid; x < kHistWords; x += kNT) hist[x] = 0;
     __syncthreads();
     for (int x = tid; x < n; x += kNT) {
       const uint32_t u = keys[x];
-      if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255], 1);
+      if ((u & pmask) == prefix) atomicAdd(&myhist[(u >> shift) & 255], 1);
     }
     __syncthreads();
-    if (tid == 0) {
-      int cum = 0, dstar = 0;
-      for (int d = 255; d >= 0; --d) {
-        if (cum + hist[d] >= need) {
-          dstar = d;
-          break;
-        }
-        cum += hist[d];
+    if (tid < 64) {
+      // lane l owns digits 4l .. 4l+3; merge the replicas, then a suffix scan
+      // over lanes (from digit 255 down) finds the digit d* where the count of
+      // keys with digit > d* is < need <= count with digit >= d*
+      int c[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        int v = 0;
+#pragma unroll
+        for (int r = 0; r < kHistCopies; ++r) v += hist[r * kHistStride + lane * 4 + q];
+        c[q] = v;
       }
-      bcast[0] = dstar;
-      bcast[1] = need - cum;
+      const int tot = c[0] + c[1] + c[2] + c[3];
+      // inclusive suffix sum over lanes >= lane
+      int suf = tot;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_down(suf, o);
+        if (lane + o < 64) suf += t;
+      }
+      const int above = suf - tot;            // keys with digits in lanes > lane
+      // the owning lane: above < need <= suf
+      if (above < need && need <= suf) {
+        int cum = above, dstar = lane * 4;
+#pragma unroll
+        for (int q = 3; q >= 0; --q) {
+          if (cum + c[q] >= need) {
+            dstar = lane * 4 + q;
+            break;
+          }
+          cum += c[q];
+        }
+        bcast[0] = dstar;
+        bcast[1] = need - cum;
+      }
     }
     __syncthreads();
     prefix |= (uint32_t)bcast[0] << shift;
@@ -103,33 +136,43 @@ __device__ inline void topk_select(const uint32_t* keys, int n, int k, int topk,
     __syncthreads();
   }
   // prefix is the k-th largest key; take every key above it and the first
-  // `need` keys equal to it in index order.
-  const int chunk = (n + kNT - 1) / kNT;
-  const int a = min(n, tid * chunk), b = min(n, a + chunk);
-  int ties = 0;
-  for (int x = a; x < b; ++x) ties += keys[x] == prefix;
-  int tot;
-  int tie_base = block_excl_scan(ties, tmp4, &tot);
-  int chosen = 0;
-  {
-    int tr = tie_base;
-    for (int x = a; x < b; ++x) {
-      const uint32_t u = keys[x];
-      if (u > prefix) ++chosen;
-      else if (u == prefix) { if (tr < need) ++chosen; ++tr; }
-    }
+  // `need` keys equal to it in index order.  Wave w scans a contiguous quarter
+  // of the index range in rounds of 64 consecutive keys (lane = offset);
+  // ranks among ties and output positions come from ballots.
+  const int wave = tid >> 6;
+  const int per_wave = ((n + 4 * 64 - 1) / (4 * 64)) * 64;
+  const int wa = min(n, wave * per_wave), wb = min(n, wa + per_wave);
+  int gt = 0, eq = 0;
+  for (int x0 = wa; x0 < wb; x0 += 64) {
+    const int x = x0 + lane;
+    const uint32_t u = x < wb ? keys[x] : 0u;
+    gt += (int)__popcll(__ballot(x < wb && u > prefix));
+    eq += (int)__popcll(__ballot(x < wb && u == prefix));
   }
-  int pos = block_excl_scan(chosen, tmp4, &tot);
-  {
-    int tr = tie_base;
-    for (int x = a; x < b; ++x) {
-      const uint32_t u = keys[x];
-      bool take = false;
-      if (u > prefix) take = true;
-      else if (u == prefix) { take = tr < need; ++tr; }
-      if (take) out[pos++] = id_base + x;
-    }
+  if (lane == 0) {
+    tmp4[wave] = eq;
+    tmp4[4 + wave] = gt;
   }
+  __syncthreads();
+  int tie_run = 0, pos_run = 0;
+  for (int w = 0; w < wave; ++w) {
+    const int eqw = tmp4[w], gtw = tmp4[4 + w];
+    pos_run += gtw + max(0, min(need - tie_run, eqw));
+    tie_run += eqw;
+  }
+  for (int x0 = wa; x0 < wb; x0 += 64) {
+    const int x = x0 + lane;
+    const uint32_t u = x < wb ? keys[x] : 0u;
+    const bool is_tie = x < wb && u == prefix;
+    const uint64_t tb = __ballot(is_tie);
+    const int tie_rank = tie_run + (int)__popcll(tb & ((1ull << lane) - 1ull));
+    const bool take = x < wb && (u > prefix || (is_tie && tie_rank < need));
+    const uint64_t kb = __ballot(take);
+    if (take) out[pos_run + (int)__popcll(kb & ((1ull << lane) - 1ull))] = id_base + x;
+    tie_run += (int)__popcll(tb);
+    pos_run += (int)__popcll(kb);
+  }
+  __syncthreads();
   for (int x = k + tid; x < topk; x += kNT) out[x] = -1;
 }
 

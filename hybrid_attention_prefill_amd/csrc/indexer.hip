@@ -99,8 +99,8 @@ __global__ __launch_bounds__(NT) void project_kernel(ProjParams p, int rows_per_
 // row's low-rank vector, keys are read wave-uniformly.
 __global__ __launch_bounds__(NT) void select_blocks_kernel(SelectParams p) {
   __shared__ uint32_t keys[kMaxSelCand];
-  __shared__ int hist[256];
-  __shared__ int tmp4[4];
+  __shared__ int hist[dev::kHistWords];
+  __shared__ int tmp4[8];
   __shared__ int bcast[2];
   const int b = blockIdx.x, t = blockIdx.y;
   const int g = p.group_of_ret[t];

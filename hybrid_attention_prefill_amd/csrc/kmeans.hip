@@ -54,17 +54,24 @@ __global__ __launch_bounds__(NT) void km_prep_kernel(KmeansParams p) {
   p.c_norm[(size_t)g * p.M + m] = nrm;
 }
 
-// Assignment: each wave owns 64 keys (two 32-key column blocks).  For every
-// tile of 32 centroids, S^T[m][j] = C_m . k_j comes from six bf16 MFMA passes
-// over the split operands (fp32-accurate), then d = |C_m|^2 - 2 S^T (the
-// |k_j|^2 term does not change the argmin).  A lane holds one key and 16 of
-// the tile's centroids in increasing order, so a strict "<" keeps the lowest
-// index; the two lane halves are merged with the same rule at the end.
+// Assignment: each wave owns 64 keys (two 32-key column blocks), the
+// workgroup 256.  Centroids are staged in LDS 256 at a time (three bf16 parts
+// + squared norm) and shared by the 4 waves.  For every tile of 32 centroids,
+// S^T[m][j] = C_m . k_j comes from six bf16 MFMA passes over the split
+// operands (fp32-accurate), then d = |C_m|^2 - 2 S^T (the |k_j|^2 term does
+// not change the argmin).  A lane holds one key and 16 of the tile's
+// centroids in increasing order, so a strict "<" keeps the lowest index; the
+// two lane halves are merged with the same rule at the end.
+constexpr int kCChunk = 256;      // centroids per LDS chunk
+constexpr int kCStr = 24;         // bf16 row stride of a staged part (48 B: conflict-free 16-B reads)
+
 __global__ __launch_bounds__(NT) void km_assign_kernel(KmeansParams p) {
+  __shared__ __attribute__((aligned(16))) __bf16 cs[3][kCChunk * kCStr];
+  __shared__ __attribute__((aligned(16))) float cns[kCChunk];
   const int g = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, lr = lane & 31, lh = lane >> 5;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, lr = lane & 31, lh = lane >> 5;
   const int j0 = (blockIdx.x * 4 + wave) * 64;
-  if (j0 >= p.N) return;
   dev::bf16x8 kh[2], km[2], kl[2];
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
@@ -81,58 +88,64 @@ __global__ __launch_bounds__(NT) void km_assign_kernel(KmeansParams p) {
   }
   float best[2] = {__builtin_inff(), __builtin_inff()};
   int arg[2] = {0, 0};
-  const __bf16* ch = p.c_hi + (size_t)g * p.M * R;
-  const __bf16* cm = p.c_mid + (size_t)g * p.M * R;
-  const __bf16* cl = p.c_lo + (size_t)g * p.M * R;
+  const __bf16* parts[3] = {p.c_hi + (size_t)g * p.M * R, p.c_mid + (size_t)g * p.M * R,
+                            p.c_lo + (size_t)g * p.M * R};
   const float* cn = p.c_norm + (size_t)g * p.M;
-  const int n_tiles = (p.M + 31) / 32;
-  // operands of tile x+1 are loaded while tile x is computed
-  auto ld = [&](int x, dev::bf16x8& ah, dev::bf16x8& am, dev::bf16x8& al, float (&nr)[16]) {
-    const int m0 = x * 32;
-    const int ma = min(p.M - 1, m0 + lr);
-    ah = *reinterpret_cast<const dev::bf16x8*>(ch + (size_t)ma * R + lh * 8);
-    am = *reinterpret_cast<const dev::bf16x8*>(cm + (size_t)ma * R + lh * 8);
-    al = *reinterpret_cast<const dev::bf16x8*>(cl + (size_t)ma * R + lh * 8);
+  for (int c0 = 0; c0 < p.M; c0 += kCChunk) {
+    const int nc = min(kCChunk, p.M - c0);
+    __syncthreads();
+    {
+      // thread t stages centroid c0 + t: three 32-B parts and the norm
+      const int m = c0 + tid;
+      const bool ok = tid < nc;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int mrow = m0 + lh * 4 + q * 8;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) nr[q * 4 + e] = (mrow + e < p.M) ? cn[mrow + e] : __builtin_inff();
-    }
-  };
-  dev::bf16x8 nah, nam, nal;
-  float nnr[16];
-  ld(0, nah, nam, nal, nnr);
-  for (int x = 0; x < n_tiles; ++x) {
-    const dev::bf16x8 ah = nah, am = nam, al = nal;
-    float nr[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) nr[e] = nnr[e];
-    if (x + 1 < n_tiles) ld(x + 1, nah, nam, nal, nnr);
-    const int m0 = x * 32;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      dev::f32x16 acc = {};
-      acc = dev::mfma32(al, kh[kt], acc);
-      acc = dev::mfma32(ah, kl[kt], acc);
-      acc = dev::mfma32(am, km[kt], acc);
-      acc = dev::mfma32(am, kh[kt], acc);
-      acc = dev::mfma32(ah, km[kt], acc);
-      acc = dev::mfma32(ah, kh[kt], acc);
-      float d[16];
-      float tmin = __builtin_inff();
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        d[e] = fmaf(-2.f, acc[e], nr[e]);
-        tmin = fminf(tmin, d[e]);
+      for (int q = 0; q < 3; ++q) {
+        const uint4* src = reinterpret_cast<const uint4*>(parts[q] + (size_t)(ok ? m : c0) * R);
+        const uint4 v0 = src[0], v1 = src[1];
+        uint4* dst = reinterpret_cast<uint4*>(&cs[q][tid * kCStr]);
+        dst[0] = v0;
+        dst[1] = v1;
       }
-      // the per-element argmin update only runs when some lane improves
-      if (__any(tmin < best[kt])) {
+      cns[tid] = ok ? cn[m] : __builtin_inff();
+    }
+    __syncthreads();
+    const int n_tiles = (nc + 31) / 32;
+    for (int x = 0; x < n_tiles; ++x) {
+      const int r0 = x * 32;
+      const dev::bf16x8 ah = *reinterpret_cast<const dev::bf16x8*>(&cs[0][(r0 + lr) * kCStr + lh * 8]);
+      const dev::bf16x8 am = *reinterpret_cast<const dev::bf16x8*>(&cs[1][(r0 + lr) * kCStr + lh * 8]);
+      const dev::bf16x8 al = *reinterpret_cast<const dev::bf16x8*>(&cs[2][(r0 + lr) * kCStr + lh * 8]);
+      float nr[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(&cns[r0 + lh * 4 + q * 8]);
+        nr[q * 4 + 0] = v.x; nr[q * 4 + 1] = v.y; nr[q * 4 + 2] = v.z; nr[q * 4 + 3] = v.w;
+      }
+      const int m0 = c0 + r0;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        dev::f32x16 acc = {};
+        acc = dev::mfma32(al, kh[kt], acc);
+        acc = dev::mfma32(ah, kl[kt], acc);
+        acc = dev::mfma32(am, km[kt], acc);
+        acc = dev::mfma32(am, kh[kt], acc);
+        acc = dev::mfma32(ah, km[kt], acc);
+        acc = dev::mfma32(ah, kh[kt], acc);
+        float d[16];
+        float tmin = __builtin_inff();
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          if (d[e] < best[kt]) {
-            best[kt] = d[e];
-            arg[kt] = m0 + lh * 4 + (e >> 2) * 8 + (e & 3);
+          d[e] = fmaf(-2.f, acc[e], nr[e]);
+          tmin = fminf(tmin, d[e]);
+        }
+        // the per-element argmin update only runs when some lane improves
+        if (__any(tmin < best[kt])) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            if (d[e] < best[kt]) {
+              best[kt] = d[e];
+              arg[kt] = m0 + lh * 4 + (e >> 2) * 8 + (e & 3);
+            }
           }
         }
       }
@@ -274,88 +287,115 @@ __global__ __launch_bounds__(NT) void cluster_prep_kernel(SelectParams p) {
   p.first_mem[(size_t)g * p.M + m] = hi_i > lo_i ? p.csr_mem[(size_t)g * p.N + lo_i] : INT_MAX;
 }
 
-// One workgroup per (retrieval head, query block).  S[i][m] = qlow_i . C_m on
-// MFMA (32 rows x 32 centroids per instruction, k = r = 16), split operands;
-// a lane ends with 16 rows of one centroid, so the row max is a lane-local
-// reduction plus one exchange with lane ^ 32.  Wave w takes centroid tiles
-// w, w+4, ...
+// One workgroup per (retrieval head, kSelBlocks query blocks).  S[i][m] =
+// qlow_i . C_m on MFMA (32 rows x 32 centroids per instruction, k = r = 16),
+// split operands; a lane ends with 16 rows of one centroid, so the row max is
+// a lane-local reduction plus one exchange with lane ^ 32.  Wave w takes
+// centroid tiles w, w+4, ...  The scores stay in LDS for the exact top-k.
+constexpr int kSelBlocks = 1;
+
 __global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
-  __shared__ uint32_t keys[kMaxSelCand];
-  __shared__ int hist[256];
-  __shared__ int tmp4[4];
+  __shared__ uint32_t keys[kSelBlocks][kMaxSelCand];
+  __shared__ int hist[dev::kHistWords];
+  __shared__ int tmp4[8];
   __shared__ int bcast[2];
-  const int b = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
+  const int t = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, lr = lane & 31, lh = lane >> 5;
   const int g = p.group_of_ret[t];
-  const int qs0 = b * kBlock;
-  const int nrow = min(kBlock, p.N - qs0);
-  const int lim = qs0 + nrow - 1 - p.window;
-  int32_t* out = p.sel + ((size_t)t * p.n_qb + b) * p.topk;
+  const int b0 = blockIdx.x * kSelBlocks;
+  const int nb = min(kSelBlocks, p.n_qb - b0);
   if (p.topk == 0) return;
 
-  dev::bf16x8 qh[2], ql[2];
+  int nrow[kSelBlocks], lim[kSelBlocks];
+  dev::bf16x8 qh[kSelBlocks][2], ql[kSelBlocks][2];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const int i = rt * 32 + lr;
-    const float* qp = p.qlow + ((size_t)t * p.N + qs0 + min(i, nrow - 1)) * R + lh * 8;
+  for (int bi = 0; bi < kSelBlocks; ++bi) {
+    const int qs0 = (b0 + bi) * kBlock;
+    nrow[bi] = bi < nb ? min(kBlock, p.N - qs0) : 0;
+    lim[bi] = bi < nb ? qs0 + nrow[bi] - 1 - p.window : -1;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float v = i < nrow ? qp[e] : 0.f;
-      __bf16 h, l;
-      dev::split2(v, h, l);
-      qh[rt][e] = h;
-      ql[rt][e] = l;
+    for (int rt = 0; rt < 2; ++rt) {
+      const int i = rt * 32 + lr;
+      const bool ok = i < nrow[bi];
+      const float* qp = p.qlow + ((size_t)t * p.N + (ok ? qs0 + i : 0)) * R + lh * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = ok ? qp[e] : 0.f;
+        __bf16 hh, ll;
+        dev::split2(v, hh, ll);
+        qh[bi][rt][e] = hh;
+        ql[bi][rt][e] = ll;
+      }
     }
   }
   const __bf16* chi = p.c_hi + (size_t)g * p.M * R;
   const __bf16* clo = p.c_lo + (size_t)g * p.M * R;
   const int32_t* fm = p.first_mem + (size_t)g * p.M;
-  const bool ragged = nrow < kBlock;
-  int n_el = 0;
+  int n_el[kSelBlocks] = {};
   const int n_tiles = (p.M + 31) / 32;
-  // operands of the next tile are loaded while the current one is computed
+  // A wave's tiles are x = wave + 4 i.  Operands are loaded kPre tiles ahead
+  // (register ring, static slots: the loop is unrolled by kPre).
+  constexpr int kPre = 4;
   auto ld = [&](int x, dev::bf16x8& bh, dev::bf16x8& bl, int& f) {
     const int m = min(p.M - 1, x * 32 + lr);
     bh = *reinterpret_cast<const dev::bf16x8*>(chi + (size_t)m * R + lh * 8);
     bl = *reinterpret_cast<const dev::bf16x8*>(clo + (size_t)m * R + lh * 8);
     f = fm[m];
   };
-  dev::bf16x8 nbh, nbl;
-  int nf = INT_MAX;
-  if (wave < n_tiles) ld(wave, nbh, nbl, nf);
-  for (int x = wave; x < n_tiles; x += 4) {
-    const dev::bf16x8 bh = nbh, bl = nbl;
-    const int fmm = nf;
-    if (x + 4 < n_tiles) ld(x + 4, nbh, nbl, nf);
-    const int m = x * 32 + lr;
-    const bool mok = m < p.M;
-    float mx = -__builtin_inff();
+  dev::bf16x8 rbh[kPre], rbl[kPre];
+  int rf[kPre];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      dev::f32x16 acc = {};
-      acc = dev::mfma32(ql[rt], bh, acc);
-      acc = dev::mfma32(qh[rt], bl, acc);
-      acc = dev::mfma32(qh[rt], bh, acc);
+  for (int u = 0; u < kPre; ++u) ld(min(n_tiles - 1, wave + 4 * u), rbh[u], rbl[u], rf[u]);
+  for (int x0 = wave; x0 < n_tiles; x0 += 4 * kPre) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = rt * 32 + lh * 4 + (e >> 2) * 8 + (e & 3);
-        const float v = (ragged && row >= nrow) ? -__builtin_inff() : acc[e];
-        mx = fmaxf(mx, v);
+    for (int u = 0; u < kPre; ++u) {
+      const int x = x0 + 4 * u;
+      if (x < n_tiles) {
+        const dev::bf16x8 bh = rbh[u], bl = rbl[u];
+        const int fmm = rf[u];
+        if (x + 4 * kPre < n_tiles) ld(x + 4 * kPre, rbh[u], rbl[u], rf[u]);
+        const int m = x * 32 + lr;
+        const bool mok = m < p.M;
+#pragma unroll
+        for (int bi = 0; bi < kSelBlocks; ++bi) {
+          float mx = -__builtin_inff();
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt) {
+            dev::f32x16 acc = {};
+            acc = dev::mfma32(ql[bi][rt], bh, acc);
+            acc = dev::mfma32(qh[bi][rt], bl, acc);
+            acc = dev::mfma32(qh[bi][rt], bh, acc);
+            const bool ragged = nrow[bi] < kBlock;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int row = rt * 32 + lh * 4 + (e >> 2) * 8 + (e & 3);
+              const float v = (ragged && row >= nrow[bi]) ? -__builtin_inff() : acc[e];
+              mx = fmaxf(mx, v);
+            }
+          }
+          mx = fmaxf(mx, __shfl_xor(mx, 32));
+          if (lh == 0 && mok) {
+            const bool el = lim[bi] >= 0 && fmm <= lim[bi];
+            keys[bi][m] = el ? dev::order_key(mx) : 0u;
+            n_el[bi] += el;
+          }
+        }
       }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    if (lh == 0 && mok) {
-      const bool el = lim >= 0 && fmm <= lim;
-      keys[m] = el ? dev::order_key(mx) : 0u;
-      n_el += el;
+  }
+#pragma unroll
+  for (int bi = 0; bi < kSelBlocks; ++bi) {
+    int nE;
+    dev::block_excl_scan(n_el[bi], tmp4, &nE);
+    __syncthreads();
+    if (bi < nb) {
+      // ineligible clusters hold key 0, below every real score's key, so the
+      // k = min(topk, nE) largest keys are eligible clusters only.
+      int32_t* out = p.sel + ((size_t)t * p.n_qb + b0 + bi) * p.topk;
+      dev::topk_select(keys[bi], p.M, min(p.topk, nE), p.topk, 0, out, hist, tmp4, bcast);
+      __syncthreads();
     }
   }
-  int nE;
-  dev::block_excl_scan(n_el, tmp4, &nE);
-  __syncthreads();
-  // ineligible clusters hold key 0, below every real score's key, so the
-  // k = min(topk, nE) largest keys are eligible clusters only.
-  dev::topk_select(keys, p.M, min(p.topk, nE), p.topk, 0, out, hist, tmp4, bcast);
 }
 
 }  // namespace
@@ -386,7 +426,8 @@ hipError_t launch_kmeans(KmeansParams p, int Hkv, int iters, hipStream_t s) {
 hipError_t launch_select_clusters(const SelectParams& p, int Hkv, hipStream_t s) {
   if (p.n_ret == 0 || p.n_qb == 0) return hipSuccess;
   hipLaunchKernelGGL(cluster_prep_kernel, dim3((p.M + NT - 1) / NT, Hkv), dim3(NT), 0, s, p);
-  hipLaunchKernelGGL(select_clusters_kernel, dim3(p.n_qb, p.n_ret), dim3(NT), 0, s, p);
+  hipLaunchKernelGGL(select_clusters_kernel, dim3((p.n_qb + kSelBlocks - 1) / kSelBlocks, p.n_ret), dim3(NT), 0,
+                     s, p);
   return hipGetLastError();
 }
 

@@ -102,3 +102,56 @@ def test_deterministic_rerun():
     b = _gpu.run_gpu(w, li)
     assert torch.equal(a[0], b[0])
     assert torch.equal(a[2]["sel"], b[2]["sel"])
+
+
+@pytest.mark.parametrize("f0", [0, 1])
+def test_block_selection_exact_ties_keep_lowest_ids(f0):
+    # every key block holds the same low-rank keys and the window (128) keeps
+    # every eligible pair causal, so all eligible blocks score exactly alike:
+    # the selection must be the k lowest eligible block ids
+    import torch
+    import hybrid_attention_prefill_amd as ha
+    N, k, w = 4096, 5, 128
+    rng = np.random.default_rng(3)
+    kl = np.tile(rng.standard_normal((64, 16)).astype(np.float32), (N // 64, 1))
+    ql = rng.standard_normal((N, 16)).astype(np.float32)
+    kinds = [HEAD_RETRIEVAL] + [HEAD_SWA] * 3
+    d = ha.make_desc(N, 4, 1, 128, window=w, topk=k, force_block0=f0)
+    klow = torch.from_numpy(kl[None]).cuda()
+    qlow = torch.from_numpy(ql[None]).cuda()
+    sel = torch.full((1, N // 64, k), -7, dtype=torch.int32, device="cuda")
+    ha.ha_select_blocks(d, kinds, qlow, klow, sel)
+    torch.cuda.synchronize()
+    sel = sel.cpu().numpy()[0]
+    for b in range(N // 64):
+        qe = b * 64 + 63
+        E = list(range(f0, (qe - w) // 64 + 1)) if qe - w >= 0 else []
+        expect = E[:k] + [-1] * (k - min(k, len(E)))
+        assert list(sel[b]) == expect, (b, list(sel[b]), expect)
+
+
+def test_cluster_selection_exact_ties_keep_lowest_ids():
+    # identical centroids: every eligible cluster scores alike
+    import torch
+    import hybrid_attention_prefill_amd as ha
+    N, M, k, w = 4096, 256, 7, 512
+    rng = np.random.default_rng(4)
+    cent = np.tile(rng.standard_normal((1, 16)).astype(np.float32), (M, 1))
+    assign = np.arange(N) % M                       # first member of cluster m is key m
+    off = np.r_[0, np.cumsum(np.bincount(assign, minlength=M))].astype(np.int32)
+    mem = np.lexsort((np.arange(N), assign)).astype(np.int32)
+    kinds = [HEAD_RETRIEVAL] * 4
+    d = ha.make_desc(N, 4, 1, 128, window=w, topk=k, n_clusters=M, kmeans_iters=1, kmeans_stride=16)
+    ql = torch.from_numpy(rng.standard_normal((4, N, 16)).astype(np.float32)).cuda()
+    sel = torch.full((4, N // 64, k), -7, dtype=torch.int32, device="cuda")
+    ws = torch.empty(ha.ha_workspace_bytes(d, kinds), dtype=torch.uint8, device="cuda")
+    ha.ha_select_clusters(d, kinds, ql, torch.from_numpy(cent[None]).cuda(), torch.from_numpy(off[None]).cuda(),
+                          torch.from_numpy(mem[None]).cuda(), sel, ws)
+    torch.cuda.synchronize()
+    sel = sel.cpu().numpy()
+    for t in range(4):
+        for b in range(N // 64):
+            lim = b * 64 + 63 - w
+            E = [m for m in range(M) if m <= lim]
+            expect = E[:k] + [-1] * (k - min(k, len(E)))
+            assert list(sel[t, b]) == expect, (t, b, list(sel[t, b]), expect)
