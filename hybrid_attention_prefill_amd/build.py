@@ -23,6 +23,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wno-unused-command-line-argument"]
+# Per-source extra flags (none at present).
+FILE_FLAGS: dict = {}
 
 
 def sources():
@@ -32,7 +34,7 @@ def sources():
 
 def _compile(src):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + COMMON + ["-c", src, "-o", obj]
+    cmd = [HIPCC] + COMMON + FILE_FLAGS.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)
