@@ -140,6 +140,22 @@ __device__ __forceinline__ void tile_store(const TileRegs& r, uint16_t* buf, int
   }
 }
 
+// Instruction-scheduler pins for a block of 16 MFMAs fed by 16 LDS fragment
+// reads: the first kAhead reads, then (MFMA, read) pairs, then the last
+// MFMAs, so each read has about kAhead MFMA issue slots (32 cycles each) to
+// land.  Other instructions are placed freely around them.
+constexpr int kAhead = 4;
+template <int Id>
+__device__ __forceinline__ void schedule_reads_ahead() {
+  __builtin_amdgcn_sched_group_barrier(0x100, kAhead, Id);   // DS reads
+#pragma unroll
+  for (int n = 0; n < 16 - kAhead; ++n) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, Id);      // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, Id);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, kAhead, Id);
+}
+
 struct WaveAcc {
   f32x16 o[4];   // O^T: [d block]
   float m;       // running max (raw score units) of this lane's query
@@ -187,6 +203,8 @@ __device__ __forceinline__ void tile_compute(const uint16_t* __restrict__ buf, c
       s[kb] = mfma(kf, qf[t], s[kb]);
     }
   }
+  // issue order: fragment reads run kAhead MFMAs ahead of their use
+  schedule_reads_ahead<0>();
 
   if (!full) {
     const int i = q0 + lr;
@@ -251,6 +269,7 @@ __device__ __forceinline__ void tile_compute(const uint16_t* __restrict__ buf, c
         acc.o[db] = mfma(vf, pf[kb][h2], acc.o[db]);
       }
     }
+  schedule_reads_ahead<1>();
 }
 
 // Q^T fragments (B operands) of the wave's 32 query rows; rows >= N are zero.
