@@ -10,7 +10,7 @@
 //
 // Every step is deterministic, so a run of t iterations reproduces the state
 // after t iterations of a longer run:
-//   assign   one thread per key, centroid tiles in LDS, d = |C|^2 - 2 k.C
+//   assign   one lane per key, centroid tiles in LDS, d = |C|^2 - 2 k.C on MFMA
 //   CSR      stable counting sort of key positions by cluster: per-chunk
 //            histograms, a column scan, then an in-order scatter (ranks among
 //            equal clusters inside a 256-key batch come from an LDS scan)
@@ -54,40 +54,55 @@ __global__ __launch_bounds__(NT) void km_prep_kernel(KmeansParams p) {
   p.c_norm[(size_t)g * p.M + m] = nrm;
 }
 
-// Assignment: each wave owns 64 keys (two 32-key column blocks), the
-// workgroup 256.  Centroids are staged in LDS 256 at a time (three bf16 parts
-// + squared norm) and shared by the 4 waves.  For every tile of 32 centroids,
-// S^T[m][j] = C_m . k_j comes from six bf16 MFMA passes over the split
-// operands (fp32-accurate), then d = |C_m|^2 - 2 S^T (the |k_j|^2 term does
-// not change the argmin).  A lane holds one key and 16 of the tile's
-// centroids in increasing order, so a strict "<" keeps the lowest index; the
+// Assignment: each wave owns 32*KT keys (KT column blocks of 32), the
+// workgroup 4 waves.  Centroids are staged in LDS 256 at a time as four
+// bf16 rows each: the three parts of C_m and (hi, mid, lo) of |C_m|^2.  For
+// every tile of 32 centroids and key block, one chain of seven MFMAs gives
+//   d^T[m][j] = |C_m|^2 - 2 C_m . k_j
+// directly: six passes over the split operands with the keys pre-scaled by
+// -2 (exact), and a seventh that adds the norm parts against a (1, 1, 1)
+// operand.  The |k_j|^2 term does not change the argmin.  A lane holds one
+// key and 16 of the tile's centroids in increasing order; the tile minimum
+// is a min3 chain; only when some lane of a key block improves on its best
+// does the wave look up the index (the lowest element equal to the tile
+// minimum; tiles are scanned in increasing order and replace the best only
+// when strictly smaller, so the lowest index wins on equal distances).  The
 // two lane halves are merged with the same rule at the end.
 constexpr int kCChunk = 256;      // centroids per LDS chunk
 constexpr int kCStr = 24;         // bf16 row stride of a staged part (48 B: conflict-free 16-B reads)
+constexpr int KT = 4;             // 32-key blocks per wave
+constexpr float kPadNorm = 1e30f; // norm of the padding rows of a partial tile
 
 __global__ __launch_bounds__(NT) void km_assign_kernel(KmeansParams p) {
-  __shared__ __attribute__((aligned(16))) __bf16 cs[3][kCChunk * kCStr];
-  __shared__ __attribute__((aligned(16))) float cns[kCChunk];
+  __shared__ __attribute__((aligned(16))) __bf16 cs[4][kCChunk * kCStr];
   const int g = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, lr = lane & 31, lh = lane >> 5;
-  const int j0 = (blockIdx.x * 4 + wave) * 64;
-  dev::bf16x8 kh[2], km[2], kl[2];
+  const int j0 = (blockIdx.x * 4 + wave) * (32 * KT);
+  dev::bf16x8 kh[KT], km[KT], kl[KT];
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
+  for (int kt = 0; kt < KT; ++kt) {
     const int j = min(p.N - 1, j0 + kt * 32 + lr);
     const float* kp = p.klow + ((size_t)g * p.N + j) * R + lh * 8;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       __bf16 h, m, l;
-      dev::split3(kp[e], h, m, l);
+      dev::split3(-2.f * kp[e], h, m, l);
       kh[kt][e] = h;
       km[kt][e] = m;
       kl[kt][e] = l;
     }
   }
-  float best[2] = {__builtin_inff(), __builtin_inff()};
-  int arg[2] = {0, 0};
+  dev::bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)((lh == 0 && e < 3) ? 1.f : 0.f);
+  float best[KT];
+  int arg[KT];
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+    best[kt] = __builtin_inff();
+    arg[kt] = 0;
+  }
   const __bf16* parts[3] = {p.c_hi + (size_t)g * p.M * R, p.c_mid + (size_t)g * p.M * R,
                             p.c_lo + (size_t)g * p.M * R};
   const float* cn = p.c_norm + (size_t)g * p.M;
@@ -95,7 +110,7 @@ __global__ __launch_bounds__(NT) void km_assign_kernel(KmeansParams p) {
     const int nc = min(kCChunk, p.M - c0);
     __syncthreads();
     {
-      // thread t stages centroid c0 + t: three 32-B parts and the norm
+      // thread t stages centroid c0 + t: three 32-B parts and the norm row
       const int m = c0 + tid;
       const bool ok = tid < nc;
 #pragma unroll
@@ -106,7 +121,19 @@ __global__ __launch_bounds__(NT) void km_assign_kernel(KmeansParams p) {
         dst[0] = v0;
         dst[1] = v1;
       }
-      cns[tid] = ok ? cn[m] : __builtin_inff();
+      dev::bf16x8 nr0, nr1;
+      __bf16 h, md, l;
+      dev::split3(ok ? cn[m] : kPadNorm, h, md, l);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        nr0[e] = (__bf16)0.f;
+        nr1[e] = (__bf16)0.f;
+      }
+      nr0[0] = h;
+      nr0[1] = md;
+      nr0[2] = l;
+      *reinterpret_cast<dev::bf16x8*>(&cs[3][tid * kCStr]) = nr0;
+      *reinterpret_cast<dev::bf16x8*>(&cs[3][tid * kCStr + 8]) = nr1;
     }
     __syncthreads();
     const int n_tiles = (nc + 31) / 32;
@@ -115,44 +142,49 @@ __global__ __launch_bounds__(NT) void km_assign_kernel(KmeansParams p) {
       const dev::bf16x8 ah = *reinterpret_cast<const dev::bf16x8*>(&cs[0][(r0 + lr) * kCStr + lh * 8]);
       const dev::bf16x8 am = *reinterpret_cast<const dev::bf16x8*>(&cs[1][(r0 + lr) * kCStr + lh * 8]);
       const dev::bf16x8 al = *reinterpret_cast<const dev::bf16x8*>(&cs[2][(r0 + lr) * kCStr + lh * 8]);
-      float nr[16];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 v = *reinterpret_cast<const float4*>(&cns[r0 + lh * 4 + q * 8]);
-        nr[q * 4 + 0] = v.x; nr[q * 4 + 1] = v.y; nr[q * 4 + 2] = v.z; nr[q * 4 + 3] = v.w;
-      }
+      const dev::bf16x8 an = *reinterpret_cast<const dev::bf16x8*>(&cs[3][(r0 + lr) * kCStr + lh * 8]);
       const int m0 = c0 + r0;
+      // KT independent MFMA chains, interleaved pass by pass
+      dev::f32x16 acc[KT];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        dev::f32x16 acc = {};
-        acc = dev::mfma32(al, kh[kt], acc);
-        acc = dev::mfma32(ah, kl[kt], acc);
-        acc = dev::mfma32(am, km[kt], acc);
-        acc = dev::mfma32(am, kh[kt], acc);
-        acc = dev::mfma32(ah, km[kt], acc);
-        acc = dev::mfma32(ah, kh[kt], acc);
-        float d[16];
-        float tmin = __builtin_inff();
+      for (int kt = 0; kt < KT; ++kt) {
+        acc[kt] = {};
+        acc[kt] = dev::mfma32(al, kh[kt], acc[kt]);
+      }
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          d[e] = fmaf(-2.f, acc[e], nr[e]);
-          tmin = fminf(tmin, d[e]);
-        }
-        // the per-element argmin update only runs when some lane improves
+      for (int kt = 0; kt < KT; ++kt) acc[kt] = dev::mfma32(ah, kl[kt], acc[kt]);
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) acc[kt] = dev::mfma32(am, km[kt], acc[kt]);
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) acc[kt] = dev::mfma32(am, kh[kt], acc[kt]);
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) acc[kt] = dev::mfma32(ah, km[kt], acc[kt]);
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) acc[kt] = dev::mfma32(ah, kh[kt], acc[kt]);
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) acc[kt] = dev::mfma32(an, ones, acc[kt]);
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        float tmin = acc[kt][0];
+#pragma unroll
+        for (int e = 1; e < 15; e += 2) tmin = __builtin_fminf(__builtin_fminf(tmin, acc[kt][e]), acc[kt][e + 1]);
+        tmin = fminf(tmin, acc[kt][15]);
+        // rare once the scan is under way: some lane of this key block
+        // improves; its index is the lowest e holding the tile minimum
         if (__any(tmin < best[kt])) {
+          int idx = 15;
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            if (d[e] < best[kt]) {
-              best[kt] = d[e];
-              arg[kt] = m0 + lh * 4 + (e >> 2) * 8 + (e & 3);
-            }
+          for (int e = 14; e >= 0; --e) idx = acc[kt][e] == tmin ? e : idx;
+          if (tmin < best[kt]) {
+            best[kt] = tmin;
+            arg[kt] = m0 + lh * 4 + (idx >> 2) * 8 + (idx & 3);
           }
         }
       }
     }
   }
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
+  for (int kt = 0; kt < KT; ++kt) {
     const float ob = __shfl_xor(best[kt], 32);
     const int oa = __shfl_xor(arg[kt], 32);
     if (ob < best[kt] || (ob == best[kt] && oa < arg[kt])) arg[kt] = oa;
@@ -412,7 +444,7 @@ hipError_t launch_kmeans(KmeansParams p, int Hkv, int iters, hipStream_t s) {
   hipError_t e = hipGetLastError();
   for (int it = 0; it < iters && e == hipSuccess; ++it) {
     hipLaunchKernelGGL(km_prep_kernel, dim3((p.M + NT - 1) / NT, Hkv), dim3(NT), 0, s, p);
-    hipLaunchKernelGGL(km_assign_kernel, dim3((p.N + NT - 1) / NT, Hkv), dim3(NT), 0, s, p);
+    hipLaunchKernelGGL(km_assign_kernel, dim3((p.N + 4 * 32 * KT - 1) / (4 * 32 * KT), Hkv), dim3(NT), 0, s, p);
     hipLaunchKernelGGL(km_hist_kernel, dim3(p.n_chunks, Hkv), dim3(NT), 0, s, p);
     hipLaunchKernelGGL(km_colscan_kernel, dim3((p.M + NT - 1) / NT, Hkv), dim3(NT), 0, s, p);
     hipLaunchKernelGGL(km_offsets_kernel, dim3(Hkv), dim3(NT), 0, s, p);
