@@ -25,6 +25,7 @@
 // so that each lane owns one query column: the row max / row sum of a query
 // live in one lane pair (lane, lane^32), and P never leaves registers.
 #include "common.h"
+#include "device_util.h"
 
 #include <limits.h>
 
@@ -231,7 +232,7 @@ __device__ __forceinline__ void tile_compute(const uint16_t* __restrict__ buf, c
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = dev::pair32_max(mx);
   if (__any((mx - acc.m) * c > kSlack)) {
     const float mnew = fmaxf(acc.m, mx);
     const float alpha = __builtin_amdgcn_exp2f((acc.m - mnew) * c);
@@ -299,7 +300,7 @@ __device__ __forceinline__ void acc_init(WaveAcc& acc) {
 __device__ __forceinline__ void store_o(const WaveAcc& acc, float* __restrict__ O, float* __restrict__ lse,
                                         int slot, int N, int Hq, int h, int q0, int lane, float c) {
   const int lr = lane & 31, lh = lane >> 5;
-  const float lt = acc.l + __shfl_xor(acc.l, 32);
+  const float lt = dev::pair32_sum(acc.l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const int i = q0 + lr;
   if (i >= N) return;

@@ -32,6 +32,28 @@ __device__ __forceinline__ void split3(float x, __bf16& hi, __bf16& mid, __bf16&
   lo = (__bf16)(r - (float)mid);
 }
 
+// Reductions over a lane pair (l, l ^ 32) or (l, l ^ 16) with the gfx950
+// lane-swap instructions: VALU only, no LDS round trip.  With both operands
+// equal, permlane32_swap returns (v[l % 32], v[32 + l % 32]) in lane l and
+// permlane16_swap returns (v[l & ~16], v[l | 16]), so both lanes of a pair
+// combine the same two values in the same order.
+__device__ __forceinline__ float pair32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair16_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {

@@ -132,8 +132,7 @@ __device__ __forceinline__ void tile_compute(const uint16_t* __restrict__ buf, c
       mx = fmaxf(mx, s[kb][e]);
     }
   }
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = dev::pair32_max(dev::pair16_max(mx));
   // lazily moved reference max (see the banded kernel): rescale only when a
   // row max exceeds it by more than kSlack in log2 units
   if (__any((mx - acc.m) * c > kSlack)) {
@@ -276,8 +275,7 @@ __global__ __launch_bounds__(NT, 2) void attn_selected_kernel(AttnParams p, SelL
   }
 
   // merge with the window result of the row
-  float lt = acc.l + __shfl_xor(acc.l, 16);
-  lt += __shfl_xor(lt, 32);
+  const float lt = dev::pair32_sum(dev::pair16_sum(acc.l));
   if (i >= p.N || !(lt > 0.f)) return;
   const float lse_s = acc.m * p.c + __log2f(lt);
   const float lse_w = p.lse[(size_t)t * p.N + i];

@@ -345,14 +345,16 @@ __global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
     const int qs0 = (b0 + bi) * kBlock;
     nrow[bi] = bi < nb ? min(kBlock, p.N - qs0) : 0;
     lim[bi] = bi < nb ? qs0 + nrow[bi] - 1 - p.window : -1;
+    // rows past the end of a ragged last block repeat the block's first
+    // row, so the row max needs no mask
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
       const int i = rt * 32 + lr;
-      const bool ok = i < nrow[bi];
-      const float* qp = p.qlow + ((size_t)t * p.N + (ok ? qs0 + i : 0)) * R + lh * 8;
+      const int row = bi < nb ? qs0 + (i < nrow[bi] ? i : 0) : 0;
+      const float* qp = p.qlow + ((size_t)t * p.N + row) * R + lh * 8;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float v = ok ? qp[e] : 0.f;
+        const float v = qp[e];
         __bf16 hh, ll;
         dev::split2(v, hh, ll);
         qh[bi][rt][e] = hh;
@@ -397,15 +399,10 @@ __global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
             acc = dev::mfma32(ql[bi][rt], bh, acc);
             acc = dev::mfma32(qh[bi][rt], bl, acc);
             acc = dev::mfma32(qh[bi][rt], bh, acc);
-            const bool ragged = nrow[bi] < kBlock;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              const int row = rt * 32 + lh * 4 + (e >> 2) * 8 + (e & 3);
-              const float v = (ragged && row >= nrow[bi]) ? -__builtin_inff() : acc[e];
-              mx = fmaxf(mx, v);
-            }
+            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[e]);
           }
-          mx = fmaxf(mx, __shfl_xor(mx, 32));
+          mx = dev::pair32_max(mx);
           if (lh == 0 && mok) {
             const bool el = lim[bi] >= 0 && fmm <= lim[bi];
             keys[bi][m] = el ? dev::order_key(mx) : 0u;
