@@ -91,13 +91,14 @@ constexpr int kHistWords = kHistCopies * kHistStride;
 
 // Exact top-k over keys[0..n) (order-preserving uint32 images of the scores),
 // larger key first, lower index first among equal keys.  Writes the chosen
-// indices + id_base in ascending order to out[0..k), -1 in out[k..topk).
+// indices + id_base in ascending order to out[0..k), -1 in out[k..topk)
+// (with idmap, idmap[x] replaces x + id_base; idmap must be increasing).
 // Radix select on 8-bit digits: per pass, a histogram of the keys that match
 // the digits found so far (8 lane-strided replicas, so lanes with equal
 // digits mostly hit different words), then one wave finds the digit where
 // the count from the top reaches k.  hist needs kHistWords ints.
 __device__ inline void topk_select(const uint32_t* keys, int n, int k, int topk, int id_base, int32_t* out,
-                                   int* hist, int* tmp4, int* bcast) {
+                                   int* hist, int* tmp4, int* bcast, const uint16_t* idmap = nullptr) {
   const int tid = threadIdx.x, lane = tid & 63;
   if (k > n) k = n;
   if (k <= 0) {
@@ -190,7 +191,7 @@ __device__ inline void topk_select(const uint32_t* keys, int n, int k, int topk,
     const int tie_rank = tie_run + (int)__popcll(tb & ((1ull << lane) - 1ull));
     const bool take = x < wb && (u > prefix || (is_tie && tie_rank < need));
     const uint64_t kb = __ballot(take);
-    if (take) out[pos_run + (int)__popcll(kb & ((1ull << lane) - 1ull))] = id_base + x;
+    if (take) out[pos_run + (int)__popcll(kb & ((1ull << lane) - 1ull))] = idmap ? (int)idmap[x] : id_base + x;
     tie_run += (int)__popcll(tb);
     pos_run += (int)__popcll(kb);
   }

@@ -319,18 +319,35 @@ __global__ __launch_bounds__(NT) void cluster_prep_kernel(SelectParams p) {
   p.first_mem[(size_t)g * p.M + m] = hi_i > lo_i ? p.csr_mem[(size_t)g * p.N + lo_i] : INT_MAX;
 }
 
-// One workgroup per (retrieval head, kSelBlocks query blocks).  S[i][m] =
-// qlow_i . C_m on MFMA (32 rows x 32 centroids per instruction, k = r = 16),
-// split operands; a lane ends with 16 rows of one centroid, so the row max is
-// a lane-local reduction plus one exchange with lane ^ 32.  Wave w takes
-// centroid tiles w, w+4, ...  The scores stay in LDS for the exact top-k.
+// One workgroup per (retrieval head, query block).  S[i][m] = qlow_i . C_m on
+// MFMA (32 rows x 32 centroids per instruction, k = r = 16), split operands;
+// a lane ends with 16 rows of one centroid, so the row max is a lane-local
+// reduction plus one exchange with lane ^ 32.  Wave w takes centroid tiles
+// w, w+4, ...  The scores stay in LDS for the exact top-k.
+//
+// Exact prefilter for the top-k: each of the 128 scoring lanes keeps the
+// largest key it wrote.  If tau is the k-th largest of these lane maxima, at
+// least k keys are >= tau, so the k-th largest key is >= tau and every key
+// of the answer (ties at the k-th value included) is >= tau.  One pass
+// collects the keys >= tau in index order (each wave a contiguous quarter of
+// the clusters, into its own region of kCapW slots, the rest of the region
+// zero-filled), and the radix select runs on those 4 * kCapW slots.  A wave
+// that finds more than kCapW candidates sends the block to the full select.
 constexpr int kSelBlocks = 1;
+constexpr int kGroups = 128;      // scoring lanes (4 waves x 32)
+constexpr int kCapW = 256;        // candidate slots per wave
 
 __global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
+  static_assert(kSelBlocks == 1, "the prefilter handles one query block per workgroup");
   __shared__ uint32_t keys[kSelBlocks][kMaxSelCand];
   __shared__ int hist[dev::kHistWords];
   __shared__ int tmp4[8];
   __shared__ int bcast[2];
+  __shared__ uint32_t ckeys[4 * kCapW];
+  __shared__ uint16_t cidx[4 * kCapW];
+  __shared__ uint32_t gmax[kGroups];
+  __shared__ uint32_t tau_s;
+  __shared__ int ovf;
   const int t = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, lr = lane & 31, lh = lane >> 5;
   const int g = p.group_of_ret[t];
@@ -366,6 +383,7 @@ __global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
   const __bf16* clo = p.c_lo + (size_t)g * p.M * R;
   const int32_t* fm = p.first_mem + (size_t)g * p.M;
   int n_el[kSelBlocks] = {};
+  uint32_t gmx = 0;                 // largest key this lane wrote
   const int n_tiles = (p.M + 31) / 32;
   // A wave's tiles are x = wave + 4 i.  Operands are loaded kPre tiles ahead
   // (register ring, static slots: the loop is unrolled by kPre).
@@ -405,25 +423,68 @@ __global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
           mx = dev::pair32_max(mx);
           if (lh == 0 && mok) {
             const bool el = lim[bi] >= 0 && fmm <= lim[bi];
-            keys[bi][m] = el ? dev::order_key(mx) : 0u;
+            const uint32_t key = el ? dev::order_key(mx) : 0u;
+            keys[bi][m] = key;
+            gmx = max(gmx, key);
             n_el[bi] += el;
           }
         }
       }
     }
   }
-#pragma unroll
-  for (int bi = 0; bi < kSelBlocks; ++bi) {
-    int nE;
-    dev::block_excl_scan(n_el[bi], tmp4, &nE);
-    __syncthreads();
-    if (bi < nb) {
-      // ineligible clusters hold key 0, below every real score's key, so the
-      // k = min(topk, nE) largest keys are eligible clusters only.
-      int32_t* out = p.sel + ((size_t)t * p.n_qb + b0 + bi) * p.topk;
-      dev::topk_select(keys[bi], p.M, min(p.topk, nE), p.topk, 0, out, hist, tmp4, bcast);
-      __syncthreads();
+  if (lh == 0) gmax[wave * 32 + lr] = gmx;
+  if (tid == 0) {
+    tau_s = 1u;
+    ovf = 0;
+  }
+  int nE;
+  dev::block_excl_scan(n_el[0], tmp4, &nE);     // (synchronizes)
+  const int k = min(p.topk, nE);
+  int32_t* out = p.sel + ((size_t)t * p.n_qb + b0) * p.topk;
+  if (k > kGroups) {
+    dev::topk_select(keys[0], p.M, k, p.topk, 0, out, hist, tmp4, bcast);
+    return;
+  }
+  // tau = k-th largest lane maximum (the one with #{>} < k <= #{>=});
+  // eligible keys are >= 1, so tau >= 1 also drops the ineligible ones
+  if (k > 0 && tid < kGroups) {
+    const uint32_t gv = gmax[tid];
+    int gt = 0, ge = 0;
+    for (int j = 0; j < kGroups; ++j) {
+      const uint32_t v = gmax[j];
+      gt += v > gv;
+      ge += v >= gv;
     }
+    if (gt < k && k <= ge && gv > 1u) tau_s = gv;
+  }
+  __syncthreads();
+  const uint32_t tau = tau_s;
+  {
+    const int per = ((p.M + 4 * 64 - 1) / (4 * 64)) * 64;
+    const int wa = min(p.M, wave * per), wb = min(p.M, wa + per);
+    uint32_t* ck = ckeys + wave * kCapW;
+    uint16_t* ci = cidx + wave * kCapW;
+    int cnt = 0;
+    for (int x0 = wa; x0 < wb; x0 += 64) {
+      const int x = x0 + lane;
+      const uint32_t u = x < wb ? keys[0][x] : 0u;
+      const bool take = u >= tau;
+      const uint64_t b = __ballot(take);
+      const int pos = cnt + (int)__popcll(b & ((1ull << lane) - 1ull));
+      if (take && pos < kCapW) {
+        ck[pos] = u;
+        ci[pos] = (uint16_t)x;
+      }
+      cnt += (int)__popcll(b);
+    }
+    for (int pos = cnt + lane; pos < kCapW; pos += 64) ck[pos] = 0u;
+    if (cnt > kCapW && lane == 0) ovf = 1;
+  }
+  __syncthreads();
+  if (ovf == 0) {
+    dev::topk_select(ckeys, 4 * kCapW, k, p.topk, 0, out, hist, tmp4, bcast, cidx);
+  } else {
+    dev::topk_select(keys[0], p.M, k, p.topk, 0, out, hist, tmp4, bcast);
   }
 }
 

@@ -130,11 +130,14 @@ def test_block_selection_exact_ties_keep_lowest_ids(f0):
         assert list(sel[b]) == expect, (b, list(sel[b]), expect)
 
 
-def test_cluster_selection_exact_ties_keep_lowest_ids():
-    # identical centroids: every eligible cluster scores alike
+@pytest.mark.parametrize("M", [256, 2048])
+def test_cluster_selection_exact_ties_keep_lowest_ids(M):
+    # identical centroids: every eligible cluster scores alike.  With M = 2048
+    # each quarter of the clusters holds more candidates than the prefilter's
+    # per-wave region, so late blocks take the full select.
     import torch
     import hybrid_attention_prefill_amd as ha
-    N, M, k, w = 4096, 256, 7, 512
+    N, k, w = 4096, 7, 512
     rng = np.random.default_rng(4)
     cent = np.tile(rng.standard_normal((1, 16)).astype(np.float32), (M, 1))
     assign = np.arange(N) % M                       # first member of cluster m is key m
