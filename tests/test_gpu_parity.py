@@ -144,7 +144,7 @@ def test_cluster_selection_exact_ties_keep_lowest_ids(M):
     off = np.r_[0, np.cumsum(np.bincount(assign, minlength=M))].astype(np.int32)
     mem = np.lexsort((np.arange(N), assign)).astype(np.int32)
     kinds = [HEAD_RETRIEVAL] * 4
-    d = ha.make_desc(N, 4, 1, 128, window=w, topk=k, n_clusters=M, kmeans_iters=1, kmeans_stride=16)
+    d = ha.make_desc(N, 4, 1, 128, window=w, topk=k, n_clusters=M, kmeans_iters=1, kmeans_stride=N // M)
     ql = torch.from_numpy(rng.standard_normal((4, N, 16)).astype(np.float32)).cuda()
     sel = torch.full((4, N // 64, k), -7, dtype=torch.int32, device="cuda")
     ws = torch.empty(ha.ha_workspace_bytes(d, kinds), dtype=torch.uint8, device="cuda")
