@@ -10,11 +10,16 @@
 // selected part for one (retrieval head, 64-row query block) and merges:
 //   O = (O_win 2^lse_win + O_sel 2^lse_sel) / (2^lse_win + 2^lse_sel).
 //
-// The selected part reads scattered K/V rows (HBM-bound).  A workgroup takes
-// one (head, block): its 4 waves own 16 query rows each and share every
-// 64-key tile staged in LDS (v_mfma_f32_16x16x32_bf16, fp32 online softmax).
-// Key rows of tile t+2 are looked up (CSR members or block keys) while tile t
-// is computed and tile t+1 is in flight; two workgroups fit on a CU.
+// The selected part reads scattered K/V rows.  A workgroup takes one (head,
+// 64-row query block); each 64-key gathered tile is staged in LDS (K rows,
+// V transposed) and split between the waves: wave w owns query rows
+// 32 (w % 2) .. +31 and key half w / 2 (keys 32 (w / 2) .. +31 of every
+// tile), so a wave reads half a tile per step.  S^T = K Q^T and O^T += V^T P^T
+// on v_mfma_f32_32x32x16_bf16 (a lane owns one query column), fp32 online
+// softmax per key half; the two halves' (max, sum, O) are merged through LDS
+// at the end.  Key rows of tile t+2 are looked up (CSR members or block keys)
+// while tile t is computed and tile t+1 is in flight; two workgroups fit on
+// a CU.
 #include "common.h"
 #include "device_util.h"
 
@@ -24,7 +29,7 @@ namespace ha {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -40,38 +45,38 @@ constexpr float kNegInf = -__builtin_inff();
 constexpr float kMInit = -1e30f;
 constexpr float kSlack = 8.f;
 
-__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Key u (0..31) of a 32-key PV k-step sits at this V^T position: lane group
-// g = lane/16 feeds B slot e' with key (e'/4)*16 + 4g + e'%4 (the S^T layout
-// of two 16-key blocks), and reads 8 contiguous positions 8g .. 8g+7.
-__device__ __forceinline__ int vt_pos(int u) { return 8 * ((u & 15) >> 2) + 4 * (u >> 4) + (u & 3); }
+// Position of key u (0..15) of a 16-key PV k-step inside an LDS V^T row, so
+// that the 8 keys one MFMA lane consumes are contiguous.  A lane of half
+// g = lane/32 holds, for C-layout element e, key g*4 + (e/4)*8 + e%4; the
+// slot it feeds at k-step element e' (0..7) is 8g + e'.
+__device__ __forceinline__ int vt_pos(int u) { return 8 * ((u >> 2) & 1) + 4 * (u >> 3) + (u & 3); }
 
 struct TileRegs {
   u32x4 k[4];
   u32x4 v[4];
 };
 
-// K slots c*16 + tid/16 (16-B chunk tid%16); V slots 4*(tid%16) + x (d chunk tid/16)
-__device__ __forceinline__ int k_slot(int c, int tid) { return c * 16 + (tid >> 4); }
-__device__ __forceinline__ int v_slot(int x, int tid) { return (tid & 15) * 4 + x; }
-
+// K slots c*16 + tid/16 (16-B chunk tid%16); V slots 4*(tid%16) + x (d chunk
+// tid/16).  Empty slots (key -1) read key row 0: the mask drops them (P = 0)
+// and the finite stand-in values leave the products exact; no per-lane
+// branches, so the loads stay in flight until the LDS store.
 __device__ __forceinline__ void tile_load(TileRegs& r, const uint16_t* __restrict__ K,
                                           const uint16_t* __restrict__ V, const int* ring, size_t rs, int g,
                                           int tid) {
-  const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const int key = ring[k_slot(c, tid)];
-    r.k[c] = key >= 0 ? *reinterpret_cast<const u32x4*>(K + (size_t)key * rs + g * D + (tid & 15) * 8) : z;
+    const int key = max(0, ring[c * 16 + (tid >> 4)]);
+    r.k[c] = *reinterpret_cast<const u32x4*>(K + (size_t)key * rs + g * D + (tid & 15) * 8);
   }
   const int dc = tid >> 4;
 #pragma unroll
   for (int x = 0; x < 4; ++x) {
-    const int key = ring[v_slot(x, tid)];
-    r.v[x] = key >= 0 ? *reinterpret_cast<const u32x4*>(V + (size_t)key * rs + g * D + dc * 8) : z;
+    const int key = max(0, ring[(tid & 15) * 4 + x]);
+    r.v[x] = *reinterpret_cast<const u32x4*>(V + (size_t)key * rs + g * D + dc * 8);
   }
 }
 
@@ -84,7 +89,7 @@ __device__ __forceinline__ void tile_store(const TileRegs& r, uint16_t* buf, int
     *reinterpret_cast<u32x4*>(Ks + (id >> 4) * KSTR + (id & 15) * 8) = r.k[c];
   }
   const int kg = tid & 15, dc = tid >> 4;
-  const int pos = 32 * (kg >> 3) + vt_pos((kg * 4) & 31);
+  const int pos = 16 * (kg >> 2) + vt_pos((kg * 4) & 15);
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     const uint32_t a0 = r.v[0][w], a1 = r.v[1][w], a2 = r.v[2][w], a3 = r.v[3][w];
@@ -99,40 +104,40 @@ __device__ __forceinline__ void tile_store(const TileRegs& r, uint16_t* buf, int
 }
 
 struct Acc {
-  f32x4 o[8];   // O^T: d block db -> rows d = 16 db + 4 (lane/16) + e, column = the lane's query
+  f32x16 o[4];  // O^T: d block db -> rows d = 32 db + 4 (lane/32) + 8 (e/4) + e%4, column = the lane's query
   float m, l;   // running max (raw scores) and this lane's partial sum
 };
 
-// One 64-key tile against the wave's 16 query rows.  Key j of slot s is
-// visible to row i iff j >= 0 and j <= i - w (outside the window).
+// The wave's key half (keys 32 kh .. +31) of one tile against its 32 query
+// rows.  Key j of slot s is visible to row i iff j >= 0 and j <= i - w
+// (outside the window).
 __device__ __forceinline__ void tile_compute(const uint16_t* __restrict__ buf, const int* __restrict__ kpos,
-                                             const bf16x8 (&qf)[4], Acc& acc, int lane, int i, int w, float c) {
+                                             const bf16x8 (&qf)[8], Acc& acc, int lane, int kh, int i, int w,
+                                             float c) {
   const uint16_t* Ks = buf;
   const uint16_t* Vt = buf + K_ELEMS;
-  const int lq = lane & 15, lg = lane >> 4;
-  f32x4 s[4];
+  const int lr = lane & 31, lh = lane >> 5;
+  f32x16 s;
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int e = 0; e < 16; ++e) s[e] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + (kb * 16 + lq) * KSTR + ks * 32 + lg * 8);
-      s[kb] = mfma16(kf, qf[ks], s[kb]);
-    }
+  for (int t = 0; t < 8; ++t) {
+    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + (kh * 32 + lr) * KSTR + t * 16 + lh * 8);
+    s = mfma(kf, qf[t], s);
   }
   float mx = kNegInf;
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    const int4 jv = *reinterpret_cast<const int4*>(kpos + kb * 16 + lg * 4);
+  for (int q = 0; q < 4; ++q) {
+    const int4 jv = *reinterpret_cast<const int4*>(kpos + kh * 32 + lh * 4 + q * 8);
     const int js[4] = {jv.x, jv.y, jv.z, jv.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const bool vis = (js[e] >= 0) & (i - js[e] >= w);
-      s[kb][e] = vis ? s[kb][e] : kNegInf;
-      mx = fmaxf(mx, s[kb][e]);
+      s[q * 4 + e] = vis ? s[q * 4 + e] : kNegInf;
+      mx = fmaxf(mx, s[q * 4 + e]);
     }
   }
-  mx = dev::pair32_max(dev::pair16_max(mx));
+  mx = dev::pair32_max(mx);
   // lazily moved reference max (see the banded kernel): rescale only when a
   // row max exceeds it by more than kSlack in log2 units
   if (__any((mx - acc.m) * c > kSlack)) {
@@ -141,27 +146,27 @@ __device__ __forceinline__ void tile_compute(const uint16_t* __restrict__ buf, c
     acc.m = mnew;
     acc.l *= alpha;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) acc.o[db] *= alpha;
+    for (int db = 0; db < 4; ++db) acc.o[db] *= alpha;
   }
   const float nb = -acc.m * c;
   float sum = 0.f;
   bf16x8 pf[2];
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][e], c, nb));
-      sum += pv;
-      pf[kb >> 1][(kb & 1) * 4 + e] = (__bf16)pv;
-    }
+  for (int e = 0; e < 16; ++e) {
+    const float pv = __builtin_amdgcn_exp2f(fmaf(s[e], c, nb));
+    sum += pv;
+    pf[e >> 3][e & 7] = (__bf16)pv;
+  }
   acc.l += sum;
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
+  for (int h2 = 0; h2 < 2; ++h2) {
+    const int t4 = kh * 2 + h2;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      const bf16x8 vf = *reinterpret_cast<const bf16x8*>(Vt + (db * 16 + lq) * VSTR + ks * 32 + lg * 8);
-      acc.o[db] = mfma16(vf, pf[ks], acc.o[db]);
+    for (int db = 0; db < 4; ++db) {
+      const bf16x8 vf = *reinterpret_cast<const bf16x8*>(Vt + (db * 32 + lr) * VSTR + t4 * 16 + lh * 8);
+      acc.o[db] = mfma(vf, pf[h2], acc.o[db]);
     }
+  }
 }
 
 __global__ __launch_bounds__(NT, 2) void attn_selected_kernel(AttnParams p, SelList sl) {
@@ -235,23 +240,26 @@ __global__ __launch_bounds__(NT, 2) void attn_selected_kernel(AttnParams p, SelL
     return ent[a] * BK + r;
   };
 
-  const int lq = lane & 15, lg = lane >> 4;
-  const int i = q0 + wave * 16 + lq;          // this lane's query row
-  bf16x8 qf[4];
+  const int lr = lane & 31, lh = lane >> 5;
+  const int kh = wave >> 1;                   // key half of every tile
+  const int i = q0 + (wave & 1) * 32 + lr;    // this lane's query row
+  bf16x8 qf[8];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
+  for (int t8 = 0; t8 < 8; ++t8) {
     if (i < p.N) {
-      qf[ks] = *reinterpret_cast<const bf16x8*>(p.Q + ((size_t)i * p.Hq + h) * D + ks * 32 + lg * 8);
+      qf[t8] = *reinterpret_cast<const bf16x8*>(p.Q + ((size_t)i * p.Hq + h) * D + t8 * 16 + lh * 8);
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)0.f;
+      for (int e = 0; e < 8; ++e) qf[t8][e] = (__bf16)0.f;
     }
   }
   Acc acc;
   acc.m = kMInit;
   acc.l = 0.f;
 #pragma unroll
-  for (int db = 0; db < 8; ++db) acc.o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc.o[db][e] = 0.f;
 
   const size_t rs = (size_t)p.Hkv * D;
   if (tid < BK) {
@@ -268,14 +276,41 @@ __global__ __launch_bounds__(NT, 2) void attn_selected_kernel(AttnParams p, SelL
     if (tt + 1 < T) tile_load(r, p.K, p.V, ring[(tt + 1) % 3], rs, g, tid);
     const bool prep = tt + 2 < T && tid < BK;
     if (prep) pending = lookup(tt + 2, tid);
-    tile_compute(smem + (tt & 1) * BUF_ELEMS, ring[tt % 3], qf, acc, lane, i, p.window, p.c);
+    tile_compute(smem + (tt & 1) * BUF_ELEMS, ring[tt % 3], qf, acc, lane, kh, i, p.window, p.c);
     if (tt + 1 < T) tile_store(r, smem + ((tt + 1) & 1) * BUF_ELEMS, tid);
     if (prep) ring[(tt + 2) % 3][tid] = pending;
     __syncthreads();
   }
 
+  // merge the key halves: waves 2, 3 hand (m, l, O) to waves 0, 1 through
+  // LDS (the tile buffers are free after the loop's last barrier)
+  float* xch = reinterpret_cast<float*>(smem) + (wave & 1) * (64 * 67);
+  if (kh == 1) {
+    float* x = xch + lane * 67;
+    x[0] = acc.m;
+    x[1] = acc.l;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) x[2 + db * 16 + e] = acc.o[db][e];
+  }
+  __syncthreads();
+  if (kh == 1) return;
+  {
+    const float* x = xch + lane * 67;
+    const float m1 = x[0], l1 = x[1];
+    const float mm = fmaxf(acc.m, m1);
+    const float a0 = __builtin_amdgcn_exp2f((acc.m - mm) * p.c), a1 = __builtin_amdgcn_exp2f((m1 - mm) * p.c);
+    acc.m = mm;
+    acc.l = acc.l * a0 + l1 * a1;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc.o[db][e] = acc.o[db][e] * a0 + x[2 + db * 16 + e] * a1;
+  }
+
   // merge with the window result of the row
-  const float lt = dev::pair32_sum(dev::pair16_sum(acc.l));
+  const float lt = dev::pair32_sum(acc.l);
   if (i >= p.N || !(lt > 0.f)) return;
   const float lse_s = acc.m * p.c + __log2f(lt);
   const float lse_w = p.lse[(size_t)t * p.N + i];
@@ -285,15 +320,17 @@ __global__ __launch_bounds__(NT, 2) void attn_selected_kernel(AttnParams p, SelL
   const float fs = ws * inv / lt, fw = ww * inv;
   float* row = p.O + ((size_t)i * p.Hq + h) * D;
 #pragma unroll
-  for (int db = 0; db < 8; ++db) {
-    float4* dst = reinterpret_cast<float4*>(row + db * 16 + lg * 4);
-    float4 v = *dst;
-    v.x = fmaf(v.x, fw, acc.o[db][0] * fs);
-    v.y = fmaf(v.y, fw, acc.o[db][1] * fs);
-    v.z = fmaf(v.z, fw, acc.o[db][2] * fs);
-    v.w = fmaf(v.w, fw, acc.o[db][3] * fs);
-    *dst = v;
-  }
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      float4* dst = reinterpret_cast<float4*>(row + db * 32 + lh * 4 + r4 * 8);
+      float4 v = *dst;
+      v.x = fmaf(v.x, fw, acc.o[db][r4 * 4 + 0] * fs);
+      v.y = fmaf(v.y, fw, acc.o[db][r4 * 4 + 1] * fs);
+      v.z = fmaf(v.z, fw, acc.o[db][r4 * 4 + 2] * fs);
+      v.w = fmaf(v.w, fw, acc.o[db][r4 * 4 + 3] * fs);
+      *dst = v;
+    }
 }
 
 }  // namespace
