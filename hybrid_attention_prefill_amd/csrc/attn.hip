@@ -33,6 +33,7 @@ namespace ha {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -69,25 +70,31 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 // Per-thread source of its share of a tile: V threads read key slots
 // 4*(t%16) + x at d = 8*(t/16) .. +8; K threads read chunk id = c*256 + t ->
 // key slot id/16, d = (id%16)*8 (coalesced rows).  Slot x of the tile is key
-// k0 + kbase + x*kstep.
+// k0 + kbase + x*kstep.  The tensor base is uniform per wave (waves 0-3 read
+// V, 4-7 K), so a load is that scalar base plus a 32-bit per-lane offset.
 struct TileSrc {
-  const uint16_t* base;   // element (key 0, the thread's d chunk)
-  int kbase, kstep;
+  const char* base;       // tensor + KV head offset (wave-uniform)
+  uint32_t off[4];        // byte offsets of the thread's slots for k0 = 0
+  int kbase, kstep, dbyte;
 };
 
 __device__ __forceinline__ TileSrc tile_src(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-                                            int g, int tid) {
+                                            int g, int rs, int tid, bool v_wave) {
   TileSrc s;
-  if (tid < 256) {
+  const uint16_t* t = v_wave ? V : K;
+  s.base = reinterpret_cast<const char*>(t + g * D);
+  if (v_wave) {
     s.kbase = (tid & 15) * 4;
     s.kstep = 1;
-    s.base = V + g * D + (tid >> 4) * 8;
+    s.dbyte = (tid >> 4) * 16;
   } else {
-    const int t = tid - 256;
-    s.kbase = t >> 4;
+    const int u = tid - 256;
+    s.kbase = u >> 4;
     s.kstep = 16;
-    s.base = K + g * D + (t & 15) * 8;
+    s.dbyte = (u & 15) * 16;
   }
+#pragma unroll
+  for (int x = 0; x < 4; ++x) s.off[x] = (uint32_t)((s.kbase + x * s.kstep) * rs * 2 + s.dbyte);
   return s;
 }
 
@@ -97,12 +104,17 @@ __device__ __forceinline__ TileSrc tile_src(const uint16_t* __restrict__ K, cons
 // the products exact.  No per-lane branches, so the loads stay in flight
 // until the LDS store needs them.
 __device__ __forceinline__ void tile_load(TileRegs& r, const TileSrc& src, int k0, int N, int rs) {
-  const uint16_t* p = src.base + (size_t)k0 * rs;
-  const int lim = N - 1 - k0;
+  const char* p = src.base + (size_t)k0 * rs * 2;
+  if (k0 + BK <= N) {
 #pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    const int kr = min(src.kbase + x * src.kstep, lim);
-    r.x[x] = *reinterpret_cast<const u32x4*>(p + __umul24((unsigned)kr, (unsigned)rs));
+    for (int x = 0; x < 4; ++x) r.x[x] = *reinterpret_cast<const u32x4*>(p + src.off[x]);
+  } else {
+    const int lim = N - 1 - k0;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int kr = min(src.kbase + x * src.kstep, lim);
+      r.x[x] = *reinterpret_cast<const u32x4*>(p + (uint32_t)(kr * rs * 2 + src.dbyte));
+    }
   }
 }
 
@@ -114,19 +126,20 @@ __device__ __forceinline__ int vt_pos(int u) {
   return 8 * ((u >> 2) & 1) + 4 * (u >> 3) + (u & 3);
 }
 
-__device__ __forceinline__ void tile_store(const TileRegs& r, uint16_t* buf, int tid) {
-  if (tid < 256) {
+__device__ __forceinline__ void tile_store(const TileRegs& r, uint16_t* buf, int tid, bool v_wave) {
+  if (v_wave) {
     uint16_t* Vt = buf + K_ELEMS;
     const int kg = tid & 15, dc = tid >> 4;
     const int pos = 16 * (kg >> 2) + vt_pos((kg * 4) & 15);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
+      // keys x = 0..3 of d = dc*8 + 2w (low halves) and dc*8 + 2w + 1 (high)
       const uint32_t a0 = r.x[0][w], a1 = r.x[1][w], a2 = r.x[2][w], a3 = r.x[3][w];
       u32x2 ev, od;
-      ev[0] = (a0 & 0xFFFFu) | (a1 << 16);
-      ev[1] = (a2 & 0xFFFFu) | (a3 << 16);
-      od[0] = (a0 >> 16) | (a1 & 0xFFFF0000u);
-      od[1] = (a2 >> 16) | (a3 & 0xFFFF0000u);
+      ev[0] = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
+      ev[1] = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
+      od[0] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
+      od[1] = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
       *reinterpret_cast<u32x2*>(Vt + (dc * 8 + 2 * w) * VSTR + pos) = ev;
       *reinterpret_cast<u32x2*>(Vt + (dc * 8 + 2 * w + 1) * VSTR + pos) = od;
     }
@@ -241,21 +254,24 @@ __device__ __forceinline__ void tile_compute(const uint16_t* __restrict__ buf, c
 #pragma unroll
     for (int db = 0; db < 4; ++db) acc.o[db] *= alpha;
   }
+  // P in bf16 feeds the PV product; the row sum adds the same bf16 values
+  // (v_dot2 against (1, 1)), so numerator and denominator use equal weights
   const float nb = -acc.m * c;
   float sum = 0.f;
   bf16x8 pf[2][2];
+  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][e], c, nb));
-      s[kb][e] = pv;
-      sum += pv;
+    for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[kb][h2][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][h2 * 8 + e], c, nb));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bf16x2 pr = {pf[kb][h2][2 * q], pf[kb][h2][2 * q + 1]};
+        sum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, sum, false);
+      }
     }
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pf[kb][h2][e] = (__bf16)s[kb][h2 * 8 + e];
   }
   acc.l += sum;
 
@@ -332,10 +348,11 @@ __device__ __forceinline__ void run_tiles(const AttnParams& p, uint16_t* smem, i
   if (active) load_q(qf, p.Q, p.N, p.Hq, h, q0, lane);
 
   TileRegs r;
-  const TileSrc src = tile_src(p.K, p.V, g, tid);
+  const bool v_wave = __builtin_amdgcn_readfirstlane(tid >> 6) < 4;
+  const TileSrc src = tile_src(p.K, p.V, g, rs, tid, v_wave);
   int k0 = k0_of(0);
   tile_load(r, src, k0, p.N, rs);
-  tile_store(r, smem, tid);
+  tile_store(r, smem, tid, v_wave);
   __syncthreads();
   for (int t = 0; t < T; ++t) {
     const int cur = k0;
@@ -344,7 +361,7 @@ __device__ __forceinline__ void run_tiles(const AttnParams& p, uint16_t* smem, i
       tile_load(r, src, k0, p.N, rs);
     }
     if (active && !tile_empty(ms, q0, cur)) tile_compute(smem + (t & 1) * BUF_ELEMS, qf, acc, lane, q0, cur, ms, p.c);
-    if (t + 1 < T) tile_store(r, smem + ((t + 1) & 1) * BUF_ELEMS, tid);
+    if (t + 1 < T) tile_store(r, smem + ((t + 1) & 1) * BUF_ELEMS, tid, v_wave);
     __syncthreads();
   }
   if (active) store_o(acc, p.O, p.lse, slot, p.N, p.Hq, h, q0, lane, p.c);
