@@ -29,6 +29,7 @@ namespace ha {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -92,12 +93,13 @@ __device__ __forceinline__ void tile_store(const TileRegs& r, uint16_t* buf, int
   const int pos = 16 * (kg >> 2) + vt_pos((kg * 4) & 15);
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
+    // keys x = 0..3 of d = dc*8 + 2w (low halves) and dc*8 + 2w + 1 (high)
     const uint32_t a0 = r.v[0][w], a1 = r.v[1][w], a2 = r.v[2][w], a3 = r.v[3][w];
     u32x2 ev, od;
-    ev[0] = (a0 & 0xFFFFu) | (a1 << 16);
-    ev[1] = (a2 & 0xFFFFu) | (a3 << 16);
-    od[0] = (a0 >> 16) | (a1 & 0xFFFF0000u);
-    od[1] = (a2 >> 16) | (a3 & 0xFFFF0000u);
+    ev[0] = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
+    ev[1] = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
+    od[0] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
+    od[1] = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
     *reinterpret_cast<u32x2*>(Vt + (dc * 8 + 2 * w) * VSTR + pos) = ev;
     *reinterpret_cast<u32x2*>(Vt + (dc * 8 + 2 * w + 1) * VSTR + pos) = od;
   }
@@ -148,14 +150,17 @@ __device__ __forceinline__ void tile_compute(const uint16_t* __restrict__ buf, c
 #pragma unroll
     for (int db = 0; db < 4; ++db) acc.o[db] *= alpha;
   }
+  // P in bf16 feeds the PV product; the row sum adds the same bf16 values
   const float nb = -acc.m * c;
   float sum = 0.f;
   bf16x8 pf[2];
+  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const float pv = __builtin_amdgcn_exp2f(fmaf(s[e], c, nb));
-    sum += pv;
-    pf[e >> 3][e & 7] = (__bf16)pv;
+  for (int e = 0; e < 16; ++e) pf[e >> 3][e & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[e], c, nb));
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const bf16x2 pr = {pf[q >> 2][2 * (q & 3)], pf[q >> 2][2 * (q & 3) + 1]};
+    sum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, sum, false);
   }
   acc.l += sum;
 #pragma unroll
@@ -225,19 +230,20 @@ __global__ __launch_bounds__(NT, 2) void attn_selected_kernel(AttnParams p, SelL
   const int T = (total + BK - 1) / BK;
   if (T == 0) return;
 
-  // key row of slot s of tile idx (flat index f = 64 idx + s over the entries)
+  // key row of slot s of tile idx (flat index f = 64 idx + s over the
+  // entries).  Slot s of every tile is looked up by thread 4 s, so all waves
+  // share the work; that thread's entry index (the largest e with
+  // pre[e] <= f) only moves forward from tile to tile.
+  const bool owner = (tid & 3) == 0;
+  const int slot = tid >> 2;
+  int cur_e = 0;
   auto lookup = [&](int idx, int s) -> int {
     const int f = idx * BK + s;
     if (f >= total) return -1;
-    int a = 0, bb = ne;              // largest e with pre[e] <= f
-    while (bb - a > 1) {
-      const int mid = (a + bb) >> 1;
-      if (pre[mid] <= f) a = mid;
-      else bb = mid;
-    }
-    const int r = f - pre[a];
-    if (p.M > 0) return (int)mem[ent[a] + r];
-    return ent[a] * BK + r;
+    while (cur_e + 1 < ne && pre[cur_e + 1] <= f) ++cur_e;
+    const int r = f - pre[cur_e];
+    if (p.M > 0) return (int)mem[ent[cur_e] + r];
+    return ent[cur_e] * BK + r;
   };
 
   const int lr = lane & 31, lh = lane >> 5;
@@ -262,9 +268,9 @@ __global__ __launch_bounds__(NT, 2) void attn_selected_kernel(AttnParams p, SelL
     for (int e = 0; e < 16; ++e) acc.o[db][e] = 0.f;
 
   const size_t rs = (size_t)p.Hkv * D;
-  if (tid < BK) {
-    ring[0][tid] = lookup(0, tid);
-    if (T > 1) ring[1][tid] = lookup(1, tid);
+  if (owner) {
+    ring[0][slot] = lookup(0, slot);
+    if (T > 1) ring[1][slot] = lookup(1, slot);
   }
   __syncthreads();
   TileRegs r;
@@ -274,11 +280,11 @@ __global__ __launch_bounds__(NT, 2) void attn_selected_kernel(AttnParams p, SelL
   for (int tt = 0; tt < T; ++tt) {
     int pending = -1;
     if (tt + 1 < T) tile_load(r, p.K, p.V, ring[(tt + 1) % 3], rs, g, tid);
-    const bool prep = tt + 2 < T && tid < BK;
-    if (prep) pending = lookup(tt + 2, tid);
+    const bool prep = tt + 2 < T && owner;
+    if (prep) pending = lookup(tt + 2, slot);
     tile_compute(smem + (tt & 1) * BUF_ELEMS, ring[tt % 3], qf, acc, lane, kh, i, p.window, p.c);
     if (tt + 1 < T) tile_store(r, smem + ((tt + 1) & 1) * BUF_ELEMS, tid);
-    if (prep) ring[(tt + 2) % 3][tid] = pending;
+    if (prep) ring[(tt + 2) % 3][slot] = pending;
     __syncthreads();
   }
 
