@@ -335,7 +335,7 @@ __global__ __launch_bounds__(NT) void cluster_prep_kernel(SelectParams p) {
 // that finds more than kCapW candidates sends the block to the full select.
 constexpr int kSelBlocks = 1;
 constexpr int kGroups = 128;      // scoring lanes (4 waves x 32)
-constexpr int kCapW = 256;        // candidate slots per wave
+constexpr int kCapW = 192;        // candidate slots per wave
 
 __global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
   static_assert(kSelBlocks == 1, "the prefilter handles one query block per workgroup");
@@ -348,8 +348,11 @@ __global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
   __shared__ uint32_t gmax[kGroups];
   __shared__ uint32_t tau_s;
   __shared__ int ovf;
+  __shared__ uint64_t elmask[kMaxSelCand / 64];   // bit m: cluster m eligible for this block
+  __shared__ uint32_t sink_word;                  // store target of padding lanes
   const int t = blockIdx.y, tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, lr = lane & 31, lh = lane >> 5;
+  const int lane = tid & 63, lr = lane & 31, lh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar loop control
   const int g = p.group_of_ret[t];
   const int b0 = blockIdx.x * kSelBlocks;
   const int nb = min(kSelBlocks, p.n_qb - b0);
@@ -382,54 +385,72 @@ __global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
   const __bf16* chi = p.c_hi + (size_t)g * p.M * R;
   const __bf16* clo = p.c_lo + (size_t)g * p.M * R;
   const int32_t* fm = p.first_mem + (size_t)g * p.M;
+  // eligibility bitmask (cluster m has a member <= lim), from coalesced reads
+  // of the first members, one ballot per 64 clusters
+  // (16 loads in flight per batch)
+  for (int c0 = wave * 64; c0 < p.M; c0 += 16 * 4 * 64) {
+    int f[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) f[j] = fm[min(c0 + j * 256 + lane, p.M - 1)];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int c = c0 + j * 256 + lane;
+      const uint64_t b = __ballot(c < p.M && lim[0] >= 0 && f[j] <= lim[0]);
+      if (lane == 0 && c0 + j * 256 < p.M) elmask[(c0 + j * 256) >> 6] = b;
+    }
+  }
+  __syncthreads();
   int n_el[kSelBlocks] = {};
   uint32_t gmx = 0;                 // largest key this lane wrote
   const int n_tiles = (p.M + 31) / 32;
   // A wave's tiles are x = wave + 4 i.  Operands are loaded kPre tiles ahead
   // (register ring, static slots: the loop is unrolled by kPre).
   constexpr int kPre = 4;
-  auto ld = [&](int x, dev::bf16x8& bh, dev::bf16x8& bl, int& f) {
+  auto ld = [&](int x, dev::bf16x8& bh, dev::bf16x8& bl) {
     const int m = min(p.M - 1, x * 32 + lr);
     bh = *reinterpret_cast<const dev::bf16x8*>(chi + (size_t)m * R + lh * 8);
     bl = *reinterpret_cast<const dev::bf16x8*>(clo + (size_t)m * R + lh * 8);
-    f = fm[m];
   };
   dev::bf16x8 rbh[kPre], rbl[kPre];
-  int rf[kPre];
+  // slot order, as in the loop body, so the first group waits only for its own slot
 #pragma unroll
-  for (int u = 0; u < kPre; ++u) ld(min(n_tiles - 1, wave + 4 * u), rbh[u], rbl[u], rf[u]);
+  for (int u = 0; u < kPre; ++u) {
+    ld(min(n_tiles - 1, wave + 4 * u), rbh[u], rbl[u]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // Groups of kPre tiles run whole (tiles past the end compute on the last
+  // tile and store nothing: their centroid index is >= M), so the body has no
+  // branches around loads.  A slot is refilled right after its MFMAs have
+  // consumed it, so the ring needs no register copies.
   for (int x0 = wave; x0 < n_tiles; x0 += 4 * kPre) {
 #pragma unroll
     for (int u = 0; u < kPre; ++u) {
       const int x = x0 + 4 * u;
-      if (x < n_tiles) {
-        const dev::bf16x8 bh = rbh[u], bl = rbl[u];
-        const int fmm = rf[u];
-        if (x + 4 * kPre < n_tiles) ld(x + 4 * kPre, rbh[u], rbl[u], rf[u]);
-        const int m = x * 32 + lr;
-        const bool mok = m < p.M;
+      const int m = x * 32 + lr;
+      const bool mok = m < p.M;
+      float mx = -__builtin_inff();
 #pragma unroll
-        for (int bi = 0; bi < kSelBlocks; ++bi) {
-          float mx = -__builtin_inff();
+      for (int rt = 0; rt < 2; ++rt) {
+        dev::f32x16 acc = {};
+        acc = dev::mfma32(ql[0][rt], rbh[u], acc);
+        acc = dev::mfma32(qh[0][rt], rbl[u], acc);
+        acc = dev::mfma32(qh[0][rt], rbh[u], acc);
 #pragma unroll
-          for (int rt = 0; rt < 2; ++rt) {
-            dev::f32x16 acc = {};
-            acc = dev::mfma32(ql[bi][rt], bh, acc);
-            acc = dev::mfma32(qh[bi][rt], bl, acc);
-            acc = dev::mfma32(qh[bi][rt], bh, acc);
-#pragma unroll
-            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[e]);
-          }
-          mx = dev::pair32_max(mx);
-          if (lh == 0 && mok) {
-            const bool el = lim[bi] >= 0 && fmm <= lim[bi];
-            const uint32_t key = el ? dev::order_key(mx) : 0u;
-            keys[bi][m] = key;
-            gmx = max(gmx, key);
-            n_el[bi] += el;
-          }
-        }
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[e]);
       }
+      // keep the refill after the slot's last reads (no register rotation)
+      __builtin_amdgcn_sched_barrier(0);
+      ld(min(x + 4 * kPre, n_tiles - 1), rbh[u], rbl[u]);
+      mx = dev::pair32_max(mx);
+      // branch-free: both lane halves store the same key; padding lanes store
+      // to a dummy word and count nothing
+      const int mc = min(m, p.M - 1);
+      const bool el = (bool)((elmask[mc >> 6] >> (mc & 63)) & 1ull) & mok;
+      const uint32_t key = el ? dev::order_key(mx) : 0u;
+      uint32_t* dst = mok ? &keys[0][mc] : &sink_word;
+      *dst = key;
+      gmx = max(gmx, key);
+      n_el[0] += (int)(el & (lh == 0));
     }
   }
   if (lh == 0) gmax[wave * 32 + lr] = gmx;
