@@ -23,11 +23,12 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wno-unused-command-line-argument"]
-# Per-source extra flags.  The k-means and cluster-scoring kernels read their
-# MFMA results with VALU ops (min / argmin, row max), which cannot read AGPRs;
+# Per-source extra flags.  The k-means, cluster- and block-scoring kernels
+# read their MFMA results with VALU ops (min / argmin, max), which cannot read AGPRs;
 # keeping the accumulators in ordinary VGPRs avoids a copy of every result.
 FILE_FLAGS = {
     "kmeans.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

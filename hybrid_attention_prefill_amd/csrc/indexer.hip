@@ -95,53 +95,120 @@ __global__ __launch_bounds__(NT) void project_kernel(ProjParams p, int rows_per_
 }
 
 // One workgroup per (retrieval head, query block).  Wave w scores the
-// eligible blocks c = c_lo + w, c_lo + w + 4, ...; each lane holds one query
-// row's low-rank vector, keys are read wave-uniformly.
+// eligible blocks c = c_lo + w, c_lo + w + 4, ... on MFMA: S[i][j] =
+// qlow_i . klow_j for the 64 x 64 pairs as 2 x 2 tiles of
+// v_mfma_f32_32x32x16_bf16 (k = r = 16) over hi/lo bf16 splits of both
+// operands (three passes, ~1e-5 relative), then the block's max: 32 max3
+// per lane and a reduction over the wave.  Rows past the end of a ragged
+// block repeat its first row (no mask); pairs with j > i or j >= N are
+// masked only in the tiles that reach past the block's first row.
+__device__ __forceinline__ void split_row8(const float* __restrict__ src, dev::bf16x8& hi, dev::bf16x8& lo) {
+  const float4 a = *reinterpret_cast<const float4*>(src);
+  const float4 b = *reinterpret_cast<const float4*>(src + 4);
+  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    __bf16 h, l;
+    dev::split2(v[e], h, l);
+    hi[e] = h;
+    lo[e] = l;
+  }
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = dev::pair32_max(dev::pair16_max(v));
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// keys: dynamic LDS of n_qb words (the eligible blocks of one query block)
 __global__ __launch_bounds__(NT) void select_blocks_kernel(SelectParams p) {
-  __shared__ uint32_t keys[kMaxSelCand];
+  extern __shared__ uint32_t keys[];
   __shared__ int hist[dev::kHistWords];
   __shared__ int tmp4[8];
   __shared__ int bcast[2];
   const int b = blockIdx.x, t = blockIdx.y;
   const int g = p.group_of_ret[t];
   const int qs = b * kBlock;
-  const int qe = min(p.N, qs + kBlock) - 1;
+  const int nrow = min(kBlock, p.N - qs);
+  const int qe = qs + nrow - 1;
   const int c_lo = p.force_block0 ? 1 : 0;
   const int c_hi = (qe - p.window >= 0) ? (qe - p.window) / kBlock : -1;
   const int nE = max(0, c_hi - c_lo + 1);
   int32_t* out = p.sel + ((size_t)t * p.n_qb + b) * p.topk;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (p.topk == 0) return;
   if (nE <= p.topk) {
     for (int x = tid; x < p.topk; x += NT) out[x] = x < nE ? c_lo + x : -1;
     return;
   }
-  const int i = qs + lane;
-  const bool row_ok = i < p.N;
-  float q[R];
-  {
-    const float* qp = p.qlow + ((size_t)t * p.N + (row_ok ? i : qs)) * R;
+  // A operands: query rows qs + 32 rt + lr, k-half lh
+  dev::bf16x8 qh[2], ql[2];
 #pragma unroll
-    for (int r = 0; r < R; r += 4) {
-      const float4 v = *reinterpret_cast<const float4*>(qp + r);
-      q[r] = v.x; q[r + 1] = v.y; q[r + 2] = v.z; q[r + 3] = v.w;
-    }
+  for (int rt = 0; rt < 2; ++rt) {
+    const int i = rt * 32 + lr;
+    const int row = qs + (i < nrow ? i : 0);
+    split_row8(p.qlow + ((size_t)t * p.N + row) * R + lh * 8, qh[rt], ql[rt]);
   }
   const float* kbase = p.klow + (size_t)g * p.N * R;
+  // B operands: keys j0 + 32 kt + lr of block c (rows past N read key N-1,
+  // masked below); the next block's rows are loaded one iteration ahead
+  auto kload = [&](int c, float4 (&v)[2][2]) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const float* src = kbase + (size_t)min(c * kBlock + kt * 32 + lr, p.N - 1) * R + lh * 8;
+      v[kt][0] = *reinterpret_cast<const float4*>(src);
+      v[kt][1] = *reinterpret_cast<const float4*>(src + 4);
+    }
+  };
+  float4 nk[2][2];
+  kload(c_lo + min(wave, nE - 1), nk);
   for (int x = wave; x < nE; x += 4) {
     const int c = c_lo + x;
     const int j0 = c * kBlock;
-    const int nj = min(kBlock, p.N - j0);
-    float mx = -__builtin_inff();
-    for (int jj = 0; jj < nj; ++jj) {
-      const float* kp = kbase + (size_t)(j0 + jj) * R;
-      float dot = 0.f;
+    dev::bf16x8 kh[2], kl[2];
 #pragma unroll
-      for (int r = 0; r < R; ++r) dot = fmaf(q[r], kp[r], dot);
-      if (row_ok && j0 + jj <= i) mx = fmaxf(mx, dot);
+    for (int kt = 0; kt < 2; ++kt) {
+      const float v[8] = {nk[kt][0].x, nk[kt][0].y, nk[kt][0].z, nk[kt][0].w,
+                          nk[kt][1].x, nk[kt][1].y, nk[kt][1].z, nk[kt][1].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        __bf16 h, l;
+        dev::split2(v[e], h, l);
+        kh[kt][e] = h;
+        kl[kt][e] = l;
+      }
     }
+    kload(c_lo + min(x + 4, nE - 1), nk);
+    const bool edge = j0 + kBlock - 1 > qs;     // some pair may have j > i or j >= N
+    float mx = -__builtin_inff();
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        // S^T tile: rows = keys (A = k), columns = queries (B = q)
+        dev::f32x16 acc = {};
+        acc = dev::mfma32(kl[kt], qh[rt], acc);
+        acc = dev::mfma32(kh[kt], ql[rt], acc);
+        acc = dev::mfma32(kh[kt], qh[rt], acc);
+        if (edge) {
+          // lane: query column qs + 32 rt + lr; element e: key j0 + 32 kt + 4 lh + 8 (e/4) + e%4
+          const int i = qs + rt * 32 + lr;
+          const bool row_ok = rt * 32 + lr < nrow;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int j = j0 + kt * 32 + lh * 4 + (e >> 2) * 8 + (e & 3);
+            const bool vis = row_ok & (j <= i) & (j < p.N);
+            mx = fmaxf(mx, vis ? acc[e] : -__builtin_inff());
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[e]);
+        }
+      }
+    mx = wave_max(mx);
     if (lane == 0) keys[x] = dev::order_key(mx);
   }
   __syncthreads();
@@ -162,7 +229,13 @@ hipError_t launch_project(const ProjParams& p, hipStream_t s) {
 
 hipError_t launch_select_blocks(const SelectParams& p, hipStream_t s) {
   if (p.n_ret == 0 || p.n_qb == 0) return hipSuccess;
-  hipLaunchKernelGGL(select_blocks_kernel, dim3(p.n_qb, p.n_ret), dim3(NT), 0, s, p);
+  const size_t lds = (size_t)p.n_qb * sizeof(uint32_t);
+  if (lds > 32 * 1024) {   // large tables: allow the dynamic size explicitly
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(select_blocks_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(select_blocks_kernel, dim3(p.n_qb, p.n_ret), dim3(NT), lds, s, p);
   return hipGetLastError();
 }
 
