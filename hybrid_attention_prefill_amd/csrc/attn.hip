@@ -15,9 +15,9 @@
 // registers (Q fragments, a 64 x 32 score tile and a 128 x 32 output
 // accumulator), so two waves share each SIMD and the hardware overlaps one
 // wave's softmax with the other's matrix products and LDS reads.  Tiles are
-// double-buffered: global loads of tile t+1 are in flight (in registers)
-// while tile t is computed from LDS; waves 0-3 stage V (transposed), waves
-// 4-7 stage K.
+// double-buffered in LDS: a step stages tile t+1 from registers, starts the
+// loads of tile t+2 and computes tile t; waves 0-3 stage V (transposed),
+// waves 4-7 stage K.
 //
 // Per wave and 64-key tile the contraction is laid out transposed,
 //   S^T[key][query] = K Q^T     (A = K rows from LDS, B = Q^T held in registers)
@@ -336,7 +336,10 @@ __device__ __forceinline__ void store_o(const WaveAcc& acc, float* __restrict__ 
 }
 
 // Shared pipeline over T tiles; k0_of(idx) is the first key of tile idx.
-// Tile t+1 is in flight (registers) while tile t is computed from LDS.
+// Step t first stages tile t+1 (registers loaded during step t-1) into the
+// other LDS buffer, which tile t-1 left before the last barrier, and starts
+// the global loads of tile t+2 into the same registers; then it computes
+// tile t.  The LDS writes drain under the compute; one barrier per step.
 template <class K0Of>
 __device__ __forceinline__ void run_tiles(const AttnParams& p, uint16_t* smem, int T, int g, int h, int slot,
                                           bool active, int q0, const MaskSpec& ms, K0Of&& k0_of) {
@@ -350,18 +353,17 @@ __device__ __forceinline__ void run_tiles(const AttnParams& p, uint16_t* smem, i
   TileRegs r;
   const bool v_wave = __builtin_amdgcn_readfirstlane(tid >> 6) < 4;
   const TileSrc src = tile_src(p.K, p.V, g, rs, tid, v_wave);
-  int k0 = k0_of(0);
-  tile_load(r, src, k0, p.N, rs);
+  tile_load(r, src, k0_of(0), p.N, rs);
   tile_store(r, smem, tid, v_wave);
+  if (T > 1) tile_load(r, src, k0_of(1), p.N, rs);
   __syncthreads();
   for (int t = 0; t < T; ++t) {
-    const int cur = k0;
     if (t + 1 < T) {
-      k0 = k0_of(t + 1);
-      tile_load(r, src, k0, p.N, rs);
+      tile_store(r, smem + ((t + 1) & 1) * BUF_ELEMS, tid, v_wave);
+      if (t + 2 < T) tile_load(r, src, k0_of(t + 2), p.N, rs);
     }
+    const int cur = k0_of(t);
     if (active && !tile_empty(ms, q0, cur)) tile_compute(smem + (t & 1) * BUF_ELEMS, qf, acc, lane, q0, cur, ms, p.c);
-    if (t + 1 < T) tile_store(r, smem + ((t + 1) & 1) * BUF_ELEMS, tid, v_wave);
     __syncthreads();
   }
   if (active) store_o(acc, p.O, p.lse, slot, p.N, p.Hq, h, q0, lane, p.c);
