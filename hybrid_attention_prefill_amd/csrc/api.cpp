@@ -274,9 +274,8 @@ int run_kmeans(const ha_layer_desc* d, const float* klow, float* cent, int32_t* 
   kp.count = kp.hist + Hkv * n_chunks * M;
   kp.c_norm = reinterpret_cast<float*>(kp.count + Hkv * M);
   // 16-byte vector loads read the split centroids: start them on an aligned address
-  kp.c_hi = reinterpret_cast<__bf16*>(align_up(reinterpret_cast<uintptr_t>(kp.c_norm + Hkv * M)));
-  kp.c_mid = kp.c_hi + Hkv * M * kRank;
-  kp.c_lo = kp.c_mid + Hkv * M * kRank;
+  kp.c_hi = reinterpret_cast<_Float16*>(align_up(reinterpret_cast<uintptr_t>(kp.c_norm + Hkv * M)));
+  kp.c_lo = kp.c_hi + Hkv * M * kRank;
   return dev_status(launch_kmeans(kp, d->n_kv_heads, d->kmeans_iters, s));
 }
 

@@ -90,9 +90,8 @@ struct KmeansParams {
   int32_t* csr_mem;    // [Hkv, N]
   int32_t* hist;       // scratch [Hkv, n_chunks, M]
   int32_t* count;      // scratch [Hkv, M]
-  __bf16* c_hi;        // scratch [Hkv, M, r]: centroids split in three bf16 parts
-  __bf16* c_mid;
-  __bf16* c_lo;
+  _Float16* c_hi;      // scratch [Hkv, M, r]: centroids split in two fp16 parts
+  _Float16* c_lo;
   float* c_norm;       // scratch [Hkv, M]
   int N, M, stride, n_chunks;
 };

@@ -36,7 +36,7 @@ __global__ __launch_bounds__(NT) void km_init_kernel(KmeansParams p) {
   p.cent[((size_t)g * p.M + m) * R + r] = p.klow[((size_t)g * p.N + (size_t)m * p.stride) * R + r];
 }
 
-// Per iteration: centroids split into three bf16 parts and their squared
+// Per iteration: centroids split into two fp16 parts and their squared
 // norms, for the MFMA distance pass.
 __global__ __launch_bounds__(NT) void km_prep_kernel(KmeansParams p) {
   const int g = blockIdx.y;
@@ -49,47 +49,49 @@ __global__ __launch_bounds__(NT) void km_prep_kernel(KmeansParams p) {
   for (int r = 0; r < R; ++r) {
     const float v = c[r];
     nrm = fmaf(v, v, nrm);
-    dev::split3(v, p.c_hi[o + r], p.c_mid[o + r], p.c_lo[o + r]);
+    dev::split2_f16(v, p.c_hi[o + r], p.c_lo[o + r]);
   }
   p.c_norm[(size_t)g * p.M + m] = nrm;
 }
 
 // Assignment: each wave owns 32*KT keys (KT column blocks of 32), the
-// workgroup 4 waves.  Centroids are staged in LDS 256 at a time as four
-// bf16 rows each: the three parts of C_m and (hi, mid, lo) of |C_m|^2.  For
-// every tile of 32 centroids and key block, one chain of seven MFMAs gives
+// workgroup 4 waves.  Centroids are staged in LDS 256 at a time as three
+// 16-bit rows each: the two fp16 parts of C_m and the bf16 (hi, mid, lo) of
+// |C_m|^2.  For every tile of 32 centroids and key block, one chain of four
+// MFMAs gives
 //   d^T[m][j] = |C_m|^2 - 2 C_m . k_j
-// directly: six passes over the split operands with the keys pre-scaled by
-// -2 (exact), and a seventh that adds the norm parts against a (1, 1, 1)
-// operand.  The |k_j|^2 term does not change the argmin.  A lane holds one
-// key and 16 of the tile's centroids in increasing order; the tile minimum
-// is a min3 chain; only when some lane of a key block improves on its best
-// does the wave look up the index (the lowest element equal to the tile
-// minimum; tiles are scanned in increasing order and replace the best only
-// when strictly smaller, so the lowest index wins on equal distances).  The
-// two lane halves are merged with the same rule at the end.
+// directly: three fp16 passes over the split operands (keys pre-scaled by -2,
+// exact; ~2^-21 relative to |C||k|), and a bf16 pass that adds the norm parts
+// against a (1, 1, 1) operand (bf16 keeps fp32's exponent range for large
+// norms).  The |k_j|^2 term does not change the argmin.  A lane holds one key
+// and 16 of the tile's centroids in increasing order; the tile minimum is a
+// min3 chain; only when some lane of a key block improves on its best does
+// the wave look up the index (the lowest element equal to the tile minimum;
+// tiles are scanned in increasing order and replace the best only when
+// strictly smaller, so the lowest index wins on equal distances).  The two
+// lane halves are merged with the same rule at the end.  Keys and centroids
+// must stay well inside the fp16 range (|component| < 16384).
 constexpr int kCChunk = 256;      // centroids per LDS chunk
-constexpr int kCStr = 24;         // bf16 row stride of a staged part (48 B: conflict-free 16-B reads)
+constexpr int kCStr = 24;         // 16-bit row stride of a staged part (48 B: conflict-free 16-B reads)
 constexpr int KT = 4;             // 32-key blocks per wave
 constexpr float kPadNorm = 1e30f; // norm of the padding rows of a partial tile
 
 __global__ __launch_bounds__(NT) void km_assign_kernel(KmeansParams p) {
-  __shared__ __attribute__((aligned(16))) __bf16 cs[4][kCChunk * kCStr];
+  __shared__ __attribute__((aligned(16))) uint16_t cs[3][kCChunk * kCStr];
   const int g = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, lr = lane & 31, lh = lane >> 5;
   const int j0 = (blockIdx.x * 4 + wave) * (32 * KT);
-  dev::bf16x8 kh[KT], km[KT], kl[KT];
+  dev::f16x8 kh[KT], kl[KT];
 #pragma unroll
   for (int kt = 0; kt < KT; ++kt) {
     const int j = min(p.N - 1, j0 + kt * 32 + lr);
     const float* kp = p.klow + ((size_t)g * p.N + j) * R + lh * 8;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      __bf16 h, m, l;
-      dev::split3(-2.f * kp[e], h, m, l);
+      _Float16 h, l;
+      dev::split2_f16(-2.f * kp[e], h, l);
       kh[kt][e] = h;
-      km[kt][e] = m;
       kl[kt][e] = l;
     }
   }
@@ -103,18 +105,17 @@ __global__ __launch_bounds__(NT) void km_assign_kernel(KmeansParams p) {
     best[kt] = __builtin_inff();
     arg[kt] = 0;
   }
-  const __bf16* parts[3] = {p.c_hi + (size_t)g * p.M * R, p.c_mid + (size_t)g * p.M * R,
-                            p.c_lo + (size_t)g * p.M * R};
+  const _Float16* parts[2] = {p.c_hi + (size_t)g * p.M * R, p.c_lo + (size_t)g * p.M * R};
   const float* cn = p.c_norm + (size_t)g * p.M;
   for (int c0 = 0; c0 < p.M; c0 += kCChunk) {
     const int nc = min(kCChunk, p.M - c0);
     __syncthreads();
     {
-      // thread t stages centroid c0 + t: three 32-B parts and the norm row
+      // thread t stages centroid c0 + t: two 32-B parts and the norm row
       const int m = c0 + tid;
       const bool ok = tid < nc;
 #pragma unroll
-      for (int q = 0; q < 3; ++q) {
+      for (int q = 0; q < 2; ++q) {
         const uint4* src = reinterpret_cast<const uint4*>(parts[q] + (size_t)(ok ? m : c0) * R);
         const uint4 v0 = src[0], v1 = src[1];
         uint4* dst = reinterpret_cast<uint4*>(&cs[q][tid * kCStr]);
@@ -132,35 +133,28 @@ __global__ __launch_bounds__(NT) void km_assign_kernel(KmeansParams p) {
       nr0[0] = h;
       nr0[1] = md;
       nr0[2] = l;
-      *reinterpret_cast<dev::bf16x8*>(&cs[3][tid * kCStr]) = nr0;
-      *reinterpret_cast<dev::bf16x8*>(&cs[3][tid * kCStr + 8]) = nr1;
+      *reinterpret_cast<dev::bf16x8*>(&cs[2][tid * kCStr]) = nr0;
+      *reinterpret_cast<dev::bf16x8*>(&cs[2][tid * kCStr + 8]) = nr1;
     }
     __syncthreads();
     const int n_tiles = (nc + 31) / 32;
     for (int x = 0; x < n_tiles; ++x) {
       const int r0 = x * 32;
-      const dev::bf16x8 ah = *reinterpret_cast<const dev::bf16x8*>(&cs[0][(r0 + lr) * kCStr + lh * 8]);
-      const dev::bf16x8 am = *reinterpret_cast<const dev::bf16x8*>(&cs[1][(r0 + lr) * kCStr + lh * 8]);
-      const dev::bf16x8 al = *reinterpret_cast<const dev::bf16x8*>(&cs[2][(r0 + lr) * kCStr + lh * 8]);
-      const dev::bf16x8 an = *reinterpret_cast<const dev::bf16x8*>(&cs[3][(r0 + lr) * kCStr + lh * 8]);
+      const dev::f16x8 ah = *reinterpret_cast<const dev::f16x8*>(&cs[0][(r0 + lr) * kCStr + lh * 8]);
+      const dev::f16x8 al = *reinterpret_cast<const dev::f16x8*>(&cs[1][(r0 + lr) * kCStr + lh * 8]);
+      const dev::bf16x8 an = *reinterpret_cast<const dev::bf16x8*>(&cs[2][(r0 + lr) * kCStr + lh * 8]);
       const int m0 = c0 + r0;
       // KT independent MFMA chains, interleaved pass by pass
       dev::f32x16 acc[KT];
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
         acc[kt] = {};
-        acc[kt] = dev::mfma32(al, kh[kt], acc[kt]);
+        acc[kt] = dev::mfma32_f16(al, kh[kt], acc[kt]);
       }
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt) acc[kt] = dev::mfma32(ah, kl[kt], acc[kt]);
+      for (int kt = 0; kt < KT; ++kt) acc[kt] = dev::mfma32_f16(ah, kl[kt], acc[kt]);
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt) acc[kt] = dev::mfma32(am, km[kt], acc[kt]);
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) acc[kt] = dev::mfma32(am, kh[kt], acc[kt]);
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) acc[kt] = dev::mfma32(ah, km[kt], acc[kt]);
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) acc[kt] = dev::mfma32(ah, kh[kt], acc[kt]);
+      for (int kt = 0; kt < KT; ++kt) acc[kt] = dev::mfma32_f16(ah, kh[kt], acc[kt]);
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) acc[kt] = dev::mfma32(an, ones, acc[kt]);
 #pragma unroll
@@ -514,7 +508,7 @@ __global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
 size_t kmeans_scratch_bytes(int N, int M, int Hkv) {
   const size_t n_chunks = (size_t)(N + kChunk - 1) / kChunk;
   return (size_t)Hkv * n_chunks * M * sizeof(int32_t) + (size_t)Hkv * M * sizeof(int32_t) +
-         (size_t)Hkv * M * (3 * R * sizeof(__bf16) + sizeof(float)) + 256;
+         (size_t)Hkv * M * (2 * R * sizeof(_Float16) + sizeof(float)) + 256;
 }
 
 hipError_t launch_kmeans(KmeansParams p, int Hkv, int iters, hipStream_t s) {
