@@ -7,6 +7,11 @@ follow [TriangleMix] and [Orthros].
 Retrieval head h, query block b (rows R_b):
   K(i) = SWA(w)(i)  U  {j <= i : block(j) in S_b}  U  (f0 ? {j <= i : j < Bk} : {})
   (cluster mode: {j <= i : a_j in S_b} in place of the block term)
+With group-shared selection ([TriangleMix] interview, GQA answer: the queries
+of one GQA group share the same keys, and sharing work across the group is
+the usual practice), S_b is chosen once per (KV head, query block) from the
+group score max over the group's retrieval heads of the head scores, and
+every retrieval head of the group uses it.
 [RTPurbo]: exact softmax over the selected candidates in full dimension, with
 the local window of the head's own neighbourhood.
 
@@ -139,6 +144,24 @@ def layer_prefill(w, q_rows: Callable[[int, int], np.ndarray], K: np.ndarray, V:
             res.centroids[g], res.assign[g] = C, a
 
     eligible_memo = {}   # (KV head, block) -> eligible clusters (shared by the group's heads)
+    group_memo = {}      # (KV head, block) -> (eligible, group scores, selection)
+    ret_of_group = {}
+    for hh in range(Hq):   # all of a group's retrieval heads, even outside `heads`
+        if w.head_kind[hh] == RETRIEVAL:
+            ret_of_group.setdefault(head_group(hh, Hq, Hkv), []).append(hh)
+
+    def scores_for(hh, g, b, Qb, rows, qe):
+        """(eligible ids, scores) of retrieval head hh for query block b."""
+        ql = project(Qb[:, hh], P[g])
+        if w.n_clusters > 0:
+            C, a = res.centroids[g], res.assign[g]
+            if (g, b) not in eligible_memo:
+                eligible_memo[(g, b)] = eligible_clusters(a, C.shape[0], qe, w.window)
+            E = eligible_memo[(g, b)]
+            return ql, E, cluster_scores(ql, C, E)
+        E = eligible_blocks(qe, w.window, w.force_block0, Bk)
+        return ql, E, (block_scores(ql, rows, res.klow[g], E, Bk) if E.size else np.zeros(0))
+
     off = 0
     for b in blocks:
         r0, r1 = b * Bq, min(N, (b + 1) * Bq)
@@ -165,25 +188,22 @@ def layer_prefill(w, q_rows: Callable[[int, int], np.ndarray], K: np.ndarray, V:
                 o = attend_rows(q, rows, K[:, g], V[:, g], keys,
                                 lambda ri, kj: visible_triangle(ri, kj, N, w.sink, w.window, w.last_q), sc)
             elif kind == RETRIEVAL:
-                ql = project(q, P[g])
+                ql, E, s = scores_for(h, g, b, Qb, rows, qe)
                 res.qlow.setdefault(h, {})[b] = ql
-                if w.n_clusters > 0:
-                    C, a = res.centroids[g], res.assign[g]
-                    if (g, b) not in eligible_memo:
-                        eligible_memo[(g, b)] = eligible_clusters(a, C.shape[0], qe, w.window)
-                    E = eligible_memo[(g, b)]
-                    s = cluster_scores(ql, C, E)
-                    S = topk_order(s, E, w.topk)
-                    if sel_override is not None:
-                        S = np.asarray(sel_override[h][b], dtype=np.int64)
-                    keys, vis = retrieval_key_set(rows, w.window, Bk, 0, clusters=S, assign=a,
-                                                  n_clusters=C.shape[0])
+                if w.group_select:
+                    if (g, b) not in group_memo:
+                        sg = np.max(np.stack([scores_for(hh, g, b, Qb, rows, qe)[2]
+                                              for hh in ret_of_group[g]]), axis=0) if E.size else s
+                        group_memo[(g, b)] = (sg, topk_order(sg, E, w.topk))
+                    s, S = group_memo[(g, b)]
                 else:
-                    E = eligible_blocks(qe, w.window, w.force_block0, Bk)
-                    s = block_scores(ql, rows, res.klow[g], E, Bk) if E.size else np.zeros(0)
                     S = topk_order(s, E, w.topk)
-                    if sel_override is not None:
-                        S = np.asarray(sel_override[h][b], dtype=np.int64)
+                if sel_override is not None:
+                    S = np.asarray(sel_override[h][b], dtype=np.int64)
+                if w.n_clusters > 0:
+                    keys, vis = retrieval_key_set(rows, w.window, Bk, 0, clusters=S, assign=res.assign[g],
+                                                  n_clusters=res.centroids[g].shape[0])
+                else:
                     keys, vis = retrieval_key_set(rows, w.window, Bk, w.force_block0, blocks=S)
                 res.sel.setdefault(h, {})[b] = S
                 res.scored.setdefault(h, {})[b] = (E, s)

@@ -42,6 +42,9 @@ class Workload:
     sink: int = 0
     last_q: int = 0
     n_out: int = 0
+    # 1: one selection per (KV head, query block), scored by the max over the
+    # group's retrieval heads and shared by them (GQA-group-shared selection)
+    group_select: int = 0
     # input recipe: "plain", "planted_lowfreq" (keys carry per-segment topic
     # vectors on the low-frequency dims), "needles" (planted key/query pairs)
     recipe: str = "plain"
@@ -69,6 +72,7 @@ class Workload:
             force_block0=self.force_block0, n_clusters=self.n_clusters,
             kmeans_iters=self.kmeans_iters, kmeans_stride=self.kmeans_stride,
             sink=self.sink, last_q=self.last_q, n_out=self.n_out,
+            group_select=self.group_select,
         )
 
 
@@ -113,12 +117,16 @@ ALLSPARSE_1M = Workload(
     n_clusters=16384, kmeans_iters=10, kmeans_stride=64,
     recipe="needles", n_needles=64)
 
+# The same layer with GQA-group-shared selection: each KV head's 8 retrieval
+# heads share one top-64 cluster selection per query block.
+ALLSPARSE_1M_GQA = ALLSPARSE_1M.with_(name="allsparse_1m_gqa", group_select=1)
+
 # The TriangleMix layer split: 12 dense shallow layers, 20 triangle layers.
 TRIANGLE_LAYER_SPLIT = (12, 20)
 
 WORKLOADS = {w.name: w for w in (
     TINY_HYBRID_2K, QWEN3_30B_32K, TRIANGLE_8B_128K, DENSE_8B_128K,
-    ORTHROS_8B_128K, ALLSPARSE_1M)}
+    ORTHROS_8B_128K, ALLSPARSE_1M, ALLSPARSE_1M_GQA)}
 
 
 def shrink(w: Workload, n_tokens: int, *, n_clusters: Optional[int] = None,
