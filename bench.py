@@ -169,7 +169,8 @@ class Layer:
         dev = self.Q.device
         self.desc = ha.make_desc(N, Hq, Hkv, D, window=w.window, topk=w.topk, force_block0=w.force_block0,
                                  n_clusters=w.n_clusters, kmeans_iters=w.kmeans_iters,
-                                 kmeans_stride=w.kmeans_stride, sink=w.sink, last_q=w.last_q, n_out=w.n_out)
+                                 kmeans_stride=w.kmeans_stride, sink=w.sink, last_q=w.last_q, n_out=w.n_out,
+                                 group_select=w.group_select)
         self.kinds = list(w.head_kind)
         self.O = torch.empty((N, Hq, D), dtype=torch.float32, device=dev)
         self.O_out = torch.empty((w.n_out, Hq, D), dtype=torch.float32, device=dev) if w.n_out else None

@@ -37,6 +37,7 @@ class LayerDesc(ctypes.Structure):
         ("n_clusters", ctypes.c_int32), ("kmeans_iters", ctypes.c_int32),
         ("kmeans_stride", ctypes.c_int32), ("sink", ctypes.c_int32),
         ("last_q", ctypes.c_int32), ("n_out", ctypes.c_int32),
+        ("group_select", ctypes.c_int32),
     ]
 
 
@@ -126,10 +127,10 @@ def _stream(stream) -> Optional[int]:
 
 def make_desc(n_tokens, n_q_heads, n_kv_heads, head_dim=128, *, softmax_scale=0.0, window=0, rank=16,
               q_block=64, k_block=64, topk=0, force_block0=0, n_clusters=0, kmeans_iters=0,
-              kmeans_stride=0, sink=0, last_q=0, n_out=0) -> LayerDesc:
+              kmeans_stride=0, sink=0, last_q=0, n_out=0, group_select=0) -> LayerDesc:
     return LayerDesc(n_tokens, n_q_heads, n_kv_heads, head_dim, float(softmax_scale or 0.0), window, rank,
                      q_block, k_block, topk, int(force_block0), n_clusters, kmeans_iters, kmeans_stride,
-                     sink, last_q, n_out)
+                     sink, last_q, n_out, int(group_select))
 
 
 def _kinds(head_kind: Sequence[int]):
@@ -209,8 +210,8 @@ def ha_attn_cross(desc, Q, K, V, xa_scale, xa_offset, O_out, workspace=None, ws_
 
 def hybrid_attn_prefill(Q, K, V, head_kind, window, P_idx=None, topk=0, block=64, *, force_block0=False,
                         n_clusters=0, kmeans_iters=10, kmeans_stride=64, sink=0, last_q=0, n_out=0,
-                        xa_scale=None, xa_offset=None, softmax_scale=None, out=None, out_cross=None,
-                        workspace=None, return_aux=False):
+                        group_select=False, xa_scale=None, xa_offset=None, softmax_scale=None, out=None,
+                        out_cross=None, workspace=None, return_aux=False):
     """One layer's hybrid attention prefill on the current HIP stream.
 
     Q [N, Hq, D], K/V [N, Hkv, D] bf16 CUDA tensors; head_kind a sequence of
@@ -225,7 +226,8 @@ def hybrid_attn_prefill(Q, K, V, head_kind, window, P_idx=None, topk=0, block=64
     desc = make_desc(N, Hq, Hkv, D, softmax_scale=softmax_scale or 0.0, window=window, topk=topk,
                      q_block=block, k_block=block, force_block0=int(bool(force_block0)),
                      n_clusters=n_clusters, kmeans_iters=kmeans_iters if n_clusters else 0,
-                     kmeans_stride=kmeans_stride if n_clusters else 0, sink=sink, last_q=last_q, n_out=n_out)
+                     kmeans_stride=kmeans_stride if n_clusters else 0, sink=sink, last_q=last_q, n_out=n_out,
+                     group_select=int(bool(group_select)))
     dev = Q.device
     O = out if out is not None else torch.empty((N, Hq, D), dtype=torch.float32, device=dev)
     O_out = None

@@ -34,6 +34,7 @@ int check_desc(const ha_layer_desc* d, const int32_t* kinds, Heads* out) {
   if (d->n_out < 0 || d->n_out > d->n_tokens) return HA_ERR_ARG;
   if (d->n_out > 0 && d->n_q_heads / d->n_kv_heads > 16) return HA_ERR_UNSUPPORTED;
   if (!kinds) return HA_ERR_ARG;
+  if (d->group_select != 0 && d->group_select != 1) return HA_ERR_ARG;
   Heads h;
   h.ret_slot.assign(d->n_q_heads, -1);
   bool need_window = false, any_tri = false;
@@ -123,15 +124,18 @@ void build_packs(const ha_layer_desc* d, const int32_t* kinds, int kind, const s
   pt->n = 0;
   for (int g = 0; g < d->n_kv_heads; ++g) {
     uint32_t w = 0, s = 0;
-    int cnt = 0;
+    int cnt = 0, row = -1;
     for (int hh = 0; hh < G; ++hh) {
       const int h = g * G + hh;
       if (kinds[h] != kind) continue;
+      const int sl = slot.empty() ? 0 : std::max(0, slot[h]);
+      if (row < 0) row = sl;
       w |= (uint32_t)h << (8 * cnt);
-      s |= (uint32_t)(slot.empty() ? 0 : std::max(0, slot[h])) << (8 * cnt);
+      s |= (uint32_t)sl << (8 * cnt);
       if (++cnt == 4) {
         pt->heads[pt->n] = w;
         pt->slots[pt->n] = s;
+        pt->sel_row[pt->n] = row;
         ++pt->n;
         w = s = 0;
         cnt = 0;
@@ -141,6 +145,7 @@ void build_packs(const ha_layer_desc* d, const int32_t* kinds, int kind, const s
       for (int x = cnt; x < 4; ++x) w |= 0xFFu << (8 * x);
       pt->heads[pt->n] = w;
       pt->slots[pt->n] = s;
+      pt->sel_row[pt->n] = row;
       ++pt->n;
     }
   }
@@ -214,6 +219,21 @@ int run_project(const ha_layer_desc* d, const Heads& h, const void* Q, const voi
   return HA_OK;
 }
 
+// Selection units: one per retrieval slot, or one per KV group in
+// group-shared mode (slots are numbered in head order, so a group's slots
+// are consecutive).
+void fill_units(const ha_layer_desc* d, const Heads& h, SelectParams* sp) {
+  const int G = d->n_q_heads / d->n_kv_heads;
+  sp->n_units = 0;
+  for (int t = 0; t < (int)h.ret.size(); ++t) {
+    if (d->group_select && t > 0 && h.ret[t] / G == h.ret[t - 1] / G) {
+      sp->unit[sp->n_units - 1] += 1u << 16;
+    } else {
+      sp->unit[sp->n_units++] = (uint32_t)t | (1u << 16);
+    }
+  }
+}
+
 int run_select_blocks(const ha_layer_desc* d, const Heads& h, const float* qlow, const float* klow,
                       int32_t* sel, hipStream_t s) {
   const int G = d->n_q_heads / d->n_kv_heads;
@@ -228,6 +248,7 @@ int run_select_blocks(const ha_layer_desc* d, const Heads& h, const float* qlow,
   sp.force_block0 = d->force_block0;
   sp.n_ret = (int)h.ret.size();
   for (int t = 0; t < sp.n_ret; ++t) sp.group_of_ret[t] = h.ret[t] / G;
+  fill_units(d, h, &sp);
   return dev_status(launch_select_blocks(sp, s));
 }
 
@@ -251,6 +272,7 @@ int run_gather(const ha_layer_desc* d, const int32_t* kinds, const Heads& h, con
     p.csr_mem = csr_mem;
     p.M = d->n_clusters;
   }
+  if (d->group_select) return dev_status(launch_attn_selected_group(p, pt, s));
   SelList sl;
   sl.n_ret = (int)h.ret.size();
   for (int t = 0; t < sl.n_ret; ++t) sl.head[t] = h.ret[t];
@@ -296,6 +318,7 @@ int run_select_clusters(const ha_layer_desc* d, const Heads& h, const float* qlo
   sp.M = d->n_clusters;
   sp.n_ret = (int)h.ret.size();
   for (int t = 0; t < sp.n_ret; ++t) sp.group_of_ret[t] = h.ret[t] / G;
+  fill_units(d, h, &sp);
   const size_t nparts = (size_t)d->n_kv_heads * d->n_clusters * kRank;
   sp.c_hi = static_cast<__bf16*>(scratch);
   sp.c_lo = sp.c_hi + nparts;

@@ -24,6 +24,7 @@ struct PackTable {
   int32_t n;
   uint32_t heads[kMaxHeads];  // 4 head ids per pack, byte w = wave w's head
   uint32_t slots[kMaxHeads];  // retrieval slot (row of sel) of each head, same packing
+  int32_t sel_row[kMaxHeads]; // group-shared selection: slot of the KV group's first retrieval head
 };
 
 struct AttnParams {
@@ -54,6 +55,10 @@ struct SelList {
 // Host launchers (each returns a hipError_t from the launch).
 hipError_t launch_attn_band(const AttnParams& p, const PackTable& packs, hipStream_t s);
 hipError_t launch_attn_selected(const AttnParams& p, const SelList& sl, hipStream_t s);
+// Group-shared selection: every retrieval head of a KV group reads the same
+// selection row, so one workgroup serves a pack of up to 4 of them (the pack's
+// first slot names the row).
+hipError_t launch_attn_selected_group(const AttnParams& p, const PackTable& packs, hipStream_t s);
 
 struct ProjParams {
   const uint16_t* X;   // bf16 [N, H, D]
@@ -79,6 +84,12 @@ struct SelectParams {
   int N, n_qb, window, topk, force_block0, M;
   int n_ret;
   int32_t group_of_ret[kMaxHeads];
+  // A selection unit is a run of retrieval slots that share one top-k: one
+  // slot per unit, or all slots of a KV group (group-shared selection).
+  // unit[u] = first slot | slot count << 16.  Scores of a unit are the max
+  // over its slots; its top-k row is written to every slot.
+  int n_units;
+  uint32_t unit[kMaxHeads];
 };
 hipError_t launch_select_blocks(const SelectParams& p, hipStream_t s);
 

@@ -75,17 +75,19 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
   return v;
 }
 
-// Exclusive prefix sum over the 256 threads in thread order; *total = sum.
-__device__ __forceinline__ int block_excl_scan(int v, int* tmp4, int* total) {
+// Exclusive prefix sum over the workgroup's threads in thread order;
+// *total = sum.  NW = waves in the workgroup; tmp holds NW ints.
+template <int NW = 4>
+__device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int inc = wave_incl_scan(v, lane);
-  if (lane == 63) tmp4[wave] = inc;
+  if (lane == 63) tmp[wave] = inc;
   __syncthreads();
   int base = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    if (w < wave) base += tmp4[w];
-    tot += tmp4[w];
+  for (int w = 0; w < NW; ++w) {
+    if (w < wave) base += tmp[w];
+    tot += tmp[w];
   }
   __syncthreads();
   *total = tot;

@@ -339,12 +339,308 @@ __global__ __launch_bounds__(NT, 2) void attn_selected_kernel(AttnParams p, SelL
     }
 }
 
+// ---------------------------------------------------------------------------
+// Group-shared selection (36kr interview, GQA answer: the query heads of one
+// GQA group share their keys, so one selection serves the group).  Every
+// retrieval head of a KV group attends to the same gathered keys, so a
+// workgroup of 8 waves serves a pack of up to 4 of them and each gathered
+// 64-key tile is read from HBM once for 4 heads x 64 rows.  Wave w takes
+// head slot w % 4 and query rows 32 (w / 4) .. +31 and computes the whole
+// tile (two 32-key halves); waves 0-3 stage V (transposed), waves 4-7 K.
+// Step t stages tile t+1 from registers, starts the loads of tile t+2 (whose
+// key rows were looked up a step earlier), looks up tile t+3 and computes
+// tile t; one barrier per step.
+namespace grp {
+
+constexpr int NT8 = 512;
+constexpr int QW = 32;     // query rows per wave
+constexpr int kRing = 4;   // looked-up key rows: tiles t .. t+3
+
+struct Regs {
+  u32x4 x[4];
+};
+
+// Thread's share: V threads (waves 0-3) read key slots 4 (tid % 16) + x at
+// d = 8 (tid / 16) .. +8; K threads read 16-byte chunk (u % 16) of key slot
+// 16 x + u / 16 (u = tid - 256).  Empty slots (key -1) read key row 0.
+__device__ __forceinline__ void load(Regs& r, const char* __restrict__ base, const int* ring, int rs2, int tid,
+                                     bool v_wave) {
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int s = v_wave ? (tid & 15) * 4 + x : x * 16 + ((tid - 256) >> 4);
+    const int db = v_wave ? (tid >> 4) * 16 : ((tid - 256) & 15) * 16;
+    const int key = max(0, ring[s]);
+    r.x[x] = *reinterpret_cast<const u32x4*>(base + (size_t)key * rs2 + db);
+  }
+}
+
+__device__ __forceinline__ void store(const Regs& r, uint16_t* buf, int tid, bool v_wave) {
+  if (v_wave) {
+    uint16_t* Vt = buf + K_ELEMS;
+    const int kg = tid & 15, dc = tid >> 4;
+    const int pos = 16 * (kg >> 2) + vt_pos((kg * 4) & 15);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t a0 = r.x[0][w], a1 = r.x[1][w], a2 = r.x[2][w], a3 = r.x[3][w];
+      u32x2 ev, od;
+      ev[0] = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
+      ev[1] = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
+      od[0] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
+      od[1] = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
+      *reinterpret_cast<u32x2*>(Vt + (dc * 8 + 2 * w) * VSTR + pos) = ev;
+      *reinterpret_cast<u32x2*>(Vt + (dc * 8 + 2 * w + 1) * VSTR + pos) = od;
+    }
+  } else {
+    uint16_t* Ks = buf;
+    const int u = tid - 256;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int id = x * 256 + u;
+      *reinterpret_cast<u32x4*>(Ks + (id >> 4) * KSTR + (id & 15) * 8) = r.x[x];
+    }
+  }
+}
+
+// The whole tile (both key halves) against the wave's 32 rows.
+__device__ __forceinline__ void compute(const uint16_t* __restrict__ buf, const int* __restrict__ kpos,
+                                        const bf16x8 (&qf)[8], Acc& acc, int lane, int i, int w, float c) {
+  const uint16_t* Ks = buf;
+  const uint16_t* Vt = buf + K_ELEMS;
+  const int lr = lane & 31, lh = lane >> 5;
+  f32x16 s[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + (kb * 32 + lr) * KSTR + t * 16 + lh * 8);
+      s[kb] = mfma(kf, qf[t], s[kb]);
+    }
+  float mx = kNegInf;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int4 jv = *reinterpret_cast<const int4*>(kpos + kb * 32 + lh * 4 + q * 8);
+      const int js[4] = {jv.x, jv.y, jv.z, jv.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool vis = (js[e] >= 0) & (i - js[e] >= w);
+        s[kb][q * 4 + e] = vis ? s[kb][q * 4 + e] : kNegInf;
+        mx = fmaxf(mx, s[kb][q * 4 + e]);
+      }
+    }
+  mx = dev::pair32_max(mx);
+  if (__any((mx - acc.m) * c > kSlack)) {
+    const float mnew = fmaxf(acc.m, mx);
+    const float alpha = __builtin_amdgcn_exp2f((acc.m - mnew) * c);
+    acc.m = mnew;
+    acc.l *= alpha;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) acc.o[db] *= alpha;
+  }
+  const float nb = -acc.m * c;
+  float sum = 0.f;
+  bf16x8 pf[2][2];
+  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[kb][h2][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][h2 * 8 + e], c, nb));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bf16x2 pr = {pf[kb][h2][2 * q], pf[kb][h2][2 * q + 1]};
+        sum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, sum, false);
+      }
+    }
+  acc.l += sum;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int t4 = kb * 2 + h2;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(Vt + (db * 32 + lr) * VSTR + t4 * 16 + lh * 8);
+        acc.o[db] = mfma(vf, pf[kb][h2], acc.o[db]);
+      }
+    }
+}
+
+}  // namespace grp
+
+__global__ __launch_bounds__(grp::NT8, 1) void attn_selected_group_kernel(AttnParams p, PackTable packs) {
+  using namespace grp;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * BUF_ELEMS];
+  __shared__ __attribute__((aligned(16))) int ring[kRing][BK];
+  __shared__ int ent[kMaxTopk + 1];     // block id (block mode) or CSR start (cluster mode)
+  __shared__ int pre[kMaxTopk + 2];     // prefix of visible key counts per entry
+  __shared__ int tmp8[8];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int pk = lid / p.n_qt;
+  const int b = p.n_qt - 1 - lid % p.n_qt;    // long key lists first
+  const uint32_t pw = packs.heads[pk];
+  const int hs = wave & 3;
+  const int h = (pw >> (8 * hs)) & 0xFF;
+  const int g = (int)(pw & 0xFF) / p.G;
+  const int slot = (packs.slots[pk] >> (8 * hs)) & 0xFF;
+  const int srow = packs.sel_row[pk];
+  const int q0 = b * BK;
+  const int lim = min(p.N, q0 + BK) - 1 - p.window;   // keys j <= lim can be visible
+  const int n_kb = (p.N + BK - 1) / BK;
+  const int32_t* mem = p.csr_mem ? p.csr_mem + (size_t)g * p.N : nullptr;
+
+  // entries: forced block 0 + the selection; count of keys j <= lim in each
+  const int ne = p.topk + (p.force_block0 ? 1 : 0);
+  int cnt = 0, start = 0;
+  if (tid < ne && lim >= 0) {
+    if (p.force_block0 && tid == 0) {
+      start = 0;
+      cnt = min(BK, lim + 1);
+    } else {
+      const int e = tid - (p.force_block0 ? 1 : 0);
+      const int v = p.sel[((size_t)srow * p.n_qt + b) * p.topk + e];
+      if (p.M > 0) {
+        if (v >= 0 && v < p.M) {
+          const int32_t* off = p.csr_off + (size_t)g * (p.M + 1);
+          const int lo = off[v];
+          int a = lo, bb = off[v + 1];
+          while (a < bb) {
+            const int mid = (a + bb) >> 1;
+            if (mem[mid] <= lim) a = mid + 1;
+            else bb = mid;
+          }
+          start = lo;
+          cnt = a - lo;
+        }
+      } else if (v >= 0 && v < n_kb && !(p.force_block0 && v == 0)) {
+        start = v;
+        cnt = max(0, min(BK, lim - v * BK + 1));
+      }
+    }
+  }
+  int total;
+  const int excl = dev::block_excl_scan<8>(cnt, tmp8, &total);
+  if (tid < ne) {
+    ent[tid] = start;
+    pre[tid] = excl;
+  }
+  if (tid == 0) pre[ne] = total;
+  __syncthreads();
+  const int T = (total + BK - 1) / BK;
+  if (T == 0) return;
+
+  // key row of slot s of tile idx (flat index f = 64 idx + s); slot s of
+  // every tile is looked up by thread 8 s, whose entry index only moves
+  // forward from tile to tile
+  const bool owner = (tid & 7) == 0;
+  const int kslot = tid >> 3;
+  int cur_e = 0;
+  auto lookup = [&](int idx) -> int {
+    const int f = idx * BK + kslot;
+    if (f >= total) return -1;
+    while (cur_e + 1 < ne && pre[cur_e + 1] <= f) ++cur_e;
+    const int r = f - pre[cur_e];
+    if (p.M > 0) return (int)mem[ent[cur_e] + r];
+    return ent[cur_e] * BK + r;
+  };
+
+  const int lr = lane & 31, lh = lane >> 5;
+  const int qw = q0 + QW * (wave >> 2);
+  const int i = qw + lr;
+  const bool active = h != 0xFF && qw < p.N;
+  bf16x8 qf[8];
+  if (active) {
+#pragma unroll
+    for (int t8 = 0; t8 < 8; ++t8) {
+      if (i < p.N) {
+        qf[t8] = *reinterpret_cast<const bf16x8*>(p.Q + ((size_t)i * p.Hq + h) * D + t8 * 16 + lh * 8);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[t8][e] = (__bf16)0.f;
+      }
+    }
+  }
+  Acc acc;
+  acc.m = kMInit;
+  acc.l = 0.f;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc.o[db][e] = 0.f;
+
+  const bool v_wave = wave < 4;
+  const int rs2 = p.Hkv * D * 2;   // bytes between consecutive keys
+  const char* base = reinterpret_cast<const char*>((v_wave ? p.V : p.K) + g * D);
+  if (owner) {
+#pragma unroll
+    for (int x = 0; x < 3; ++x)
+      if (x < T) ring[x][kslot] = lookup(x);
+  }
+  __syncthreads();
+  Regs r;
+  load(r, base, ring[0], rs2, tid, v_wave);
+  store(r, smem, tid, v_wave);
+  if (T > 1) load(r, base, ring[1], rs2, tid, v_wave);
+  __syncthreads();
+  for (int t = 0; t < T; ++t) {
+    if (t + 1 < T) {
+      store(r, smem + ((t + 1) & 1) * BUF_ELEMS, tid, v_wave);
+      if (t + 2 < T) load(r, base, ring[(t + 2) % kRing], rs2, tid, v_wave);
+    }
+    const bool prep = owner && t + 3 < T;
+    int pending = -1;
+    if (prep) pending = lookup(t + 3);
+    if (active) compute(smem + (t & 1) * BUF_ELEMS, ring[t % kRing], qf, acc, lane, i, p.window, p.c);
+    if (prep) ring[(t + 3) % kRing][kslot] = pending;
+    __syncthreads();
+  }
+
+  // merge with the window result of the row
+  if (!active) return;
+  const float lt = dev::pair32_sum(acc.l);
+  if (i >= p.N || !(lt > 0.f)) return;
+  const float lse_s = acc.m * p.c + __log2f(lt);
+  const float lse_w = p.lse[(size_t)slot * p.N + i];
+  const float M = fmaxf(lse_s, lse_w);
+  const float ws = exp2f(lse_s - M), ww = exp2f(lse_w - M);
+  const float inv = 1.f / (ws + ww);
+  const float fs = ws * inv / lt, fw = ww * inv;
+  float* row = p.O + ((size_t)i * p.Hq + h) * D;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      float4* dst = reinterpret_cast<float4*>(row + db * 32 + lh * 4 + r4 * 8);
+      float4 v = *dst;
+      v.x = fmaf(v.x, fw, acc.o[db][r4 * 4 + 0] * fs);
+      v.y = fmaf(v.y, fw, acc.o[db][r4 * 4 + 1] * fs);
+      v.z = fmaf(v.z, fw, acc.o[db][r4 * 4 + 2] * fs);
+      v.w = fmaf(v.w, fw, acc.o[db][r4 * 4 + 3] * fs);
+      *dst = v;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_attn_selected(const AttnParams& p, const SelList& sl, hipStream_t s) {
   const int nwg = sl.n_ret * p.n_qt;
   if (nwg == 0 || (p.topk == 0 && !p.force_block0)) return hipSuccess;
   hipLaunchKernelGGL(attn_selected_kernel, dim3(nwg), dim3(NT), 0, s, p, sl);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_selected_group(const AttnParams& p, const PackTable& packs, hipStream_t s) {
+  const int nwg = packs.n * p.n_qt;
+  if (nwg == 0 || (p.topk == 0 && !p.force_block0)) return hipSuccess;
+  hipLaunchKernelGGL(attn_selected_group_kernel, dim3(nwg), dim3(grp::NT8), 0, s, p, packs);
   return hipGetLastError();
 }
 

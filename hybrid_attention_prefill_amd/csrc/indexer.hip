@@ -122,97 +122,119 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// A unit of several slots (group-shared selection) scores every block once
+// per slot and keeps the max (the order key is monotone, so the max of keys
+// is the key of the max); a wave owns the same blocks for every slot.
+//
 // keys: dynamic LDS of n_qb words (the eligible blocks of one query block)
 __global__ __launch_bounds__(NT) void select_blocks_kernel(SelectParams p) {
   extern __shared__ uint32_t keys[];
   __shared__ int hist[dev::kHistWords];
   __shared__ int tmp4[8];
   __shared__ int bcast[2];
-  const int b = blockIdx.x, t = blockIdx.y;
-  const int g = p.group_of_ret[t];
+  const int b = blockIdx.x;
+  const int t0 = (int)(p.unit[blockIdx.y] & 0xFFFFu), ns = (int)(p.unit[blockIdx.y] >> 16);
+  const int g = p.group_of_ret[t0];
   const int qs = b * kBlock;
   const int nrow = min(kBlock, p.N - qs);
   const int qe = qs + nrow - 1;
   const int c_lo = p.force_block0 ? 1 : 0;
   const int c_hi = (qe - p.window >= 0) ? (qe - p.window) / kBlock : -1;
   const int nE = max(0, c_hi - c_lo + 1);
-  int32_t* out = p.sel + ((size_t)t * p.n_qb + b) * p.topk;
+  const size_t row_stride = (size_t)p.n_qb * p.topk;   // between slots' sel rows
+  int32_t* out = p.sel + ((size_t)t0 * p.n_qb + b) * p.topk;
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (p.topk == 0) return;
   if (nE <= p.topk) {
-    for (int x = tid; x < p.topk; x += NT) out[x] = x < nE ? c_lo + x : -1;
+    for (int s = 0; s < ns; ++s)
+      for (int x = tid; x < p.topk; x += NT) out[s * row_stride + x] = x < nE ? c_lo + x : -1;
     return;
   }
-  // A operands: query rows qs + 32 rt + lr, k-half lh
-  dev::bf16x8 qh[2], ql[2];
+  for (int s = 0; s < ns; ++s) {
+    const int t = t0 + s;
+    // A operands: query rows qs + 32 rt + lr, k-half lh
+    dev::bf16x8 qh[2], ql[2];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const int i = rt * 32 + lr;
-    const int row = qs + (i < nrow ? i : 0);
-    split_row8(p.qlow + ((size_t)t * p.N + row) * R + lh * 8, qh[rt], ql[rt]);
-  }
-  const float* kbase = p.klow + (size_t)g * p.N * R;
-  // B operands: keys j0 + 32 kt + lr of block c (rows past N read key N-1,
-  // masked below); the next block's rows are loaded one iteration ahead
-  auto kload = [&](int c, float4 (&v)[2][2]) {
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const float* src = kbase + (size_t)min(c * kBlock + kt * 32 + lr, p.N - 1) * R + lh * 8;
-      v[kt][0] = *reinterpret_cast<const float4*>(src);
-      v[kt][1] = *reinterpret_cast<const float4*>(src + 4);
+    for (int rt = 0; rt < 2; ++rt) {
+      const int i = rt * 32 + lr;
+      const int row = qs + (i < nrow ? i : 0);
+      split_row8(p.qlow + ((size_t)t * p.N + row) * R + lh * 8, qh[rt], ql[rt]);
     }
-  };
-  float4 nk[2][2];
-  kload(c_lo + min(wave, nE - 1), nk);
-  for (int x = wave; x < nE; x += 4) {
-    const int c = c_lo + x;
-    const int j0 = c * kBlock;
-    dev::bf16x8 kh[2], kl[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const float v[8] = {nk[kt][0].x, nk[kt][0].y, nk[kt][0].z, nk[kt][0].w,
-                          nk[kt][1].x, nk[kt][1].y, nk[kt][1].z, nk[kt][1].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        __bf16 h, l;
-        dev::split2(v[e], h, l);
-        kh[kt][e] = h;
-        kl[kt][e] = l;
-      }
-    }
-    kload(c_lo + min(x + 4, nE - 1), nk);
-    const bool edge = j0 + kBlock - 1 > qs;     // some pair may have j > i or j >= N
-    float mx = -__builtin_inff();
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    const float* kbase = p.klow + (size_t)g * p.N * R;
+    // B operands: keys j0 + 32 kt + lr of block c (rows past N read key N-1,
+    // masked below); the next block's rows are loaded one iteration ahead
+    auto kload = [&](int c, float4 (&v)[2][2]) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        // S^T tile: rows = keys (A = k), columns = queries (B = q)
-        dev::f32x16 acc = {};
-        acc = dev::mfma32(kl[kt], qh[rt], acc);
-        acc = dev::mfma32(kh[kt], ql[rt], acc);
-        acc = dev::mfma32(kh[kt], qh[rt], acc);
-        if (edge) {
-          // lane: query column qs + 32 rt + lr; element e: key j0 + 32 kt + 4 lh + 8 (e/4) + e%4
-          const int i = qs + rt * 32 + lr;
-          const bool row_ok = rt * 32 + lr < nrow;
+        const float* src = kbase + (size_t)min(c * kBlock + kt * 32 + lr, p.N - 1) * R + lh * 8;
+        v[kt][0] = *reinterpret_cast<const float4*>(src);
+        v[kt][1] = *reinterpret_cast<const float4*>(src + 4);
+      }
+    };
+    float4 nk[2][2];
+    kload(c_lo + min(wave, nE - 1), nk);
+    for (int x = wave; x < nE; x += 4) {
+      const int c = c_lo + x;
+      const int j0 = c * kBlock;
+      dev::bf16x8 kh[2], kl[2];
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int j = j0 + kt * 32 + lh * 4 + (e >> 2) * 8 + (e & 3);
-            const bool vis = row_ok & (j <= i) & (j < p.N);
-            mx = fmaxf(mx, vis ? acc[e] : -__builtin_inff());
-          }
-        } else {
+      for (int kt = 0; kt < 2; ++kt) {
+        const float v[8] = {nk[kt][0].x, nk[kt][0].y, nk[kt][0].z, nk[kt][0].w,
+                            nk[kt][1].x, nk[kt][1].y, nk[kt][1].z, nk[kt][1].w};
 #pragma unroll
-          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[e]);
+        for (int e = 0; e < 8; ++e) {
+          __bf16 h, l;
+          dev::split2(v[e], h, l);
+          kh[kt][e] = h;
+          kl[kt][e] = l;
         }
       }
-    mx = wave_max(mx);
-    if (lane == 0) keys[x] = dev::order_key(mx);
+      kload(c_lo + min(x + 4, nE - 1), nk);
+      const bool edge = j0 + kBlock - 1 > qs;     // some pair may have j > i or j >= N
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          // S^T tile: rows = keys (A = k), columns = queries (B = q)
+          dev::f32x16 acc = {};
+          acc = dev::mfma32(kl[kt], qh[rt], acc);
+          acc = dev::mfma32(kh[kt], ql[rt], acc);
+          acc = dev::mfma32(kh[kt], qh[rt], acc);
+          if (edge) {
+            // lane: query column qs + 32 rt + lr; element e: key j0 + 32 kt + 4 lh + 8 (e/4) + e%4
+            const int i = qs + rt * 32 + lr;
+            const bool row_ok = rt * 32 + lr < nrow;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int j = j0 + kt * 32 + lh * 4 + (e >> 2) * 8 + (e & 3);
+              const bool vis = row_ok & (j <= i) & (j < p.N);
+              mx = fmaxf(mx, vis ? acc[e] : -__builtin_inff());
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[e]);
+          }
+        }
+      mx = wave_max(mx);
+      if (lane == 0) keys[x] = s == 0 ? dev::order_key(mx) : max(keys[x], dev::order_key(mx));
+    }
   }
   __syncthreads();
-  dev::topk_select(keys, nE, p.topk, p.topk, c_lo, out, hist, tmp4, bcast);
+  if (ns == 1) {
+    dev::topk_select(keys, nE, p.topk, p.topk, c_lo, out, hist, tmp4, bcast);
+    return;
+  }
+  // shared row: select into LDS (the histogram is free once the last radix
+  // pass is done), then write it to every slot of the unit
+  int32_t* shared_row = reinterpret_cast<int32_t*>(hist);
+  dev::topk_select(keys, nE, p.topk, p.topk, c_lo, shared_row, hist, tmp4, bcast);
+  __syncthreads();
+  for (int x = tid; x < ns * p.topk; x += NT) {
+    const int s = x / p.topk, e = x - s * p.topk;
+    out[s * row_stride + e] = shared_row[e];
+  }
 }
 
 }  // namespace
@@ -235,7 +257,7 @@ hipError_t launch_select_blocks(const SelectParams& p, hipStream_t s) {
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(select_blocks_kernel, dim3(p.n_qb, p.n_ret), dim3(NT), lds, s, p);
+  hipLaunchKernelGGL(select_blocks_kernel, dim3(p.n_qb, p.n_units), dim3(NT), lds, s, p);
   return hipGetLastError();
 }
 

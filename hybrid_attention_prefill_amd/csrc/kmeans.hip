@@ -327,6 +327,11 @@ __global__ __launch_bounds__(NT) void cluster_prep_kernel(SelectParams p) {
 // the clusters, into its own region of kCapW slots, the rest of the region
 // zero-filled), and the radix select runs on those 4 * kCapW slots.  A wave
 // that finds more than kCapW candidates sends the block to the full select.
+//
+// A unit of several slots (group-shared selection) repeats the scoring for
+// each slot and keeps the max key per cluster (the order key is monotone);
+// a lane owns the same clusters for every slot, so the lane maxima and the
+// prefilter hold for the max scores as they do for one slot.
 constexpr int kSelBlocks = 1;
 constexpr int kGroups = 128;      // scoring lanes (4 waves x 32)
 constexpr int kCapW = 192;        // candidate slots per wave
@@ -344,38 +349,45 @@ __global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
   __shared__ int ovf;
   __shared__ uint64_t elmask[kMaxSelCand / 64];   // bit m: cluster m eligible for this block
   __shared__ uint32_t sink_word;                  // store target of padding lanes
-  const int t = blockIdx.y, tid = threadIdx.x;
+  const int t0 = (int)(p.unit[blockIdx.y] & 0xFFFFu), ns = (int)(p.unit[blockIdx.y] >> 16);
+  const int tid = threadIdx.x;
   const int lane = tid & 63, lr = lane & 31, lh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar loop control
-  const int g = p.group_of_ret[t];
+  const int g = p.group_of_ret[t0];
   const int b0 = blockIdx.x * kSelBlocks;
   const int nb = min(kSelBlocks, p.n_qb - b0);
   if (p.topk == 0) return;
 
   int nrow[kSelBlocks], lim[kSelBlocks];
-  dev::bf16x8 qh[kSelBlocks][2], ql[kSelBlocks][2];
 #pragma unroll
   for (int bi = 0; bi < kSelBlocks; ++bi) {
     const int qs0 = (b0 + bi) * kBlock;
     nrow[bi] = bi < nb ? min(kBlock, p.N - qs0) : 0;
     lim[bi] = bi < nb ? qs0 + nrow[bi] - 1 - p.window : -1;
-    // rows past the end of a ragged last block repeat the block's first
-    // row, so the row max needs no mask
+  }
+  // split query rows of slot t; rows past the end of a ragged last block
+  // repeat the block's first row, so the row max needs no mask
+  dev::bf16x8 qh[kSelBlocks][2], ql[kSelBlocks][2];
+  auto load_q = [&](int t) {
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      const int i = rt * 32 + lr;
-      const int row = bi < nb ? qs0 + (i < nrow[bi] ? i : 0) : 0;
-      const float* qp = p.qlow + ((size_t)t * p.N + row) * R + lh * 8;
+    for (int bi = 0; bi < kSelBlocks; ++bi) {
+      const int qs0 = (b0 + bi) * kBlock;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float v = qp[e];
-        __bf16 hh, ll;
-        dev::split2(v, hh, ll);
-        qh[bi][rt][e] = hh;
-        ql[bi][rt][e] = ll;
+      for (int rt = 0; rt < 2; ++rt) {
+        const int i = rt * 32 + lr;
+        const int row = bi < nb ? qs0 + (i < nrow[bi] ? i : 0) : 0;
+        const float* qp = p.qlow + ((size_t)t * p.N + row) * R + lh * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = qp[e];
+          __bf16 hh, ll;
+          dev::split2(v, hh, ll);
+          qh[bi][rt][e] = hh;
+          ql[bi][rt][e] = ll;
+        }
       }
     }
-  }
+  };
   const __bf16* chi = p.c_hi + (size_t)g * p.M * R;
   const __bf16* clo = p.c_lo + (size_t)g * p.M * R;
   const int32_t* fm = p.first_mem + (size_t)g * p.M;
@@ -406,45 +418,49 @@ __global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
     bl = *reinterpret_cast<const dev::bf16x8*>(clo + (size_t)m * R + lh * 8);
   };
   dev::bf16x8 rbh[kPre], rbl[kPre];
-  // slot order, as in the loop body, so the first group waits only for its own slot
-#pragma unroll
-  for (int u = 0; u < kPre; ++u) {
-    ld(min(n_tiles - 1, wave + 4 * u), rbh[u], rbl[u]);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  // Groups of kPre tiles run whole (tiles past the end compute on the last
-  // tile and store nothing: their centroid index is >= M), so the body has no
-  // branches around loads.  A slot is refilled right after its MFMAs have
-  // consumed it, so the ring needs no register copies.
-  for (int x0 = wave; x0 < n_tiles; x0 += 4 * kPre) {
+  for (int s = 0; s < ns; ++s) {
+    load_q(t0 + s);
+    // slot order, as in the loop body, so the first group waits only for its own slot
 #pragma unroll
     for (int u = 0; u < kPre; ++u) {
-      const int x = x0 + 4 * u;
-      const int m = x * 32 + lr;
-      const bool mok = m < p.M;
-      float mx = -__builtin_inff();
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        dev::f32x16 acc = {};
-        acc = dev::mfma32(ql[0][rt], rbh[u], acc);
-        acc = dev::mfma32(qh[0][rt], rbl[u], acc);
-        acc = dev::mfma32(qh[0][rt], rbh[u], acc);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[e]);
-      }
-      // keep the refill after the slot's last reads (no register rotation)
+      ld(min(n_tiles - 1, wave + 4 * u), rbh[u], rbl[u]);
       __builtin_amdgcn_sched_barrier(0);
-      ld(min(x + 4 * kPre, n_tiles - 1), rbh[u], rbl[u]);
-      mx = dev::pair32_max(mx);
-      // branch-free: both lane halves store the same key; padding lanes store
-      // to a dummy word and count nothing
-      const int mc = min(m, p.M - 1);
-      const bool el = (bool)((elmask[mc >> 6] >> (mc & 63)) & 1ull) & mok;
-      const uint32_t key = el ? dev::order_key(mx) : 0u;
-      uint32_t* dst = mok ? &keys[0][mc] : &sink_word;
-      *dst = key;
-      gmx = max(gmx, key);
-      n_el[0] += (int)(el & (lh == 0));
+    }
+    // Groups of kPre tiles run whole (tiles past the end compute on the last
+    // tile and store nothing: their centroid index is >= M), so the body has no
+    // branches around loads.  A slot is refilled right after its MFMAs have
+    // consumed it, so the ring needs no register copies.
+    for (int x0 = wave; x0 < n_tiles; x0 += 4 * kPre) {
+#pragma unroll
+      for (int u = 0; u < kPre; ++u) {
+        const int x = x0 + 4 * u;
+        const int m = x * 32 + lr;
+        const bool mok = m < p.M;
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          dev::f32x16 acc = {};
+          acc = dev::mfma32(ql[0][rt], rbh[u], acc);
+          acc = dev::mfma32(qh[0][rt], rbl[u], acc);
+          acc = dev::mfma32(qh[0][rt], rbh[u], acc);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[e]);
+        }
+        // keep the refill after the slot's last reads (no register rotation)
+        __builtin_amdgcn_sched_barrier(0);
+        ld(min(x + 4 * kPre, n_tiles - 1), rbh[u], rbl[u]);
+        mx = dev::pair32_max(mx);
+        // branch-free: both lane halves store the same key; padding lanes store
+        // to a dummy word and count nothing
+        const int mc = min(m, p.M - 1);
+        const bool el = (bool)((elmask[mc >> 6] >> (mc & 63)) & 1ull) & mok;
+        const uint32_t key = el ? dev::order_key(mx) : 0u;
+        uint32_t* dst = mok ? &keys[0][mc] : &sink_word;
+        // later slots of a unit keep the max with what this lane stored before
+        *dst = s > 0 ? max(*dst, key) : key;
+        gmx = max(gmx, key);
+        n_el[0] += (int)(el & (lh == 0) & (s == 0));
+      }
     }
   }
   if (lh == 0) gmax[wave * 32 + lr] = gmx;
@@ -455,9 +471,22 @@ __global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
   int nE;
   dev::block_excl_scan(n_el[0], tmp4, &nE);     // (synchronizes)
   const int k = min(p.topk, nE);
-  int32_t* out = p.sel + ((size_t)t * p.n_qb + b0) * p.topk;
+  const size_t row_stride = (size_t)p.n_qb * p.topk;   // between slots' sel rows
+  int32_t* out = p.sel + ((size_t)t0 * p.n_qb + b0) * p.topk;
+  // a unit of several slots selects into LDS (the histogram is free once the
+  // last radix pass is done) and copies the row to every slot
+  int32_t* dst_row = ns == 1 ? out : reinterpret_cast<int32_t*>(hist);
+  auto copy_row = [&]() {
+    if (ns == 1) return;
+    __syncthreads();
+    for (int x = tid; x < ns * p.topk; x += NT) {
+      const int s = x / p.topk, e = x - s * p.topk;
+      out[s * row_stride + e] = dst_row[e];
+    }
+  };
   if (k > kGroups) {
-    dev::topk_select(keys[0], p.M, k, p.topk, 0, out, hist, tmp4, bcast);
+    dev::topk_select(keys[0], p.M, k, p.topk, 0, dst_row, hist, tmp4, bcast);
+    copy_row();
     return;
   }
   // tau = k-th largest lane maximum (the one with #{>} < k <= #{>=});
@@ -497,10 +526,11 @@ __global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
   }
   __syncthreads();
   if (ovf == 0) {
-    dev::topk_select(ckeys, 4 * kCapW, k, p.topk, 0, out, hist, tmp4, bcast, cidx);
+    dev::topk_select(ckeys, 4 * kCapW, k, p.topk, 0, dst_row, hist, tmp4, bcast, cidx);
   } else {
-    dev::topk_select(keys[0], p.M, k, p.topk, 0, out, hist, tmp4, bcast);
+    dev::topk_select(keys[0], p.M, k, p.topk, 0, dst_row, hist, tmp4, bcast);
   }
+  copy_row();
 }
 
 }  // namespace
@@ -531,8 +561,8 @@ hipError_t launch_kmeans(KmeansParams p, int Hkv, int iters, hipStream_t s) {
 hipError_t launch_select_clusters(const SelectParams& p, int Hkv, hipStream_t s) {
   if (p.n_ret == 0 || p.n_qb == 0) return hipSuccess;
   hipLaunchKernelGGL(cluster_prep_kernel, dim3((p.M + NT - 1) / NT, Hkv), dim3(NT), 0, s, p);
-  hipLaunchKernelGGL(select_clusters_kernel, dim3((p.n_qb + kSelBlocks - 1) / kSelBlocks, p.n_ret), dim3(NT), 0,
-                     s, p);
+  hipLaunchKernelGGL(select_clusters_kernel, dim3((p.n_qb + kSelBlocks - 1) / kSelBlocks, p.n_units), dim3(NT),
+                     0, s, p);
   return hipGetLastError();
 }
 

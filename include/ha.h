@@ -19,6 +19,8 @@
  *     low-rank space; all-sparse mode when most heads are retrieval heads.
  *   36kr interview "Agent 的注意力系统" (TriangleMix introduction): streaming
  *     region + last Q-K region in deep layers; top-k over key blocks.
+ *   Same interview, GQA answer: queries of one GQA group share their keys, so
+ *     one selection can serve the group (group_select).
  *   "一个 Attention,两种工作模式" (Orthros), "Prefilling" and design sections:
  *     SWA for all tokens, full cross-attention for output positions, a light
  *     scale-offset separating the two query roles.
@@ -51,7 +53,7 @@
 extern "C" {
 #endif
 
-#define HA_VERSION 1
+#define HA_VERSION 2
 
 typedef enum {
   HA_SWA = 0,        /* causal sliding window: keys i-w < j <= i */
@@ -86,6 +88,12 @@ typedef struct {
   int32_t sink;          /* TriangleMix: keys [0, sink) always visible */
   int32_t last_q;        /* TriangleMix: rows >= N - last_q attend densely */
   int32_t n_out;         /* Orthros: the last n_out rows also run cross-attention */
+  int32_t group_select;  /* 0: one selection per retrieval head and query block;
+                          * 1: one per KV head and query block, scored by the max
+                          *    over the group's retrieval heads and shared by them
+                          *    (36kr interview, GQA answer: the queries of one GQA
+                          *    group share their keys); every retrieval head's row
+                          *    of `sel` then holds its group's selection */
 } ha_layer_desc;
 
 /* Optional copies of the indexer's intermediate results (caller-owned device
@@ -170,7 +178,9 @@ int ha_attn_band(const ha_layer_desc* desc, const int32_t* head_kind,
 
 /* Stage: retrieval heads: window U selected keys (U key block 0 when forced).
  * Block mode reads sel only; cluster mode also reads assign/csr.
- *   csr_off, csr_mem: NULL in block mode. */
+ *   csr_off, csr_mem: NULL in block mode.
+ * With group_select = 1 every retrieval head of a KV group reads the sel row
+ * of the group's first retrieval head (the rows ha_select_* writes are equal). */
 int ha_attn_gather(const ha_layer_desc* desc, const int32_t* head_kind,
                    const void* Q, const void* K, const void* V, const int32_t* sel,
                    const int32_t* csr_off, const int32_t* csr_mem, float* O,

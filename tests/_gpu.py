@@ -37,7 +37,7 @@ def run_gpu(w, li, return_aux=True):
     res = ha.hybrid_attn_prefill(
         Q, K, V, w.head_kind, w.window, P, topk=w.topk, block=w.q_block, force_block0=w.force_block0,
         n_clusters=w.n_clusters, kmeans_iters=w.kmeans_iters, kmeans_stride=w.kmeans_stride,
-        sink=w.sink, last_q=w.last_q, n_out=w.n_out, xa_scale=xs, xa_offset=xo,
+        sink=w.sink, last_q=w.last_q, n_out=w.n_out, group_select=w.group_select, xa_scale=xs, xa_offset=xo,
         return_aux=return_aux and bool(w.ret_heads))
     torch.cuda.synchronize()
     if not isinstance(res, tuple):
@@ -62,6 +62,20 @@ def assert_lowrank(gpu, ref, what=""):
     nrm = np.linalg.norm(ref, axis=-1, keepdims=True)
     bad = np.abs(gpu - ref) > LOWRANK_REL * np.maximum(nrm, 1e-30)
     assert not bad.any(), f"{what}: {int(bad.sum())} low-rank entries off"
+
+
+def check_group_rows(sel, w):
+    """Group-shared selection: the retrieval heads of a KV group hold equal rows."""
+    if not w.group_select:
+        return
+    G = w.n_q_heads // w.n_kv_heads
+    first = {}
+    for t, h in enumerate(w.ret_heads):
+        g = h // G
+        if g in first:
+            np.testing.assert_array_equal(sel[t], sel[first[g]], err_msg=f"head {h} vs group {g} row")
+        else:
+            first[g] = t
 
 
 def check_selection(gpu_sel, eligible, scores, k, what=""):

@@ -127,6 +127,7 @@ def _layer_cluster(w, blocks=None):
     off = aux["csr_off"].cpu().numpy()
     mem = aux["csr_mem"].cpu().numpy()
     sel = aux["sel"].cpu().numpy()
+    _gpu.check_group_rows(sel, w)
     for g in range(w.n_kv_heads):
         check_csr(asg[g], off[g], mem[g], w.n_clusters, f"kv {g}")
         # final centroids are the means of the final assignment
@@ -156,6 +157,22 @@ def test_cluster_layer_small(N, M, window, topk):
     base = synth.WORKLOADS["allsparse_1m"]
     w = synth.configs.shrink(base, N, n_clusters=M, window=window, n_needles=2)
     w = w.with_(kmeans_stride=N // M if N // M >= 1 else 1, topk=topk, kmeans_iters=3)
+    _layer_cluster(w)
+
+
+@pytest.mark.parametrize("N,M,window,topk", [(4096, 64, 256, 4), (3000, 50, 100, 8), (2048, 128, 200, 200)])
+def test_group_select_cluster_layer(N, M, window, topk):
+    base = synth.WORKLOADS["allsparse_1m_gqa"]
+    w = synth.configs.shrink(base, N, n_clusters=M, window=window, n_needles=2)
+    w = w.with_(kmeans_stride=N // M, topk=topk, kmeans_iters=3)
+    _layer_cluster(w)
+
+
+def test_group_select_cluster_mixed_with_swa_heads():
+    base = synth.WORKLOADS["allsparse_1m_gqa"]
+    kinds = tuple(1 if h % 3 == 0 else 0 for h in range(16))
+    w = synth.configs.shrink(base, 6000, n_clusters=96, window=300, n_needles=2)
+    w = w.with_(head_kind=kinds, kmeans_stride=62, topk=6, kmeans_iters=2)
     _layer_cluster(w)
 
 

@@ -23,9 +23,9 @@ def _sample_blocks(w, extra=()):
     return sorted(set(b for b in edge + strata + list(extra) if 0 <= b < n))
 
 
-def _run(name, heads=None, blocks=None):
-    w = synth.WORKLOADS[name]
-    print(f"\n[case] full-size {name}", flush=True)
+def _run(name, heads=None, blocks=None, **changes):
+    w = synth.WORKLOADS[name].with_(**changes)
+    print(f"\n[case] full-size {name} {changes}", flush=True)
     li = synth.make_layer_inputs(w)
     O, O_out, aux = _gpu.run_gpu(w, li)
     blocks = _sample_blocks(w) if blocks is None else blocks
@@ -40,6 +40,7 @@ def _run(name, heads=None, blocks=None):
     ref = layer_prefill(w, q_rows, K, V, P, xs, xo, blocks=blocks, heads=heads)
     if w.ret_heads:
         sel = aux["sel"].cpu().numpy()
+        _gpu.check_group_rows(sel, w)
         override = {}
         n_diff = 0
         for t, h in enumerate(w.ret_heads):
@@ -61,6 +62,11 @@ def _run(name, heads=None, blocks=None):
 
 def test_qwen3_30b_layer_32k():
     _run("qwen3_30b_a3b_32k")
+
+
+def test_qwen3_30b_layer_32k_group_select():
+    # retrieval heads 0 and 7 share KV head 0: one shared selection
+    _run("qwen3_30b_a3b_32k", group_select=1)
 
 
 def test_trianglemix_layer_128k():
@@ -143,3 +149,42 @@ def test_allsparse_layer_1m():
     ref = layer_prefill(w, q_rows, K, V, P, blocks=blocks, kmeans_override=km, sel_override=override)
     mx, mean = _gpu.assert_close_out(O.cpu().numpy()[ref.rows], ref.O, w.name)
     print(f"allsparse_1m: {len(blocks)} blocks x 16 heads, max abs {mx:.3e}, mean abs {mean:.3e}")
+
+
+def test_allsparse_gqa_layer_1m():
+    """The 1M all-retrieval layer with group-shared selection (one top-k per
+    KV head and query block, scored by the max over the group's 8 heads):
+    equal rows within each group, the CSR of the GPU's clusters, and the
+    selection and outputs of 24 sampled query blocks, every head."""
+    w = synth.WORKLOADS["allsparse_1m_gqa"]
+    print(f"\n[case] full-size {w.name}", flush=True)
+    li = synth.make_layer_inputs(w)
+    O, _, aux = _gpu.run_gpu(w, li)
+    C = aux["centroids"].cpu().numpy()
+    asg = aux["assign"].cpu().numpy()
+    off = aux["csr_off"].cpu().numpy()
+    mem = aux["csr_mem"].cpu().numpy()
+    sel = aux["sel"].cpu().numpy()
+    _gpu.check_group_rows(sel, w)
+    for g in range(w.n_kv_heads):
+        cnt = np.bincount(asg[g], minlength=w.n_clusters)
+        np.testing.assert_array_equal(off[g], np.r_[0, np.cumsum(cnt)])
+        np.testing.assert_array_equal(mem[g], np.lexsort((np.arange(w.n_tokens), asg[g])))
+    n = w.n_qb
+    rng = np.random.default_rng(6)
+    blocks = sorted({int(rng.integers(s * n // 24, (s + 1) * n // 24)) for s in range(24)} | {n - 1})
+    K, V = si.bf16_to_f64(li.K), si.bf16_to_f64(li.V)
+    P = li.P.astype(np.float64)
+    q_rows = lambda a, b: si.bf16_to_f64(li.Q[a:b])
+    km = {g: (C[g], asg[g]) for g in range(w.n_kv_heads)}
+    ref = layer_prefill(w, q_rows, K, V, P, blocks=blocks, kmeans_override=km)
+    override, n_diff = {}, 0
+    for t, h in enumerate(w.ret_heads):
+        override[h] = {}
+        for b, (E, s) in ref.scored[h].items():
+            n_diff += _gpu.check_selection(sel[t, b], E, s, w.topk, f"head {h} block {b}")
+            override[h][b] = np.array([x for x in sel[t, b] if x >= 0], dtype=np.int64)
+    print(f"selection near-tie differences: {n_diff}", flush=True)
+    ref = layer_prefill(w, q_rows, K, V, P, blocks=blocks, kmeans_override=km, sel_override=override)
+    mx, mean = _gpu.assert_close_out(O.cpu().numpy()[ref.rows], ref.O, w.name)
+    print(f"{w.name}: {len(blocks)} blocks x 16 heads, max abs {mx:.3e}, mean abs {mean:.3e}")

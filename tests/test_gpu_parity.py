@@ -25,6 +25,7 @@ def _compare(w, blocks=None, check_sel=True):
     Og = O.cpu().numpy()[ref.rows]
     if w.ret_heads and check_sel:
         sel = aux["sel"].cpu().numpy()
+        _gpu.check_group_rows(sel, w)
         klow = aux["klow"].cpu().numpy()
         for g, kl in ref.klow.items():
             _gpu.assert_lowrank(klow[g], kl, f"klow[{g}]")
@@ -77,6 +78,25 @@ def test_retrieval_block_mode(N, window, topk, f0):
     kinds = [HEAD_RETRIEVAL, HEAD_SWA, HEAD_RETRIEVAL, HEAD_RETRIEVAL, HEAD_SWA, HEAD_RETRIEVAL, HEAD_RETRIEVAL,
              HEAD_RETRIEVAL]
     _compare(_layer(kinds, N, window=window, topk=topk, force_block0=f0))
+
+
+@pytest.mark.parametrize("N,window,topk,f0", [(1000, 100, 3, 0), (1337, 64, 8, 1), (700, 1, 2, 0),
+                                              (640, 50, 100, 0), (300, 5000, 4, 1)])
+def test_group_select_block_mode(N, window, topk, f0):
+    # groups of 3 retrieval heads (one pack each) next to streaming heads
+    kinds = [HEAD_RETRIEVAL, HEAD_SWA, HEAD_RETRIEVAL, HEAD_RETRIEVAL, HEAD_SWA, HEAD_RETRIEVAL, HEAD_RETRIEVAL,
+             HEAD_RETRIEVAL]
+    _compare(_layer(kinds, N, window=window, topk=topk, force_block0=f0, group_select=1))
+
+
+def test_group_select_pack_shapes():
+    # G = 8, all retrieval: two full packs per group
+    _compare(_layer([HEAD_RETRIEVAL] * 16, 900, Hkv=2, window=70, topk=4, group_select=1))
+    # G = 6: a full pack and a half-empty one
+    _compare(_layer([HEAD_RETRIEVAL] * 6, 900, Hkv=1, window=70, topk=5, force_block0=1, group_select=1))
+    # one retrieval head per group: same as per-head selection
+    kinds = [HEAD_RETRIEVAL if h % 4 == 1 else HEAD_SWA for h in range(8)]
+    _compare(_layer(kinds, 900, window=70, topk=3, group_select=1))
 
 
 def test_tiny_hybrid_layer_full():
