@@ -152,7 +152,8 @@ def layer_work(w, sel=None, csr=None):
                 act += pairs_retrieval_clusters(N, w.window, sel[t], csr[0][g], csr[1][g])
             else:
                 act += pairs_retrieval_blocks(N, w.window, sel[t], w.force_block0)
-    act += w.n_out * w.n_q_heads * N
+    # cross-attention rows p = N - n_out .. N - 1 see keys 0..p
+    act += w.n_q_heads * (w.n_out * (N - w.n_out) + w.n_out * (w.n_out + 1) // 2)
     return act, w.n_q_heads * pairs_dense(N)
 
 
@@ -270,7 +271,8 @@ def cpu_baseline(names, log, budget_s=20.0):
             xs, xo = s.astype(np.float64), o.astype(np.float64)
         b = w.n_qb - 1
         t = time.time()
-        res = layer_prefill(w, lambda a, c: si.bf16_to_f64(si.gen_q(w, a, c)), K, V, P, xs, xo, blocks=[b])
+        res = layer_prefill(w, lambda a, c: si.bf16_to_f64(si.gen_q(w, a, c)), K, V, P, xs, xo, blocks=[b],
+                            out_rows=[w.n_out - 1] if w.n_out else None)
         dt = time.time() - t
         # attention pairs the oracle evaluated for that block (+ the cross row)
         act = 0
@@ -285,10 +287,10 @@ def cpu_baseline(names, log, budget_s=20.0):
                     int(np.minimum(w.window, rows + 1).sum())
             else:
                 act += int(np.minimum(w.window, rows + 1).sum()) + 64 * 64 * len(res.sel[h][b])
-        act += w.n_out * w.n_q_heads * w.n_tokens
+        act += w.n_q_heads * w.n_tokens if w.n_out else 0   # the last output row: all N keys
         flops += 4.0 * w.head_dim * act
         secs += dt
-        done.append(f"{name}: block {b} all heads")
+        done.append(f"{name}: block {b} all heads" + (", last output row" if w.n_out else ""))
         log(f"cpu oracle {name}: {dt:.1f}s")
         if secs > budget_s:
             break

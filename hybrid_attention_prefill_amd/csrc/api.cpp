@@ -32,7 +32,9 @@ int check_desc(const ha_layer_desc* d, const int32_t* kinds, Heads* out) {
   if (d->head_dim != kHeadDim) return HA_ERR_UNSUPPORTED;
   if (d->q_block != kBlock || d->k_block != kBlock) return HA_ERR_UNSUPPORTED;
   if (d->n_out < 0 || d->n_out > d->n_tokens) return HA_ERR_ARG;
-  if (d->n_out > 0 && d->n_q_heads / d->n_kv_heads > 16) return HA_ERR_UNSUPPORTED;
+  // the memory-bound path for a few output rows keeps a KV head's queries in LDS
+  if (d->n_out > 0 && d->n_out < kCrossMfmaMinRows && d->n_q_heads / d->n_kv_heads > 16)
+    return HA_ERR_UNSUPPORTED;
   if (!kinds) return HA_ERR_ARG;
   if (d->group_select != 0 && d->group_select != 1) return HA_ERR_ARG;
   Heads h;
@@ -75,6 +77,39 @@ int check_desc(const ha_layer_desc* d, const int32_t* kinds, Heads* out) {
 inline int n_qb_of(const ha_layer_desc* d) { return (d->n_tokens + kBlock - 1) / kBlock; }
 inline int n_cross_chunks(const ha_layer_desc* d) { return (d->n_tokens + kCrossChunk - 1) / kCrossChunk; }
 
+// Orthros cross-attention with n_out >= kCrossMfmaMinRows runs on the matrix
+// cores: workgroups = packs x row tiles x key chunks.  Few row tiles split
+// the key range so that about 1024 workgroups run; chunks hold >= 8 tiles.
+struct CrossPlan {
+  int n_packs, n_qt, n_kc, kc_tiles;
+};
+
+CrossPlan cross_plan(const ha_layer_desc* d) {
+  CrossPlan c{};
+  const int G = d->n_q_heads / d->n_kv_heads;
+  c.n_packs = d->n_kv_heads * ((G + 3) / 4);
+  c.n_qt = (d->n_out + kBlock - 1) / kBlock;
+  const int n_kt = (d->n_tokens + kBlock - 1) / kBlock;
+  const int base = c.n_packs * c.n_qt;
+  int n_kc = base >= 512 ? 1 : (1024 + base - 1) / base;
+  n_kc = std::max(1, std::min(n_kc, n_kt / 8));
+  c.kc_tiles = (n_kt + n_kc - 1) / n_kc;
+  c.n_kc = (n_kt + c.kc_tiles - 1) / c.kc_tiles;
+  return c;
+}
+
+// Workspace of the cross-attention stage (partials of either path).
+size_t cross_ws_bytes(const ha_layer_desc* d) {
+  if (d->n_out <= 0) return 0;
+  const size_t n_out = (size_t)d->n_out, Hq = (size_t)d->n_q_heads;
+  if (d->n_out < kCrossMfmaMinRows)
+    return align_up(n_out * Hq * (size_t)n_cross_chunks(d) * (kHeadDim + 2) * sizeof(float));
+  const CrossPlan c = cross_plan(d);
+  if (c.n_kc == 1) return 0;
+  return align_up((size_t)c.n_kc * n_out * Hq * kHeadDim * sizeof(float)) +
+         align_up((size_t)c.n_kc * n_out * Hq * sizeof(float));
+}
+
 struct Layout {
   size_t qlow, klow, sel, lse, cent, assign, csr_off, csr_mem, km_scratch, cross, total;
 };
@@ -105,7 +140,7 @@ Layout layout_of(const ha_layer_desc* d, const Heads& h) {
                                select_clusters_scratch_bytes((int)M, d->n_kv_heads)))
            : 0;
   L.cross = off;
-  off += align_up((size_t)d->n_out * d->n_q_heads * (size_t)n_cross_chunks(d) * (kHeadDim + 2) * sizeof(float));
+  off += cross_ws_bytes(d);
   L.total = off;
   return L;
 }
@@ -127,7 +162,7 @@ void build_packs(const ha_layer_desc* d, const int32_t* kinds, int kind, const s
     int cnt = 0, row = -1;
     for (int hh = 0; hh < G; ++hh) {
       const int h = g * G + hh;
-      if (kinds[h] != kind) continue;
+      if (kind >= 0 && kinds[h] != kind) continue;   // kind < 0: every head
       const int sl = slot.empty() ? 0 : std::max(0, slot[h]);
       if (row < 0) row = sl;
       w |= (uint32_t)h << (8 * cnt);
@@ -329,6 +364,27 @@ int run_select_clusters(const ha_layer_desc* d, const Heads& h, const float* qlo
 int run_cross(const ha_layer_desc* d, const void* Q, const void* K, const void* V, const float* xs,
               const float* xo, float* O_out, float* part, hipStream_t s) {
   if (d->n_out == 0) return HA_OK;
+  if (d->n_out >= kCrossMfmaMinRows) {
+    AttnParams p = attn_params(d, Q, K, V, nullptr);
+    const CrossPlan c = cross_plan(d);
+    p.kind = DENSE;
+    p.xs = xs;
+    p.xo = xo;
+    p.O_out = O_out;
+    p.row0 = d->n_tokens - d->n_out;
+    p.n_out = d->n_out;
+    p.n_qt = c.n_qt;
+    p.n_kc = c.n_kc;
+    p.kc_tiles = c.kc_tiles;
+    if (c.n_kc > 1) {
+      p.part = part;
+      p.part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(part) +
+                                            align_up((size_t)c.n_kc * d->n_out * d->n_q_heads * kHeadDim * sizeof(float)));
+    }
+    PackTable pt;
+    build_packs(d, nullptr, -1, {}, &pt);
+    return dev_status(launch_attn_cross_mfma(p, pt, s));
+  }
   CrossParams cp{};
   cp.Q = static_cast<const uint16_t*>(Q);
   cp.K = static_cast<const uint16_t*>(K);
@@ -513,11 +569,10 @@ int ha_attn_cross(const ha_layer_desc* desc, const void* Q, const void* K, const
       desc->n_q_heads % desc->n_kv_heads != 0 || desc->n_out < 1 || desc->n_out > desc->n_tokens)
     return HA_ERR_ARG;
   if (desc->head_dim != kHeadDim) return desc->head_dim < 1 ? HA_ERR_ARG : HA_ERR_UNSUPPORTED;
-  if (desc->n_q_heads / desc->n_kv_heads > 16 || desc->n_q_heads > kMaxHeads) return HA_ERR_UNSUPPORTED;
+  if (desc->n_q_heads > kMaxHeads) return HA_ERR_UNSUPPORTED;
+  if (desc->n_out < kCrossMfmaMinRows && desc->n_q_heads / desc->n_kv_heads > 16) return HA_ERR_UNSUPPORTED;
   if (!Q || !K || !V || !xa_scale || !xa_offset || !O_out) return HA_ERR_ARG;
-  const size_t need = align_up((size_t)desc->n_out * desc->n_q_heads * (size_t)n_cross_chunks(desc) *
-                               (kHeadDim + 2) * sizeof(float));
-  if (!ws_ok(workspace, ws_bytes, need)) return HA_ERR_WORKSPACE;
+  if (!ws_ok(workspace, ws_bytes, cross_ws_bytes(desc))) return HA_ERR_WORKSPACE;
   return run_cross(desc, Q, K, V, xa_scale, xa_offset, O_out, static_cast<float*>(workspace),
                    static_cast<hipStream_t>(stream));
 }

@@ -170,6 +170,7 @@ __device__ __forceinline__ void schedule_reads_ahead() {
   __builtin_amdgcn_sched_group_barrier(0x008, kAhead, Id);
 }
 
+
 struct WaveAcc {
   f32x16 o[4];   // O^T: [d block]
   float m;       // running max (raw score units) of this lane's query
@@ -194,10 +195,13 @@ __device__ __forceinline__ bool tile_empty(const MaskSpec& ms, int q0, int k0) {
 }
 
 // One 64-key tile (keys k0 .. k0+63) against the wave's 32 query rows: one
-// online-softmax step.
+// online-softmax step.  kSplitQ: the query is the sum of two bf16 parts,
+// qf in registers and the low part in LDS (qlo: this wave's 8 fragments x
+// 64 lanes), so S takes two products per k-step.
+template <bool kSplitQ>
 __device__ __forceinline__ void tile_compute(const uint16_t* __restrict__ buf, const bf16x8 (&qf)[8],
-                                             WaveAcc& acc, int lane, int q0, int k0, const MaskSpec& ms,
-                                             float c) {
+                                             const uint16_t* __restrict__ qlo, WaveAcc& acc, int lane, int q0,
+                                             int k0, const MaskSpec& ms, float c) {
   const uint16_t* Ks = buf;
   const uint16_t* Vt = buf + K_ELEMS;
   const int lr = lane & 31, lh = lane >> 5;
@@ -211,14 +215,17 @@ __device__ __forceinline__ void tile_compute(const uint16_t* __restrict__ buf, c
     for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
+    bf16x8 qlt;
+    if constexpr (kSplitQ) qlt = *reinterpret_cast<const bf16x8*>(qlo + (t * 64 + lane) * 8);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + (kb * 32 + lr) * KSTR + t * 16 + lh * 8);
       s[kb] = mfma(kf, qf[t], s[kb]);
+      if constexpr (kSplitQ) s[kb] = mfma(kf, qlt, s[kb]);
     }
   }
   // issue order: fragment reads run kAhead MFMAs ahead of their use
-  schedule_reads_ahead<0>();
+  if constexpr (!kSplitQ) schedule_reads_ahead<0>();
 
   if (!full) {
     const int i = q0 + lr;
@@ -335,20 +342,89 @@ __device__ __forceinline__ void store_o(const WaveAcc& acc, float* __restrict__ 
     }
 }
 
+// Orthros cross-attention query of the wave's rows: q' = q * s_h + o_h in
+// fp32 (Orthros page, design section: a scale-offset separates the cross-
+// attention query from the SWA query), held as two bf16 parts hi + lo
+// (relative error ~2^-16): hi in registers, lo in the wave's LDS region
+// (written and read back by the same lane); rows >= N are zero.
+__device__ __forceinline__ void load_q_cross(bf16x8 (&qh)[8], uint16_t* qlo, const AttnParams& p, int h, int q0,
+                                             int lane) {
+  const int i = q0 + (lane & 31), lh = lane >> 5;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int d0 = t * 16 + lh * 8;
+    if (i < p.N) {
+      const bf16x8 q = *reinterpret_cast<const bf16x8*>(p.Q + ((size_t)i * p.Hq + h) * D + d0);
+      const float* sp = p.xs + (size_t)h * D + d0;
+      const float* op = p.xo + (size_t)h * D + d0;
+      bf16x8 lo8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        __bf16 hi, lo;
+        dev::split2(fmaf((float)q[e], sp[e], op[e]), hi, lo);
+        qh[t][e] = hi;
+        lo8[e] = lo;
+      }
+      *reinterpret_cast<bf16x8*>(qlo + (t * 64 + lane) * 8) = lo8;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qh[t][e] = (__bf16)0.f;
+      *reinterpret_cast<bf16x8*>(qlo + (t * 64 + lane) * 8) = qh[t];
+    }
+  }
+}
+
+// Cross-attention rows: normalised output to O_out (one key chunk), or the
+// chunk's normalised partial and log2-sum-exp (split key range).
+__device__ __forceinline__ void store_cross(const WaveAcc& acc, const AttnParams& p, int kc, int h, int q0,
+                                            int lane) {
+  const int lr = lane & 31, lh = lane >> 5;
+  const float lt = dev::pair32_sum(acc.l);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const int i = q0 + lr;
+  if (i >= p.N) return;
+  const size_t r = (size_t)(i - p.row0);
+  float* row;
+  if (p.n_kc == 1) {
+    row = p.O_out + (r * p.Hq + h) * D;
+  } else {
+    const size_t pr = ((size_t)kc * p.n_out + r) * p.Hq + h;
+    row = p.part + pr * D;
+    if (lh == 0) p.part_lse[pr] = lt > 0.f ? acc.m * p.c + __log2f(lt) : -__builtin_inff();
+  }
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      float4 v;
+      v.x = acc.o[db][r4 * 4 + 0] * inv;
+      v.y = acc.o[db][r4 * 4 + 1] * inv;
+      v.z = acc.o[db][r4 * 4 + 2] * inv;
+      v.w = acc.o[db][r4 * 4 + 3] * inv;
+      *reinterpret_cast<float4*>(row + db * 32 + lh * 4 + r4 * 8) = v;
+    }
+}
+
 // Shared pipeline over T tiles; k0_of(idx) is the first key of tile idx.
 // Step t first stages tile t+1 (registers loaded during step t-1) into the
 // other LDS buffer, which tile t-1 left before the last barrier, and starts
 // the global loads of tile t+2 into the same registers; then it computes
 // tile t.  The LDS writes drain under the compute; one barrier per step.
-template <class K0Of>
+// kCross: Orthros cross-attention rows (split query, low parts in LDS after
+// the two tile buffers; output to O_out or the partials of key chunk `slot`).
+template <bool kCross, class K0Of>
 __device__ __forceinline__ void run_tiles(const AttnParams& p, uint16_t* smem, int T, int g, int h, int slot,
                                           bool active, int q0, const MaskSpec& ms, K0Of&& k0_of) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int rs = p.Hkv * D;   // elements between consecutive keys
   bf16x8 qf[8];
+  uint16_t* qlo = kCross ? smem + SMEM_ELEMS + (tid >> 6) * (8 * 64 * 8) : nullptr;
   WaveAcc acc;
   acc_init(acc);
-  if (active) load_q(qf, p.Q, p.N, p.Hq, h, q0, lane);
+  if (active) {
+    if constexpr (kCross) load_q_cross(qf, qlo, p, h, q0, lane);
+    else load_q(qf, p.Q, p.N, p.Hq, h, q0, lane);
+  }
 
   TileRegs r;
   const bool v_wave = __builtin_amdgcn_readfirstlane(tid >> 6) < 4;
@@ -363,10 +439,14 @@ __device__ __forceinline__ void run_tiles(const AttnParams& p, uint16_t* smem, i
       if (t + 2 < T) tile_load(r, src, k0_of(t + 2), p.N, rs);
     }
     const int cur = k0_of(t);
-    if (active && !tile_empty(ms, q0, cur)) tile_compute(smem + (t & 1) * BUF_ELEMS, qf, acc, lane, q0, cur, ms, p.c);
+    if (active && !tile_empty(ms, q0, cur))
+      tile_compute<kCross>(smem + (t & 1) * BUF_ELEMS, qf, qlo, acc, lane, q0, cur, ms, p.c);
     __syncthreads();
   }
-  if (active) store_o(acc, p.O, p.lse, slot, p.N, p.Hq, h, q0, lane, p.c);
+  if (active) {
+    if constexpr (kCross) store_cross(acc, p, slot, h, q0, lane);
+    else store_o(acc, p.O, p.lse, slot, p.N, p.Hq, h, q0, lane, p.c);
+  }
 }
 
 __global__ __launch_bounds__(NT, 1) void attn_band_kernel(AttnParams p, PackTable packs) {
@@ -401,8 +481,63 @@ __global__ __launch_bounds__(NT, 1) void attn_band_kernel(AttnParams p, PackTabl
   }
   const int T = st + (hi_t - bl + 1);
   const int slot = (packs.slots[pk] >> (8 * hs)) & 0xFF;
-  run_tiles(p, smem, T, g, h, slot, active, q0, ms,
-            [&](int idx) { return (idx < st ? idx : bl + idx - st) * BK; });
+  run_tiles<false>(p, smem, T, g, h, slot, active, q0, ms,
+                   [&](int idx) { return (idx < st ? idx : bl + idx - st) * BK; });
+}
+
+// Orthros cross-attention for many output positions (Orthros page: in
+// pre-training every position predicts, in SFT the response positions do, so
+// the cross-attention rows form a causal flash attention over all keys).
+// Workgroup = (pack, 64-row tile of the rows row0 .. N-1, key chunk kc);
+// chunks of kc_tiles key tiles spread short row ranges over the chip.
+__global__ __launch_bounds__(NT, 1) void attn_cross_mfma_kernel(AttnParams p, PackTable packs) {
+  // two tile buffers + the low query parts of the 8 waves (8 KB each)
+  __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM_ELEMS + 8 * 8 * 64 * 8];
+  const int wave = threadIdx.x >> 6;
+  const int hs = wave & 3;
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int per_pack = p.n_qt * p.n_kc;
+  const int pk = lid / per_pack;
+  const int rem = lid % per_pack;
+  const int qt = p.n_qt - 1 - rem / p.n_kc;   // long causal rows first
+  const int kc = rem % p.n_kc;
+  const uint32_t pw = packs.heads[pk];
+  const int h = (pw >> (8 * hs)) & 0xFF;
+  const int g = (int)(pw & 0xFF) / p.G;
+  const int qt0 = p.row0 + qt * BK;
+  const int q0 = qt0 + QW * (wave >> 2);
+  const bool active = h != 0xFF && q0 < p.N;
+  const int n_tiles = (min(p.N - 1, qt0 + 63) >> 6) + 1;
+  const int kt0 = kc * p.kc_tiles;
+  const int T = min(n_tiles, kt0 + p.kc_tiles) - kt0;
+  if (T <= 0) {   // chunk past the tile's last key: an empty partial
+    if (active) {
+      WaveAcc acc;
+      acc_init(acc);
+      store_cross(acc, p, kc, h, q0, threadIdx.x & 63);
+    }
+    return;
+  }
+  const MaskSpec ms = {0, INT_MAX, 0, INT_MAX};
+  run_tiles<true>(p, smem, T, g, h, kc, active, q0, ms, [&](int idx) { return (kt0 + idx) * BK; });
+}
+
+// Merge of the key-chunk partials of one (output row, head): weights
+// 2^(lse_c - max) on the normalised partials.
+__global__ __launch_bounds__(D) void cross_merge_kernel(AttnParams p) {
+  const int r = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+  float M = -__builtin_inff();
+  for (int kc = 0; kc < p.n_kc; ++kc) M = fmaxf(M, p.part_lse[((size_t)kc * p.n_out + r) * p.Hq + h]);
+  float wsum = 0.f, acc = 0.f;
+  if (M > -__builtin_inff()) {
+    for (int kc = 0; kc < p.n_kc; ++kc) {
+      const size_t pr = ((size_t)kc * p.n_out + r) * p.Hq + h;
+      const float wgt = exp2f(p.part_lse[pr] - M);
+      wsum += wgt;
+      acc = fmaf(wgt, p.part[pr * D + d], acc);
+    }
+  }
+  p.O_out[((size_t)r * p.Hq + h) * D + d] = wsum > 0.f ? acc / wsum : 0.f;
 }
 
 }  // namespace
@@ -411,6 +546,16 @@ hipError_t launch_attn_band(const AttnParams& p, const PackTable& packs, hipStre
   const int nwg = packs.n * p.n_qt;
   if (nwg == 0) return hipSuccess;
   hipLaunchKernelGGL(attn_band_kernel, dim3(nwg), dim3(NT), 0, s, p, packs);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_cross_mfma(const AttnParams& p, const PackTable& packs, hipStream_t s) {
+  const int nwg = packs.n * p.n_qt * p.n_kc;
+  if (nwg == 0) return hipSuccess;
+  hipLaunchKernelGGL(attn_cross_mfma_kernel, dim3(nwg), dim3(NT), 0, s, p, packs);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.n_kc == 1) return e;
+  hipLaunchKernelGGL(cross_merge_kernel, dim3(p.n_out, p.Hq), dim3(D), 0, s, p);
   return hipGetLastError();
 }
 

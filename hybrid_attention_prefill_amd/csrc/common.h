@@ -44,6 +44,13 @@ struct AttnParams {
   const int32_t* csr_mem;  // cluster mode: [Hkv, N]
   int M;                   // 0 = block mode
   float* lse;              // [Hret, N] log2-sum-exp of the window part (retrieval heads)
+  // Orthros cross-attention on the matrix cores (rows row0 .. N-1)
+  const float* xs;         // [Hq, D] scale s_h
+  const float* xo;         // [Hq, D] offset o_h
+  float* O_out;            // [n_out, Hq, D]
+  float* part;             // split-K partials [n_kc, n_out, Hq, D] (n_kc > 1)
+  float* part_lse;         // [n_kc, n_out, Hq] log2-sum-exp of each partial
+  int row0, n_out, n_kc, kc_tiles;   // key range split into n_kc chunks of kc_tiles 64-key tiles
 };
 
 // Retrieval heads handled by the selected-key kernel (slot t = row of sel / lse).
@@ -124,6 +131,11 @@ struct CrossParams {
 };
 constexpr int kCrossChunk = 1024;
 hipError_t launch_cross(const CrossParams& p, hipStream_t s);
+// Many output positions: flash attention of q' = q * s + o over keys 0..p on
+// the matrix cores (q' split into two bf16 parts), packs of 4 heads of one
+// KV head, key range optionally split (then merged by a second kernel).
+constexpr int kCrossMfmaMinRows = 16;   // n_out from which this path is used
+hipError_t launch_attn_cross_mfma(const AttnParams& p, const PackTable& packs, hipStream_t s);
 
 // XCD-aware remap of a linear workgroup id: workgroups are dealt round-robin
 // to the 8 XCDs; this makes consecutive logical ids land on the same XCD (and

@@ -82,13 +82,14 @@ def retrieval_key_set(rows: np.ndarray, w: int, Bk: int, f0: int, *,
 class OracleResult:
     rows: np.ndarray                       # query rows computed, ascending
     O: np.ndarray                          # [len(rows), Hq, D] fp64
-    O_out: Optional[np.ndarray]            # [n_out, Hq, D] fp64
+    O_out: Optional[np.ndarray]            # [len(out_rows), Hq, D] fp64
     sel: Dict[int, Dict[int, np.ndarray]]  # head -> query block -> selected ids
     scored: Dict[int, Dict[int, tuple]]    # head -> block -> (eligible ids, scores)
     klow: Dict[int, np.ndarray]            # KV head -> [N, r]
     qlow: Dict[int, Dict[int, np.ndarray]]  # head -> block -> [rows, r]
     centroids: Dict[int, np.ndarray]
     assign: Dict[int, np.ndarray]
+    out_rows: Optional[np.ndarray] = None  # output positions t (row N - n_out + t) held in O_out
 
 
 def orthros_cross(q: np.ndarray, s: np.ndarray, o: np.ndarray, K: np.ndarray,
@@ -108,7 +109,8 @@ def layer_prefill(w, q_rows: Callable[[int, int], np.ndarray], K: np.ndarray, V:
                   sel_override: Optional[Dict[int, Dict[int, np.ndarray]]] = None,
                   kmeans_override: Optional[Dict[int, tuple]] = None,
                   scale: Optional[float] = None,
-                  with_out: bool = True) -> OracleResult:
+                  with_out: bool = True,
+                  out_rows: Optional[Sequence[int]] = None) -> OracleResult:
     """Oracle output of one layer.
 
     w          a ``synth.Workload`` (sizes, head roles, parameters)
@@ -119,6 +121,7 @@ def layer_prefill(w, q_rows: Callable[[int, int], np.ndarray], K: np.ndarray, V:
     sel_override  head -> block -> selection to use instead of the oracle's own
                   (to grade attention given a validated GPU selection)
     kmeans_override  KV head -> (centroids, assign) to use instead of Lloyd
+    out_rows   Orthros output positions t in [0, n_out) to compute (default: all)
     """
     N, Hq, Hkv, D = w.n_tokens, w.n_q_heads, w.n_kv_heads, w.head_dim
     Bq, Bk = w.q_block, w.k_block
@@ -214,12 +217,14 @@ def layer_prefill(w, q_rows: Callable[[int, int], np.ndarray], K: np.ndarray, V:
         off += rows.size
 
     if with_out and w.n_out > 0:
-        Oo = np.zeros((w.n_out, Hq, D), dtype=np.float64)
-        for t in range(w.n_out):
+        ts = np.arange(w.n_out) if out_rows is None else np.asarray(sorted(set(int(t) for t in out_rows)))
+        Oo = np.zeros((ts.size, Hq, D), dtype=np.float64)
+        for x, t in enumerate(ts):
             p = N - w.n_out + t
             qp = q_rows(p, p + 1)[0]
             for h in heads:
                 g = head_group(h, Hq, Hkv)
-                Oo[t, h] = orthros_cross(qp[h], xa_scale[h], xa_offset[h], K[:, g], V[:, g], p, sc)
+                Oo[x, h] = orthros_cross(qp[h], xa_scale[h], xa_offset[h], K[:, g], V[:, g], p, sc)
         res.O_out = Oo
+        res.out_rows = ts
     return res

@@ -108,6 +108,11 @@ ORTHROS_8B_128K = Workload(
     name="orthros_8b_128k", n_tokens=131072, n_q_heads=32, n_kv_heads=8,
     head_kind=(HEAD_SWA,) * 32, window=4096, n_out=1)
 
+# Orthros with many output positions (SFT: the response tokens predict): the
+# same layer with its last 8192 rows as output positions.  The response
+# length is this suite's choice; the pages give none.
+ORTHROS_8B_128K_SFT = ORTHROS_8B_128K.with_(name="orthros_8b_128k_sft8k", n_out=8192)
+
 # 1M-token all-sparse layer: every head is a retrieval head, the low-rank keys
 # are clustered (16384 centroids, 10 Lloyd iterations, seeds every 64th key),
 # each query block takes its top-64 clusters plus a 4096 window.
@@ -126,7 +131,7 @@ TRIANGLE_LAYER_SPLIT = (12, 20)
 
 WORKLOADS = {w.name: w for w in (
     TINY_HYBRID_2K, QWEN3_30B_32K, TRIANGLE_8B_128K, DENSE_8B_128K,
-    ORTHROS_8B_128K, ALLSPARSE_1M, ALLSPARSE_1M_GQA)}
+    ORTHROS_8B_128K, ORTHROS_8B_128K_SFT, ALLSPARSE_1M, ALLSPARSE_1M_GQA)}
 
 
 def shrink(w: Workload, n_tokens: int, *, n_clusters: Optional[int] = None,

@@ -23,7 +23,7 @@ def _sample_blocks(w, extra=()):
     return sorted(set(b for b in edge + strata + list(extra) if 0 <= b < n))
 
 
-def _run(name, heads=None, blocks=None, **changes):
+def _run(name, heads=None, blocks=None, out_rows=None, **changes):
     w = synth.WORKLOADS[name].with_(**changes)
     print(f"\n[case] full-size {name} {changes}", flush=True)
     li = synth.make_layer_inputs(w)
@@ -37,7 +37,7 @@ def _run(name, heads=None, blocks=None, **changes):
     def q_rows(a, b):
         return si.bf16_to_f64(li.Q[a:b])
 
-    ref = layer_prefill(w, q_rows, K, V, P, xs, xo, blocks=blocks, heads=heads)
+    ref = layer_prefill(w, q_rows, K, V, P, xs, xo, blocks=blocks, heads=heads, out_rows=out_rows)
     if w.ret_heads:
         sel = aux["sel"].cpu().numpy()
         _gpu.check_group_rows(sel, w)
@@ -51,13 +51,16 @@ def _run(name, heads=None, blocks=None, **changes):
                 n_diff += _gpu.check_selection(sel[t, b], E, s, w.topk, f"head {h} block {b}")
                 override[h][b] = np.array([x for x in sel[t, b] if x >= 0], dtype=np.int64)
         print(f"selection differences inside the tie band: {n_diff}")
-        ref = layer_prefill(w, q_rows, K, V, P, xs, xo, blocks=blocks, heads=heads, sel_override=override)
+        ref = layer_prefill(w, q_rows, K, V, P, xs, xo, blocks=blocks, heads=heads, sel_override=override,
+                            out_rows=out_rows)
     Og = O.cpu().numpy()[ref.rows]
     hs = list(range(w.n_q_heads)) if heads is None else list(heads)
     mx, mean = _gpu.assert_close_out(Og[:, hs], ref.O[:, hs], name)
     print(f"{name}: {len(blocks)} blocks x {len(hs)} heads, max abs {mx:.3e}, mean abs {mean:.3e}")
     if w.n_out:
-        _gpu.assert_close_out(O_out.cpu().numpy()[:, hs], ref.O_out[:, hs], name + " cross")
+        Og_out = O_out.cpu().numpy()[ref.out_rows]
+        mx, mean = _gpu.assert_close_out(Og_out[:, hs], ref.O_out[:, hs], name + " cross")
+        print(f"{name} cross: {len(ref.out_rows)} output rows, max abs {mx:.3e}, mean abs {mean:.3e}")
 
 
 def test_qwen3_30b_layer_32k():
@@ -82,6 +85,15 @@ def test_dense_layer_128k():
 
 def test_orthros_layer_128k():
     _run("orthros_8b_128k", heads=list(range(0, 32, 5)))
+
+
+def test_orthros_sft_layer_128k():
+    """8192 output positions at 128K (the matrix-core cross-attention path):
+    12 sampled output rows (first, last, and one per tenth), 7 heads."""
+    w = synth.WORKLOADS["orthros_8b_128k_sft8k"]
+    rng = np.random.default_rng(8)
+    rows = [0, w.n_out - 1] + [int(rng.integers(s * w.n_out // 10, (s + 1) * w.n_out // 10)) for s in range(10)]
+    _run("orthros_8b_128k_sft8k", heads=list(range(0, 32, 5)), blocks=[0, w.n_qb - 1], out_rows=rows)
 
 
 def test_allsparse_layer_1m():

@@ -108,10 +108,20 @@ def test_planted_component_layer_reduced():
     _compare(w)
 
 
-@pytest.mark.parametrize("N,n_out", [(1, 1), (3000, 1), (2500, 3)])
+@pytest.mark.parametrize("N,n_out", [(1, 1), (3000, 1), (2500, 3), (2500, 15),
+                                     # matrix-core path: split key range, one tile, ragged rows
+                                     (2500, 16), (130, 100), (3000, 700),
+                                     # every position an output position (pre-training)
+                                     (1000, 1000), (64, 64)])
 def test_orthros_cross(N, n_out):
     w = _layer([HEAD_SWA] * 8, N, window=256, n_out=n_out)
     _compare(w)
+
+
+def test_orthros_cross_many_rows_wide_groups():
+    # G = 20 (five packs of four heads per KV head), a partial last pack (G = 6)
+    _compare(_layer([HEAD_SWA] * 20, 900, Hkv=1, window=100, n_out=200))
+    _compare(_layer([HEAD_SWA] * 12, 900, Hkv=2, window=100, n_out=77))
 
 
 def test_deterministic_rerun():

@@ -102,6 +102,28 @@ def test_orthros_identity_affine_is_dense_last_row():
     assert np.max(np.abs(r2.O_out[0] - d.O[-1])) > 1e-3
 
 
+def test_orthros_every_position_identity_affine_is_dense():
+    # pre-training: every position is an output position; with s = 1, o = 0
+    # each cross-attention row is the dense causal row
+    w = _w(HEAD_SWA, N=200, window=16, n_out=200)
+    q, K, V, P, xs, xo = oracle_arrays(w)
+    r = layer_prefill(w, q, K, V, None, np.ones_like(xs), np.zeros_like(xo))
+    d = _run(w.with_(head_kind=(HEAD_DENSE,) * 4, n_out=0))
+    np.testing.assert_allclose(r.O_out, d.O, atol=1e-12)
+    # output position t is row N - n_out + t: a suffix of the rows
+    w2 = w.with_(n_out=37)
+    r2 = layer_prefill(w2, q, K, V, None, np.ones_like(xs), np.zeros_like(xo))
+    np.testing.assert_allclose(r2.O_out, d.O[-37:], atol=1e-12)
+
+
+def test_orthros_out_rows_subset_equals_full():
+    w = _w(HEAD_SWA, N=150, window=16, n_out=40)
+    full = _run(w)
+    part = _run(w, out_rows=[0, 17, 39])
+    assert list(part.out_rows) == [0, 17, 39]
+    np.testing.assert_allclose(part.O_out, full.O_out[[0, 17, 39]], atol=0)
+
+
 def test_blocks_subset_equals_full_rows():
     w = _w(HEAD_RETRIEVAL, window=40, topk=2, q_block=32, k_block=32)
     full = _run(w)
