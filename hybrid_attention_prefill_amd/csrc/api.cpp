@@ -32,9 +32,6 @@ int check_desc(const ha_layer_desc* d, const int32_t* kinds, Heads* out) {
   if (d->head_dim != kHeadDim) return HA_ERR_UNSUPPORTED;
   if (d->q_block != kBlock || d->k_block != kBlock) return HA_ERR_UNSUPPORTED;
   if (d->n_out < 0 || d->n_out > d->n_tokens) return HA_ERR_ARG;
-  // the memory-bound path for a few output rows keeps a KV head's queries in LDS
-  if (d->n_out > 0 && d->n_out < kCrossMfmaMinRows && d->n_q_heads / d->n_kv_heads > 16)
-    return HA_ERR_UNSUPPORTED;
   if (!kinds) return HA_ERR_ARG;
   if (d->group_select != 0 && d->group_select != 1) return HA_ERR_ARG;
   Heads h;
@@ -75,11 +72,10 @@ int check_desc(const ha_layer_desc* d, const int32_t* kinds, Heads* out) {
 }
 
 inline int n_qb_of(const ha_layer_desc* d) { return (d->n_tokens + kBlock - 1) / kBlock; }
-inline int n_cross_chunks(const ha_layer_desc* d) { return (d->n_tokens + kCrossChunk - 1) / kCrossChunk; }
 
-// Orthros cross-attention with n_out >= kCrossMfmaMinRows runs on the matrix
-// cores: workgroups = packs x row tiles x key chunks.  Few row tiles split
-// the key range so that about 1024 workgroups run; chunks hold >= 8 tiles.
+// Orthros cross-attention runs on the matrix cores: workgroups = packs x row
+// tiles x key chunks.  Few row tiles split the key range so that about 1024
+// workgroups run; chunks hold >= 8 tiles.
 struct CrossPlan {
   int n_packs, n_qt, n_kc, kc_tiles;
 };
@@ -98,12 +94,10 @@ CrossPlan cross_plan(const ha_layer_desc* d) {
   return c;
 }
 
-// Workspace of the cross-attention stage (partials of either path).
+// Workspace of the cross-attention stage (split-key partials).
 size_t cross_ws_bytes(const ha_layer_desc* d) {
   if (d->n_out <= 0) return 0;
   const size_t n_out = (size_t)d->n_out, Hq = (size_t)d->n_q_heads;
-  if (d->n_out < kCrossMfmaMinRows)
-    return align_up(n_out * Hq * (size_t)n_cross_chunks(d) * (kHeadDim + 2) * sizeof(float));
   const CrossPlan c = cross_plan(d);
   if (c.n_kc == 1) return 0;
   return align_up((size_t)c.n_kc * n_out * Hq * kHeadDim * sizeof(float)) +
@@ -364,43 +358,25 @@ int run_select_clusters(const ha_layer_desc* d, const Heads& h, const float* qlo
 int run_cross(const ha_layer_desc* d, const void* Q, const void* K, const void* V, const float* xs,
               const float* xo, float* O_out, float* part, hipStream_t s) {
   if (d->n_out == 0) return HA_OK;
-  if (d->n_out >= kCrossMfmaMinRows) {
-    AttnParams p = attn_params(d, Q, K, V, nullptr);
-    const CrossPlan c = cross_plan(d);
-    p.kind = DENSE;
-    p.xs = xs;
-    p.xo = xo;
-    p.O_out = O_out;
-    p.row0 = d->n_tokens - d->n_out;
-    p.n_out = d->n_out;
-    p.n_qt = c.n_qt;
-    p.n_kc = c.n_kc;
-    p.kc_tiles = c.kc_tiles;
-    if (c.n_kc > 1) {
-      p.part = part;
-      p.part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(part) +
-                                            align_up((size_t)c.n_kc * d->n_out * d->n_q_heads * kHeadDim * sizeof(float)));
-    }
-    PackTable pt;
-    build_packs(d, nullptr, -1, {}, &pt);
-    return dev_status(launch_attn_cross_mfma(p, pt, s));
+  AttnParams p = attn_params(d, Q, K, V, nullptr);
+  const CrossPlan c = cross_plan(d);
+  p.kind = DENSE;
+  p.xs = xs;
+  p.xo = xo;
+  p.O_out = O_out;
+  p.row0 = d->n_tokens - d->n_out;
+  p.n_out = d->n_out;
+  p.n_qt = c.n_qt;
+  p.n_kc = c.n_kc;
+  p.kc_tiles = c.kc_tiles;
+  if (c.n_kc > 1) {
+    p.part = part;
+    p.part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(part) +
+                                          align_up((size_t)c.n_kc * d->n_out * d->n_q_heads * kHeadDim * sizeof(float)));
   }
-  CrossParams cp{};
-  cp.Q = static_cast<const uint16_t*>(Q);
-  cp.K = static_cast<const uint16_t*>(K);
-  cp.V = static_cast<const uint16_t*>(V);
-  cp.xs = xs;
-  cp.xo = xo;
-  cp.O_out = O_out;
-  cp.part = part;
-  cp.N = d->n_tokens;
-  cp.Hq = d->n_q_heads;
-  cp.Hkv = d->n_kv_heads;
-  cp.G = d->n_q_heads / d->n_kv_heads;
-  cp.n_out = d->n_out;
-  cp.n_chunks = n_cross_chunks(d);
-  cp.c = scale_c(d);
-  return dev_status(launch_cross(cp, s));
+  PackTable pt;
+  build_packs(d, nullptr, -1, {}, &pt);
+  return dev_status(launch_attn_cross(p, pt, s));
 }
 
 inline char* ws_at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
@@ -570,7 +546,6 @@ int ha_attn_cross(const ha_layer_desc* desc, const void* Q, const void* K, const
     return HA_ERR_ARG;
   if (desc->head_dim != kHeadDim) return desc->head_dim < 1 ? HA_ERR_ARG : HA_ERR_UNSUPPORTED;
   if (desc->n_q_heads > kMaxHeads) return HA_ERR_UNSUPPORTED;
-  if (desc->n_out < kCrossMfmaMinRows && desc->n_q_heads / desc->n_kv_heads > 16) return HA_ERR_UNSUPPORTED;
   if (!Q || !K || !V || !xa_scale || !xa_offset || !O_out) return HA_ERR_ARG;
   if (!ws_ok(workspace, ws_bytes, cross_ws_bytes(desc))) return HA_ERR_WORKSPACE;
   return run_cross(desc, Q, K, V, xa_scale, xa_offset, O_out, static_cast<float*>(workspace),

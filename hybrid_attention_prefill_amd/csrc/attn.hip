@@ -549,7 +549,7 @@ hipError_t launch_attn_band(const AttnParams& p, const PackTable& packs, hipStre
   return hipGetLastError();
 }
 
-hipError_t launch_attn_cross_mfma(const AttnParams& p, const PackTable& packs, hipStream_t s) {
+hipError_t launch_attn_cross(const AttnParams& p, const PackTable& packs, hipStream_t s) {
   const int nwg = packs.n * p.n_qt * p.n_kc;
   if (nwg == 0) return hipSuccess;
   hipLaunchKernelGGL(attn_cross_mfma_kernel, dim3(nwg), dim3(NT), 0, s, p, packs);

@@ -118,24 +118,10 @@ hipError_t launch_kmeans(KmeansParams p, int Hkv, int iters, hipStream_t s);
 hipError_t launch_select_clusters(const SelectParams& p, int Hkv, hipStream_t s);
 size_t select_clusters_scratch_bytes(int M, int Hkv);
 
-struct CrossParams {
-  const uint16_t* Q;
-  const uint16_t* K;
-  const uint16_t* V;
-  const float* xs;     // [Hq, D]
-  const float* xo;     // [Hq, D]
-  float* O_out;        // [n_out, Hq, D]
-  float* part;         // workspace partials [n_out, Hq, n_chunks, D + 2]
-  int N, Hq, Hkv, G, n_out, n_chunks;
-  float c;             // scale * log2(e)
-};
-constexpr int kCrossChunk = 1024;
-hipError_t launch_cross(const CrossParams& p, hipStream_t s);
-// Many output positions: flash attention of q' = q * s + o over keys 0..p on
-// the matrix cores (q' split into two bf16 parts), packs of 4 heads of one
-// KV head, key range optionally split (then merged by a second kernel).
-constexpr int kCrossMfmaMinRows = 16;   // n_out from which this path is used
-hipError_t launch_attn_cross_mfma(const AttnParams& p, const PackTable& packs, hipStream_t s);
+// Orthros cross-attention rows: flash attention of q' = q * s + o over keys
+// 0..p on the matrix cores (q' split into two bf16 parts), packs of 4 heads
+// of one KV head, key range optionally split (then merged by a second kernel).
+hipError_t launch_attn_cross(const AttnParams& p, const PackTable& packs, hipStream_t s);
 
 // XCD-aware remap of a linear workgroup id: workgroups are dealt round-robin
 // to the 8 XCDs; this makes consecutive logical ids land on the same XCD (and

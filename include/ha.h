@@ -190,9 +190,8 @@ int ha_attn_gather(const ha_layer_desc* desc, const int32_t* head_kind,
  *   q' = q_p * xa_scale[h] + xa_offset[h] (fp32), attention over keys 0..p.
  * Orthros page, "Training, SFT and inference share one mechanism": the
  * number of output positions is 1 when prefilling, the response length in
- * SFT and N in pre-training.  n_out < 16: a memory-bound pass per output row
- * (G = Hq / Hkv <= 16); n_out >= 16: flash attention on the matrix cores with
- * q' held as two bf16 parts (hi + lo, ~2^-16 relative).
+ * SFT and N in pre-training.  Flash attention on the matrix cores with q'
+ * held as two bf16 parts (hi + lo, ~2^-16 relative).
  *   workspace  >= ha_workspace_bytes(desc, head_kind) bytes, 256-byte aligned
  *              (split-key partials; none when the rows fill the chip) */
 int ha_attn_cross(const ha_layer_desc* desc, const void* Q, const void* K, const void* V,

@@ -122,8 +122,11 @@ def test_prefill_orthros_argument_checks():
     assert _prefill(d, kinds, xs=FAKE, xo=None, Oo=FAKE) == ha.HA_ERR_ARG
     assert _prefill(d, kinds, xs=FAKE, xo=FAKE, Oo=None) == ha.HA_ERR_ARG
     assert _prefill(_desc(n_out=2000), kinds, xs=FAKE, xo=FAKE, Oo=FAKE) == ha.HA_ERR_ARG
-    d16 = _desc(n_q_heads=34, n_kv_heads=2, n_out=1)
-    assert _prefill(d16, [0] * 34, xs=FAKE, xo=FAKE, Oo=FAKE) == ha.HA_ERR_UNSUPPORTED
+    # any group size (G = 17 here) passes the checks; the split-key partials
+    # then need a workspace
+    d17 = _desc(n_q_heads=34, n_kv_heads=2, n_out=1)
+    assert ha.lib().ha_workspace_bytes(ctypes.byref(d17), ha._kinds([0] * 34)) > 0
+    assert _prefill(d17, [0] * 34, xs=FAKE, xo=FAKE, Oo=FAKE) == ha.HA_ERR_WORKSPACE
 
 
 def test_stage_argument_checks():
