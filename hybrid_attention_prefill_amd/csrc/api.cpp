@@ -105,8 +105,13 @@ size_t cross_ws_bytes(const ha_layer_desc* d) {
 }
 
 struct Layout {
-  size_t qlow, klow, sel, lse, cent, assign, csr_off, csr_mem, km_scratch, cross, total;
+  size_t qlow, klow, sel, lse, cent, assign, csr_off, csr_mem, km_scratch, kvc, cross, total;
 };
+
+// Cluster mode: K and V copied into CSR order for the selected-key kernels.
+size_t kvc_bytes(const ha_layer_desc* d) {
+  return d->n_clusters > 0 ? align_up(2 * (size_t)d->n_kv_heads * d->n_tokens * kHeadDim * sizeof(uint16_t)) : 0;
+}
 
 Layout layout_of(const ha_layer_desc* d, const Heads& h) {
   Layout L{};
@@ -133,6 +138,8 @@ Layout layout_of(const ha_layer_desc* d, const Heads& h) {
   off += M ? align_up(std::max(kmeans_scratch_bytes(d->n_tokens, (int)M, d->n_kv_heads),
                                select_clusters_scratch_bytes((int)M, d->n_kv_heads)))
            : 0;
+  L.kvc = off;
+  off += Hret ? kvc_bytes(d) : 0;
   L.cross = off;
   off += cross_ws_bytes(d);
   L.total = off;
@@ -285,7 +292,7 @@ int run_select_blocks(const ha_layer_desc* d, const Heads& h, const float* qlow,
 // leaves each row's log2-sum-exp), then the selected keys, merged in.
 int run_gather(const ha_layer_desc* d, const int32_t* kinds, const Heads& h, const void* Q, const void* K,
                const void* V, const int32_t* sel, const int32_t* csr_off, const int32_t* csr_mem, float* O,
-               float* lse, hipStream_t s) {
+               float* lse, void* kvc, hipStream_t s) {
   if (h.ret.empty()) return HA_OK;
   AttnParams p = attn_params(d, Q, K, V, O);
   p.kind = SWA;
@@ -300,6 +307,10 @@ int run_gather(const ha_layer_desc* d, const int32_t* kinds, const Heads& h, con
     p.csr_off = csr_off;
     p.csr_mem = csr_mem;
     p.M = d->n_clusters;
+    p.Kc = static_cast<uint16_t*>(kvc);
+    p.Vc = p.Kc + (size_t)d->n_kv_heads * d->n_tokens * kHeadDim;
+    st = dev_status(launch_permute_kv(p, s));
+    if (st != HA_OK) return st;
   }
   if (d->group_select) return dev_status(launch_attn_selected_group(p, pt, s));
   SelList sl;
@@ -450,7 +461,7 @@ int ha_prefill(const ha_layer_desc* desc, const int32_t* head_kind, const void* 
       if (st != HA_OK) return st;
     }
     st = run_gather(desc, head_kind, h, Q, K, V, sel, off, mem, O, reinterpret_cast<float*>(ws_at(workspace, L.lse)),
-                    s);
+                    ws_at(workspace, L.kvc), s);
     if (st != HA_OK) return st;
   }
   if (h.any_band) {
@@ -532,10 +543,10 @@ int ha_attn_gather(const ha_layer_desc* desc, const int32_t* head_kind, const vo
   if (h.ret.empty()) return HA_ERR_ARG;
   if (!Q || !K || !V || !O || (desc->topk > 0 && !sel)) return HA_ERR_ARG;
   if (desc->n_clusters > 0 && (!csr_off || !csr_mem)) return HA_ERR_ARG;
-  const size_t need = align_up(h.ret.size() * (size_t)desc->n_tokens * sizeof(float));
-  if (!ws_ok(workspace, ws_bytes, need)) return HA_ERR_WORKSPACE;
+  const size_t lse_bytes = align_up(h.ret.size() * (size_t)desc->n_tokens * sizeof(float));
+  if (!ws_ok(workspace, ws_bytes, lse_bytes + kvc_bytes(desc))) return HA_ERR_WORKSPACE;
   return run_gather(desc, head_kind, h, Q, K, V, sel, csr_off, csr_mem, O, static_cast<float*>(workspace),
-                    static_cast<hipStream_t>(stream));
+                    ws_at(workspace, lse_bytes), static_cast<hipStream_t>(stream));
 }
 
 int ha_attn_cross(const ha_layer_desc* desc, const void* Q, const void* K, const void* V, const float* xa_scale,

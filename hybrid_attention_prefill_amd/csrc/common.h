@@ -43,6 +43,8 @@ struct AttnParams {
   const int32_t* csr_off;  // cluster mode: [Hkv, M+1]
   const int32_t* csr_mem;  // cluster mode: [Hkv, N]
   int M;                   // 0 = block mode
+  uint16_t* Kc;            // cluster mode: K and V rows in CSR order, [Hkv, N, D]
+  uint16_t* Vc;            //   (row e of KV head g = key csr_mem[g][e])
   float* lse;              // [Hret, N] log2-sum-exp of the window part (retrieval heads)
   // Orthros cross-attention on the matrix cores (rows row0 .. N-1)
   const float* xs;         // [Hq, D] scale s_h
@@ -66,6 +68,9 @@ hipError_t launch_attn_selected(const AttnParams& p, const SelList& sl, hipStrea
 // selection row, so one workgroup serves a pack of up to 4 of them (the pack's
 // first slot names the row).
 hipError_t launch_attn_selected_group(const AttnParams& p, const PackTable& packs, hipStream_t s);
+// Cluster mode: copies K and V rows into CSR order (Kc, Vc) so that the
+// visible members of a cluster are one contiguous range of rows.
+hipError_t launch_permute_kv(const AttnParams& p, hipStream_t s);
 
 struct ProjParams {
   const uint16_t* X;   // bf16 [N, H, D]

@@ -10,16 +10,25 @@
 // selected part for one (retrieval head, 64-row query block) and merges:
 //   O = (O_win 2^lse_win + O_sel 2^lse_sel) / (2^lse_win + 2^lse_sel).
 //
-// The selected part reads scattered K/V rows.  A workgroup takes one (head,
-// 64-row query block); each 64-key gathered tile is staged in LDS (K rows,
-// V transposed) and split between the waves: wave w owns query rows
+// The selected part reads K/V rows by position.  In cluster mode the members
+// of a cluster lie anywhere in the sequence; a copy of K and V in CSR order
+// (made once per layer after k-means, one pass over K/V) turns the visible
+// members of a selected cluster (a prefix of its ascending member list) into
+// one contiguous range of rows, so tiles are read as runs of rows rather
+// than as 64 rows from 64 places.  Each tile slot carries two numbers: the
+// row it loads (CSR index or key position; looked up from LDS, no memory
+// read) and the key position that the causal / window mask tests (read from
+// the CSR together with the tile's K/V rows and staged in LDS with them).
+//
+// A workgroup takes one (head, 64-row query block); each 64-key gathered
+// tile is staged in LDS (K rows, V transposed) and split between the waves:
+// wave w owns query rows
 // 32 (w % 2) .. +31 and key half w / 2 (keys 32 (w / 2) .. +31 of every
 // tile), so a wave reads half a tile per step.  S^T = K Q^T and O^T += V^T P^T
 // on v_mfma_f32_32x32x16_bf16 (a lane owns one query column), fp32 online
 // softmax per key half; the two halves' (max, sum, O) are merged through LDS
-// at the end.  Key rows of tile t+2 are looked up (CSR members or block keys)
-// while tile t is computed and tile t+1 is in flight; two workgroups fit on
-// a CU.
+// at the end.  Rows of tile t+2 are looked up while tile t is computed and
+// tile t+1 is in flight; two workgroups fit on a CU.
 #include "common.h"
 #include "device_util.h"
 
@@ -59,31 +68,48 @@ __device__ __forceinline__ int vt_pos(int u) { return 8 * ((u >> 2) & 1) + 4 * (
 struct TileRegs {
   u32x4 k[4];
   u32x4 v[4];
+  int row, pos;   // row of slot `lane` and the word read for its key position
 };
 
+// Key position of a tile slot: the CSR member at that index in cluster mode,
+// else the row itself; -1 for an empty slot.  Every wave issues the read
+// (block mode reads a word of `any`, a valid address, and ignores it): no
+// branch around it, and it is not used until the tile is staged (pos_of),
+// so it stays in flight with the tile's rows.
+__device__ __forceinline__ void slot_position(const int32_t* __restrict__ mem, const int32_t* __restrict__ any,
+                                              int row, int& r_row, int& r_pos) {
+  r_row = row;
+  r_pos = mem ? mem[max(row, 0)] : *any;
+}
+__device__ __forceinline__ int pos_of(int row, int pos, bool clus) { return row < 0 ? -1 : (clus ? pos : row); }
+
 // K slots c*16 + tid/16 (16-B chunk tid%16); V slots 4*(tid%16) + x (d chunk
-// tid/16).  Empty slots (key -1) read key row 0: the mask drops them (P = 0)
-// and the finite stand-in values leave the products exact; no per-lane
+// tid/16).  Kb / Vb point at the KV head's first row, rs = elements between
+// rows.  Empty slots (row -1) read row 0: the mask drops them (P = 0) and
+// the finite stand-in values leave the products exact; no per-lane
 // branches, so the loads stay in flight until the LDS store.
-__device__ __forceinline__ void tile_load(TileRegs& r, const uint16_t* __restrict__ K,
-                                          const uint16_t* __restrict__ V, const int* ring, size_t rs, int g,
-                                          int tid) {
+__device__ __forceinline__ void tile_load(TileRegs& r, const uint16_t* __restrict__ Kb,
+                                          const uint16_t* __restrict__ Vb, const int* kidx, size_t rs, int tid,
+                                          const int32_t* __restrict__ mem) {
+  slot_position(mem, reinterpret_cast<const int32_t*>(Kb), kidx[tid & 63], r.row, r.pos);
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const int key = max(0, ring[c * 16 + (tid >> 4)]);
-    r.k[c] = *reinterpret_cast<const u32x4*>(K + (size_t)key * rs + g * D + (tid & 15) * 8);
+    const int row = max(0, kidx[c * 16 + (tid >> 4)]);
+    r.k[c] = *reinterpret_cast<const u32x4*>(Kb + (size_t)row * rs + (tid & 15) * 8);
   }
   const int dc = tid >> 4;
 #pragma unroll
   for (int x = 0; x < 4; ++x) {
-    const int key = max(0, ring[(tid & 15) * 4 + x]);
-    r.v[x] = *reinterpret_cast<const u32x4*>(V + (size_t)key * rs + g * D + dc * 8);
+    const int row = max(0, kidx[(tid & 15) * 4 + x]);
+    r.v[x] = *reinterpret_cast<const u32x4*>(Vb + (size_t)row * rs + dc * 8);
   }
 }
 
-__device__ __forceinline__ void tile_store(const TileRegs& r, uint16_t* buf, int tid) {
+__device__ __forceinline__ void tile_store(const TileRegs& r, uint16_t* buf, int* kposb, int tid, bool pos_wave,
+                                           bool clus) {
   uint16_t* Ks = buf;
   uint16_t* Vt = buf + K_ELEMS;
+  if (pos_wave) kposb[tid & 63] = pos_of(r.row, r.pos, clus);
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int id = c * NT + tid;
@@ -103,6 +129,76 @@ __device__ __forceinline__ void tile_store(const TileRegs& r, uint16_t* buf, int
     *reinterpret_cast<u32x2*>(Vt + (dc * 8 + 2 * w) * VSTR + pos) = ev;
     *reinterpret_cast<u32x2*>(Vt + (dc * 8 + 2 * w + 1) * VSTR + pos) = od;
   }
+}
+
+// Entries of one query block: key block 0 when forced, then the selected
+// blocks / clusters (sel = the block's selection row).  For entry e:
+// ent[e] = its first row (block id, or CSR start of the cluster) and
+// cntv[e] = its keys at positions <= lim (a prefix of the block, or a prefix
+// of the cluster's ascending member list).  Cluster counts: wave w takes
+// entries w, w + NW, ... and counts members <= lim 64 at a time with a
+// ballot; the first 64 members of 8 entries are read at once (independent
+// loads, clamped into the member range), longer prefixes go on 64 at a
+// time.  Every thread takes part; the results are visible on return.
+template <int NW>
+__device__ __forceinline__ void entry_table(const AttnParams& p, const int32_t* __restrict__ sel, int g, int lim,
+                                            int ne, int* ent, int* ehi, int* cntv) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int f0 = p.force_block0 ? 1 : 0;
+  const int n_kb = (p.N + BK - 1) / BK;
+  const bool clus = p.M > 0;
+  if (tid < ne) {
+    int start = 0, cnt = 0, hi = 0;
+    if (lim >= 0) {
+      if (f0 && tid == 0) {
+        cnt = min(BK, lim + 1);
+      } else {
+        const int v = sel[tid - f0];
+        if (clus) {
+          if (v >= 0 && v < p.M) {
+            const int32_t* off = p.csr_off + (size_t)g * (p.M + 1);
+            start = off[v];
+            hi = off[v + 1];
+          }
+        } else if (v >= 0 && v < n_kb && !(f0 && v == 0)) {
+          start = v;
+          cnt = max(0, min(BK, lim - v * BK + 1));
+        }
+      }
+    }
+    ent[tid] = start;
+    ehi[tid] = hi;
+    cntv[tid] = cnt;
+  }
+  __syncthreads();
+  if (!clus || lim < 0) return;
+  const int32_t* mem = p.csr_mem + (size_t)g * p.N;
+  for (int e0 = wave; e0 < ne; e0 += 8 * NW) {
+    int lo[8], hi[8], m[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = e0 + u * NW;
+      lo[u] = e < ne ? ent[e] : 0;
+      hi[u] = e < ne ? ehi[e] : 0;
+      m[u] = mem[min(lo[u] + lane, max(hi[u] - 1, 0))];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = e0 + u * NW;
+      int c = (int)__popcll(__ballot(lo[u] + lane < hi[u] && m[u] <= lim));
+      if (c == 64) {   // a full round: the prefix may go on
+        for (int x0 = lo[u] + 64; x0 < hi[u]; x0 += 64) {
+          const int x = x0 + lane;
+          const int cc = (int)__popcll(__ballot(x < hi[u] && mem[min(x, hi[u] - 1)] <= lim));
+          c += cc;
+          if (cc < 64) break;
+        }
+      }
+      if (e < ne && lane == 0) cntv[e] = c;
+    }
+  }
+  __syncthreads();
 }
 
 struct Acc {
@@ -176,8 +272,10 @@ __device__ __forceinline__ void tile_compute(const uint16_t* __restrict__ buf, c
 
 __global__ __launch_bounds__(NT, 2) void attn_selected_kernel(AttnParams p, SelList sl) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * BUF_ELEMS];
-  __shared__ __attribute__((aligned(16))) int ring[3][BK];
+  __shared__ __attribute__((aligned(16))) int kidx[3][BK];    // row each slot loads
+  __shared__ __attribute__((aligned(16))) int kposb[2][BK];   // key positions of the staged tiles
   __shared__ int ent[kMaxTopk + 1];     // block id (block mode) or CSR start (cluster mode)
+  __shared__ int ehi[kMaxTopk + 1];     // cluster mode: end of the member range
   __shared__ int pre[kMaxTopk + 2];     // prefix of visible key counts per entry
   __shared__ int tmp4[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -187,53 +285,25 @@ __global__ __launch_bounds__(NT, 2) void attn_selected_kernel(AttnParams p, SelL
   const int g = h / p.G;
   const int q0 = b * BK;
   const int lim = min(p.N, q0 + BK) - 1 - p.window;   // keys j <= lim can be visible
-  const int n_kb = (p.N + BK - 1) / BK;
   const int32_t* mem = p.csr_mem ? p.csr_mem + (size_t)g * p.N : nullptr;
 
   // entries: forced block 0 + the selection; count of keys j <= lim in each
   const int ne = p.topk + (p.force_block0 ? 1 : 0);
-  int cnt = 0, start = 0;
-  if (tid < ne && lim >= 0) {
-    if (p.force_block0 && tid == 0) {
-      start = 0;
-      cnt = min(BK, lim + 1);
-    } else {
-      const int e = tid - (p.force_block0 ? 1 : 0);
-      const int v = p.sel[((size_t)t * p.n_qt + b) * p.topk + e];
-      if (p.M > 0) {
-        if (v >= 0 && v < p.M) {
-          const int32_t* off = p.csr_off + (size_t)g * (p.M + 1);
-          const int lo = off[v];
-          int a = lo, bb = off[v + 1];
-          while (a < bb) {
-            const int mid = (a + bb) >> 1;
-            if (mem[mid] <= lim) a = mid + 1;
-            else bb = mid;
-          }
-          start = lo;
-          cnt = a - lo;
-        }
-      } else if (v >= 0 && v < n_kb && !(p.force_block0 && v == 0)) {
-        start = v;
-        cnt = max(0, min(BK, lim - v * BK + 1));
-      }
-    }
-  }
+  entry_table<4>(p, p.sel + ((size_t)t * p.n_qt + b) * p.topk, g, lim, ne, ent, ehi, pre);
+  const int cnt = tid < ne ? pre[tid] : 0;
   int total;
-  const int excl = dev::block_excl_scan(cnt, tmp4, &total);
-  if (tid < ne) {
-    ent[tid] = start;
-    pre[tid] = excl;
-  }
+  const int excl = dev::block_excl_scan<4>(cnt, tmp4, &total);
+  if (tid < ne) pre[tid] = excl;
   if (tid == 0) pre[ne] = total;
   __syncthreads();
   const int T = (total + BK - 1) / BK;
   if (T == 0) return;
 
-  // key row of slot s of tile idx (flat index f = 64 idx + s over the
-  // entries).  Slot s of every tile is looked up by thread 4 s, so all waves
-  // share the work; that thread's entry index (the largest e with
-  // pre[e] <= f) only moves forward from tile to tile.
+  // row of slot s of tile idx (flat index f = 64 idx + s over the entries):
+  // the key position (block mode) or the CSR index (cluster mode).  Slot s
+  // of every tile is looked up by thread 4 s, so all waves share the work;
+  // that thread's entry index (the largest e with pre[e] <= f) only moves
+  // forward from tile to tile.
   const bool owner = (tid & 3) == 0;
   const int slot = tid >> 2;
   int cur_e = 0;
@@ -242,10 +312,8 @@ __global__ __launch_bounds__(NT, 2) void attn_selected_kernel(AttnParams p, SelL
     if (f >= total) return -1;
     while (cur_e + 1 < ne && pre[cur_e + 1] <= f) ++cur_e;
     const int r = f - pre[cur_e];
-    if (p.M > 0) return (int)mem[ent[cur_e] + r];
-    return ent[cur_e] * BK + r;
+    return p.M > 0 ? ent[cur_e] + r : ent[cur_e] * BK + r;
   };
-
   const int lr = lane & 31, lh = lane >> 5;
   const int kh = wave >> 1;                   // key half of every tile
   const int i = q0 + (wave & 1) * 32 + lr;    // this lane's query row
@@ -267,24 +335,28 @@ __global__ __launch_bounds__(NT, 2) void attn_selected_kernel(AttnParams p, SelL
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc.o[db][e] = 0.f;
 
-  const size_t rs = (size_t)p.Hkv * D;
+  const bool clus = p.M > 0;
+  const size_t rs = clus ? (size_t)D : (size_t)p.Hkv * D;
+  const uint16_t* Kb = clus ? p.Kc + (size_t)g * p.N * D : p.K + g * D;
+  const uint16_t* Vb = clus ? p.Vc + (size_t)g * p.N * D : p.V + g * D;
+  const int32_t* cmem = clus ? mem : nullptr;
+  const bool pos_wave = __builtin_amdgcn_readfirstlane(wave) == 0;
   if (owner) {
-    ring[0][slot] = lookup(0, slot);
-    if (T > 1) ring[1][slot] = lookup(1, slot);
+    kidx[0][slot] = lookup(0, slot);
+    kidx[1][slot] = T > 1 ? lookup(1, slot) : -1;
   }
   __syncthreads();
   TileRegs r;
-  tile_load(r, p.K, p.V, ring[0], rs, g, tid);
-  tile_store(r, smem, tid);
+  tile_load(r, Kb, Vb, kidx[0], rs, tid, cmem);
+  tile_store(r, smem, kposb[0], tid, pos_wave, clus);
   __syncthreads();
   for (int tt = 0; tt < T; ++tt) {
-    int pending = -1;
-    if (tt + 1 < T) tile_load(r, p.K, p.V, ring[(tt + 1) % 3], rs, g, tid);
+    if (tt + 1 < T) tile_load(r, Kb, Vb, kidx[(tt + 1) % 3], rs, tid, cmem);
     const bool prep = tt + 2 < T && owner;
-    if (prep) pending = lookup(tt + 2, slot);
-    tile_compute(smem + (tt & 1) * BUF_ELEMS, ring[tt % 3], qf, acc, lane, kh, i, p.window, p.c);
-    if (tt + 1 < T) tile_store(r, smem + ((tt + 1) & 1) * BUF_ELEMS, tid);
-    if (prep) ring[(tt + 2) % 3][slot] = pending;
+    const int nrow = prep ? lookup(tt + 2, slot) : -1;
+    tile_compute(smem + (tt & 1) * BUF_ELEMS, kposb[tt & 1], qf, acc, lane, kh, i, p.window, p.c);
+    if (tt + 1 < T) tile_store(r, smem + ((tt + 1) & 1) * BUF_ELEMS, kposb[(tt + 1) & 1], tid, pos_wave, clus);
+    if (prep) kidx[(tt + 2) % 3][slot] = nrow;
     __syncthreads();
   }
 
@@ -346,10 +418,11 @@ __global__ __launch_bounds__(NT, 2) void attn_selected_kernel(AttnParams p, SelL
 // workgroup of 8 waves serves a pack of up to 4 of them and each gathered
 // 64-key tile is read from HBM once for 4 heads x 64 rows.  Wave w takes
 // head slot w % 4 and query rows 32 (w / 4) .. +31 and computes the whole
-// tile (two 32-key halves); waves 0-3 stage V (transposed), waves 4-7 K.
-// Step t stages tile t+1 from registers, starts the loads of tile t+2 (whose
-// key rows were looked up a step earlier), looks up tile t+3 and computes
-// tile t; one barrier per step.
+// tile (two 32-key halves); waves 0-3 stage V (transposed), waves 4-7 K,
+// wave 0 also the slots' key positions.  Step t stages tile t+1 from
+// registers, starts the loads of tile t+2, looks up the rows of tile t+3
+// (from LDS only) and computes tile t; one barrier per step, and no wait
+// inside a step covers the loads that step starts.
 namespace grp {
 
 constexpr int NT8 = 512;
@@ -358,23 +431,28 @@ constexpr int kRing = 4;   // looked-up key rows: tiles t .. t+3
 
 struct Regs {
   u32x4 x[4];
+  int row, pos;   // row of slot `lane` and the word read for its key position
 };
 
-// Thread's share: V threads (waves 0-3) read key slots 4 (tid % 16) + x at
-// d = 8 (tid / 16) .. +8; K threads read 16-byte chunk (u % 16) of key slot
-// 16 x + u / 16 (u = tid - 256).  Empty slots (key -1) read key row 0.
-__device__ __forceinline__ void load(Regs& r, const char* __restrict__ base, const int* ring, int rs2, int tid,
-                                     bool v_wave) {
+// Thread's share: V threads (waves 0-3) read slots 4 (tid % 16) + x at
+// d = 8 (tid / 16) .. +8; K threads read 16-byte chunk (u % 16) of slot
+// 16 x + u / 16 (u = tid - 256).  base = the KV head's first row (V or K),
+// rs2 = bytes between rows; empty slots (row -1) read row 0.
+__device__ __forceinline__ void load(Regs& r, const char* __restrict__ base, const int* kidx, int rs2, int tid,
+                                     bool v_wave, const int32_t* __restrict__ mem) {
+  slot_position(mem, reinterpret_cast<const int32_t*>(base), kidx[tid & 63], r.row, r.pos);
 #pragma unroll
   for (int x = 0; x < 4; ++x) {
     const int s = v_wave ? (tid & 15) * 4 + x : x * 16 + ((tid - 256) >> 4);
     const int db = v_wave ? (tid >> 4) * 16 : ((tid - 256) & 15) * 16;
-    const int key = max(0, ring[s]);
-    r.x[x] = *reinterpret_cast<const u32x4*>(base + (size_t)key * rs2 + db);
+    const int row = max(0, kidx[s]);
+    r.x[x] = *reinterpret_cast<const u32x4*>(base + (size_t)row * rs2 + db);
   }
 }
 
-__device__ __forceinline__ void store(const Regs& r, uint16_t* buf, int tid, bool v_wave) {
+__device__ __forceinline__ void store(const Regs& r, uint16_t* buf, int* kposb, int tid, bool v_wave,
+                                      bool pos_wave, bool clus) {
+  if (pos_wave) kposb[tid & 63] = pos_of(r.row, r.pos, clus);
   if (v_wave) {
     uint16_t* Vt = buf + K_ELEMS;
     const int kg = tid & 15, dc = tid >> 4;
@@ -477,8 +555,10 @@ __device__ __forceinline__ void compute(const uint16_t* __restrict__ buf, const 
 __global__ __launch_bounds__(grp::NT8, 1) void attn_selected_group_kernel(AttnParams p, PackTable packs) {
   using namespace grp;
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * BUF_ELEMS];
-  __shared__ __attribute__((aligned(16))) int ring[kRing][BK];
+  __shared__ __attribute__((aligned(16))) int kidx[kRing][BK];   // row each slot loads
+  __shared__ __attribute__((aligned(16))) int kposb[2][BK];      // key positions of the staged tiles
   __shared__ int ent[kMaxTopk + 1];     // block id (block mode) or CSR start (cluster mode)
+  __shared__ int ehi[kMaxTopk + 1];     // cluster mode: end of the member range
   __shared__ int pre[kMaxTopk + 2];     // prefix of visible key counts per entry
   __shared__ int tmp8[8];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -494,52 +574,23 @@ __global__ __launch_bounds__(grp::NT8, 1) void attn_selected_group_kernel(AttnPa
   const int srow = packs.sel_row[pk];
   const int q0 = b * BK;
   const int lim = min(p.N, q0 + BK) - 1 - p.window;   // keys j <= lim can be visible
-  const int n_kb = (p.N + BK - 1) / BK;
   const int32_t* mem = p.csr_mem ? p.csr_mem + (size_t)g * p.N : nullptr;
 
   // entries: forced block 0 + the selection; count of keys j <= lim in each
   const int ne = p.topk + (p.force_block0 ? 1 : 0);
-  int cnt = 0, start = 0;
-  if (tid < ne && lim >= 0) {
-    if (p.force_block0 && tid == 0) {
-      start = 0;
-      cnt = min(BK, lim + 1);
-    } else {
-      const int e = tid - (p.force_block0 ? 1 : 0);
-      const int v = p.sel[((size_t)srow * p.n_qt + b) * p.topk + e];
-      if (p.M > 0) {
-        if (v >= 0 && v < p.M) {
-          const int32_t* off = p.csr_off + (size_t)g * (p.M + 1);
-          const int lo = off[v];
-          int a = lo, bb = off[v + 1];
-          while (a < bb) {
-            const int mid = (a + bb) >> 1;
-            if (mem[mid] <= lim) a = mid + 1;
-            else bb = mid;
-          }
-          start = lo;
-          cnt = a - lo;
-        }
-      } else if (v >= 0 && v < n_kb && !(p.force_block0 && v == 0)) {
-        start = v;
-        cnt = max(0, min(BK, lim - v * BK + 1));
-      }
-    }
-  }
+  entry_table<8>(p, p.sel + ((size_t)srow * p.n_qt + b) * p.topk, g, lim, ne, ent, ehi, pre);
+  const int cnt = tid < ne ? pre[tid] : 0;
   int total;
   const int excl = dev::block_excl_scan<8>(cnt, tmp8, &total);
-  if (tid < ne) {
-    ent[tid] = start;
-    pre[tid] = excl;
-  }
+  if (tid < ne) pre[tid] = excl;
   if (tid == 0) pre[ne] = total;
   __syncthreads();
   const int T = (total + BK - 1) / BK;
   if (T == 0) return;
 
-  // key row of slot s of tile idx (flat index f = 64 idx + s); slot s of
-  // every tile is looked up by thread 8 s, whose entry index only moves
-  // forward from tile to tile
+  // row of slot s of tile idx (flat index f = 64 idx + s): key position
+  // (block mode) or CSR index (cluster mode); slot s of every tile is looked
+  // up by thread 8 s, whose entry index only moves forward from tile to tile
   const bool owner = (tid & 7) == 0;
   const int kslot = tid >> 3;
   int cur_e = 0;
@@ -548,10 +599,8 @@ __global__ __launch_bounds__(grp::NT8, 1) void attn_selected_group_kernel(AttnPa
     if (f >= total) return -1;
     while (cur_e + 1 < ne && pre[cur_e + 1] <= f) ++cur_e;
     const int r = f - pre[cur_e];
-    if (p.M > 0) return (int)mem[ent[cur_e] + r];
-    return ent[cur_e] * BK + r;
+    return p.M > 0 ? ent[cur_e] + r : ent[cur_e] * BK + r;
   };
-
   const int lr = lane & 31, lh = lane >> 5;
   const int qw = q0 + QW * (wave >> 2);
   const int i = qw + lr;
@@ -577,29 +626,31 @@ __global__ __launch_bounds__(grp::NT8, 1) void attn_selected_group_kernel(AttnPa
     for (int e = 0; e < 16; ++e) acc.o[db][e] = 0.f;
 
   const bool v_wave = wave < 4;
-  const int rs2 = p.Hkv * D * 2;   // bytes between consecutive keys
-  const char* base = reinterpret_cast<const char*>((v_wave ? p.V : p.K) + g * D);
+  const bool clus = p.M > 0;
+  const int rs2 = (clus ? D : p.Hkv * D) * 2;   // bytes between consecutive rows
+  const uint16_t* src = clus ? (v_wave ? p.Vc : p.Kc) + (size_t)g * p.N * D : (v_wave ? p.V : p.K) + g * D;
+  const char* base = reinterpret_cast<const char*>(src);
+  const int32_t* cmem = clus ? mem : nullptr;
+  const bool pos_wave = wave == 0;
   if (owner) {
 #pragma unroll
-    for (int x = 0; x < 3; ++x)
-      if (x < T) ring[x][kslot] = lookup(x);
+    for (int x = 0; x < 3; ++x) kidx[x][kslot] = x < T ? lookup(x) : -1;
   }
   __syncthreads();
   Regs r;
-  load(r, base, ring[0], rs2, tid, v_wave);
-  store(r, smem, tid, v_wave);
-  if (T > 1) load(r, base, ring[1], rs2, tid, v_wave);
+  load(r, base, kidx[0], rs2, tid, v_wave, cmem);
+  store(r, smem, kposb[0], tid, v_wave, pos_wave, clus);
+  if (T > 1) load(r, base, kidx[1], rs2, tid, v_wave, cmem);
   __syncthreads();
   for (int t = 0; t < T; ++t) {
     if (t + 1 < T) {
-      store(r, smem + ((t + 1) & 1) * BUF_ELEMS, tid, v_wave);
-      if (t + 2 < T) load(r, base, ring[(t + 2) % kRing], rs2, tid, v_wave);
+      store(r, smem + ((t + 1) & 1) * BUF_ELEMS, kposb[(t + 1) & 1], tid, v_wave, pos_wave, clus);
+      if (t + 2 < T) load(r, base, kidx[(t + 2) % kRing], rs2, tid, v_wave, cmem);
     }
     const bool prep = owner && t + 3 < T;
-    int pending = -1;
-    if (prep) pending = lookup(t + 3);
-    if (active) compute(smem + (t & 1) * BUF_ELEMS, ring[t % kRing], qf, acc, lane, i, p.window, p.c);
-    if (prep) ring[(t + 3) % kRing][kslot] = pending;
+    const int nrow = prep ? lookup(t + 3) : -1;
+    if (active) compute(smem + (t & 1) * BUF_ELEMS, kposb[t & 1], qf, acc, lane, i, p.window, p.c);
+    if (prep) kidx[(t + 3) % kRing][kslot] = nrow;
     __syncthreads();
   }
 
@@ -628,7 +679,30 @@ __global__ __launch_bounds__(grp::NT8, 1) void attn_selected_group_kernel(AttnPa
     }
 }
 
+// Cluster mode: row e of KV head g in Kc / Vc is key csr_mem[g][e] of K / V
+// (16 threads per row, 16 bytes each; positions are clamped into [0, N)).
+// Memory-bound: K and V are read once and written once.
+__global__ __launch_bounds__(256) void permute_kv_kernel(AttnParams p) {
+  const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t row = t >> 4;   // g * N + e
+  const int c = (int)(t & 15);
+  if (row >= (size_t)p.Hkv * p.N) return;
+  const int g = (int)(row / (size_t)p.N);
+  const int j = min(max((int)p.csr_mem[row], 0), p.N - 1);
+  const size_t src = ((size_t)j * p.Hkv + g) * D + c * 8;
+  const size_t dst = row * D + c * 8;
+  *reinterpret_cast<u32x4*>(p.Kc + dst) = *reinterpret_cast<const u32x4*>(p.K + src);
+  *reinterpret_cast<u32x4*>(p.Vc + dst) = *reinterpret_cast<const u32x4*>(p.V + src);
+}
+
 }  // namespace
+
+hipError_t launch_permute_kv(const AttnParams& p, hipStream_t s) {
+  const size_t threads = (size_t)p.Hkv * p.N * 16;
+  if (threads == 0) return hipSuccess;
+  hipLaunchKernelGGL(permute_kv_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_attn_selected(const AttnParams& p, const SelList& sl, hipStream_t s) {
   const int nwg = sl.n_ret * p.n_qt;

@@ -178,7 +178,13 @@ int ha_attn_band(const ha_layer_desc* desc, const int32_t* head_kind,
 
 /* Stage: retrieval heads: window U selected keys (U key block 0 when forced).
  * Block mode reads sel only; cluster mode also reads assign/csr.
- *   csr_off, csr_mem: NULL in block mode.
+ *   csr_off, csr_mem: NULL in block mode; in cluster mode a valid CSR (each
+ *              cluster's members ascending, positions in [0, N)).
+ *   workspace  >= ha_workspace_bytes(desc, head_kind) bytes, 256-byte aligned:
+ *              the window part's log2-sum-exp per retrieval row and, in
+ *              cluster mode, K and V copied into CSR order (2 * Hkv * N * D
+ *              bf16), so that a selected cluster's visible members are read
+ *              as one contiguous range of rows.
  * With group_select = 1 every retrieval head of a KV group reads the sel row
  * of the group's first retrieval head (the rows ha_select_* writes are equal). */
 int ha_attn_gather(const ha_layer_desc* desc, const int32_t* head_kind,
