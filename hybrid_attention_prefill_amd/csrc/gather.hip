@@ -564,8 +564,10 @@ __global__ __launch_bounds__(grp::NT8, 1) void attn_selected_group_kernel(AttnPa
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int pk = lid / p.n_qt;
-  const int b = p.n_qt - 1 - lid % p.n_qt;    // long key lists first
+  // packs fastest: the packs of a KV group (same selection, same rows) run
+  // side by side on one XCD and share its L2; long key lists first
+  const int pk = lid % packs.n;
+  const int b = p.n_qt - 1 - lid / packs.n;
   const uint32_t pw = packs.heads[pk];
   const int hs = wave & 3;
   const int h = (pw >> (8 * hs)) & 0xFF;
