@@ -289,20 +289,17 @@ int run_select_blocks(const ha_layer_desc* d, const Heads& h, const float* qlow,
 }
 
 // Retrieval heads: the window part through the banded kernel (which also
-// leaves each row's log2-sum-exp), then the selected keys, merged in.
+// leaves each row's log2-sum-exp), then the selected keys, merged in; with
+// group-shared selection one kernel computes both parts.
 int run_gather(const ha_layer_desc* d, const int32_t* kinds, const Heads& h, const void* Q, const void* K,
                const void* V, const int32_t* sel, const int32_t* csr_off, const int32_t* csr_mem, float* O,
                float* lse, void* kvc, hipStream_t s) {
   if (h.ret.empty()) return HA_OK;
   AttnParams p = attn_params(d, Q, K, V, O);
-  p.kind = SWA;
-  p.lse = lse;
   PackTable pt;
   build_packs(d, kinds, RETRIEVAL, h.ret_slot, &pt);
-  int st = dev_status(launch_attn_band(p, pt, s));
-  if (st != HA_OK) return st;
-  p.kind = RETRIEVAL;
   p.sel = sel;
+  int st = HA_OK;
   if (d->n_clusters > 0) {
     p.csr_off = csr_off;
     p.csr_mem = csr_mem;
@@ -312,7 +309,14 @@ int run_gather(const ha_layer_desc* d, const int32_t* kinds, const Heads& h, con
     st = dev_status(launch_permute_kv(p, s));
     if (st != HA_OK) return st;
   }
-  if (d->group_select) return dev_status(launch_attn_selected_group(p, pt, s));
+  // group-shared selection: window and selected keys of a pack in one kernel
+  p.kind = RETRIEVAL;
+  if (d->group_select) return dev_status(launch_attn_retrieval_group(p, pt, s));
+  p.kind = SWA;
+  p.lse = lse;
+  st = dev_status(launch_attn_band(p, pt, s));
+  if (st != HA_OK) return st;
+  p.kind = RETRIEVAL;
   SelList sl;
   sl.n_ret = (int)h.ret.size();
   for (int t = 0; t < sl.n_ret; ++t) sl.head[t] = h.ret[t];

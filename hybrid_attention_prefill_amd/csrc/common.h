@@ -64,10 +64,11 @@ struct SelList {
 // Host launchers (each returns a hipError_t from the launch).
 hipError_t launch_attn_band(const AttnParams& p, const PackTable& packs, hipStream_t s);
 hipError_t launch_attn_selected(const AttnParams& p, const SelList& sl, hipStream_t s);
-// Group-shared selection: every retrieval head of a KV group reads the same
-// selection row, so one workgroup serves a pack of up to 4 of them (the pack's
-// first slot names the row).
-hipError_t launch_attn_selected_group(const AttnParams& p, const PackTable& packs, hipStream_t s);
+// Group-shared selection: every retrieval head of a KV group has the same key
+// set (window + the selection row of the group's first retrieval head), so
+// one workgroup computes a pack of up to 4 of them, window and selected keys
+// together, and writes O (no log2-sum-exp).
+hipError_t launch_attn_retrieval_group(const AttnParams& p, const PackTable& packs, hipStream_t s);
 // Cluster mode: copies K and V rows into CSR order (Kc, Vc) so that the
 // visible members of a cluster are one contiguous range of rows.
 hipError_t launch_permute_kv(const AttnParams& p, hipStream_t s);

@@ -341,6 +341,9 @@ __global__ __launch_bounds__(NT, 2) void attn_selected_kernel(AttnParams p, SelL
   const uint16_t* Vb = clus ? p.Vc + (size_t)g * p.N * D : p.V + g * D;
   const int32_t* cmem = clus ? mem : nullptr;
   const bool pos_wave = __builtin_amdgcn_readfirstlane(wave) == 0;
+  // every earlier global read (Q fragments, entry table) is complete here, so
+  // the waits inside the loop count only the tile loads
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   if (owner) {
     kidx[0][slot] = lookup(0, slot);
     kidx[1][slot] = T > 1 ? lookup(1, slot) : -1;
@@ -414,38 +417,58 @@ __global__ __launch_bounds__(NT, 2) void attn_selected_kernel(AttnParams p, SelL
 // ---------------------------------------------------------------------------
 // Group-shared selection (36kr interview, GQA answer: the query heads of one
 // GQA group share their keys, so one selection serves the group).  Every
-// retrieval head of a KV group attends to the same gathered keys, so a
-// workgroup of 8 waves serves a pack of up to 4 of them and each gathered
-// 64-key tile is read from HBM once for 4 heads x 64 rows.  Wave w takes
-// head slot w % 4 and query rows 32 (w / 4) .. +31 and computes the whole
-// tile (two 32-key halves); waves 0-3 stage V (transposed), waves 4-7 K,
-// wave 0 also the slots' key positions.  Step t stages tile t+1 from
-// registers, starts the loads of tile t+2, looks up the rows of tile t+3
-// (from LDS only) and computes tile t; one barrier per step, and no wait
-// inside a step covers the loads that step starts.
+// retrieval head of a KV group then has the same key set per query block,
+// window included, so one workgroup computes a pack of up to 4 of them
+// completely: the window tiles (contiguous keys) and the gathered tiles go
+// through one online softmax and O is written once (no separate window pass,
+// no log2-sum-exp, no read-back of O).  8 waves: wave w takes head slot
+// w % 4 and query rows 32 (w / 4) .. +31 and computes the whole tile, so a
+// tile read from HBM serves 256 rows; waves 0-3 stage V (transposed), waves
+// 4-7 K, wave 0 also the gathered slots' key positions.  Step t stages tile
+// t+1 from registers, starts the loads of tile t+2, looks up the rows of
+// gathered tile t+3 (from LDS only) and computes tile t; one barrier per
+// step, and no wait inside a step covers the loads that step starts.
 namespace grp {
 
 constexpr int NT8 = 512;
 constexpr int QW = 32;     // query rows per wave
-constexpr int kRing = 4;   // looked-up key rows: tiles t .. t+3
+constexpr int kRing = 4;   // looked-up rows of gathered tiles
 
 struct Regs {
   u32x4 x[4];
   int row, pos;   // row of slot `lane` and the word read for its key position
 };
 
-// Thread's share: V threads (waves 0-3) read slots 4 (tid % 16) + x at
-// d = 8 (tid / 16) .. +8; K threads read 16-byte chunk (u % 16) of slot
-// 16 x + u / 16 (u = tid - 256).  base = the KV head's first row (V or K),
-// rs2 = bytes between rows; empty slots (row -1) read row 0.
-__device__ __forceinline__ void load(Regs& r, const char* __restrict__ base, const int* kidx, int rs2, int tid,
-                                     bool v_wave, const int32_t* __restrict__ mem) {
+// Thread's share of a tile: V threads (waves 0-3) read slots 4 (tid % 16) + x
+// at d = 8 (tid / 16) .. +8; K threads read 16-byte chunk (u % 16) of slot
+// 16 x + u / 16 (u = tid - 256).
+__device__ __forceinline__ int slot_of(int tid, int x, bool v_wave) {
+  return v_wave ? (tid & 15) * 4 + x : x * 16 + ((tid - 256) >> 4);
+}
+__device__ __forceinline__ int dbyte_of(int tid, bool v_wave) {
+  return v_wave ? (tid >> 4) * 16 : ((tid - 256) & 15) * 16;
+}
+
+// Gathered tile: base = the KV head's first row (V or K, original or in CSR
+// order), rs2 = bytes between rows; empty slots (row -1) read row 0.
+__device__ __forceinline__ void load_gathered(Regs& r, const char* __restrict__ base, const int* kidx, int rs2,
+                                              int tid, bool v_wave, const int32_t* __restrict__ mem) {
   slot_position(mem, reinterpret_cast<const int32_t*>(base), kidx[tid & 63], r.row, r.pos);
+  const int db = dbyte_of(tid, v_wave);
 #pragma unroll
   for (int x = 0; x < 4; ++x) {
-    const int s = v_wave ? (tid & 15) * 4 + x : x * 16 + ((tid - 256) >> 4);
-    const int db = v_wave ? (tid >> 4) * 16 : ((tid - 256) & 15) * 16;
-    const int row = max(0, kidx[s]);
+    const int row = max(0, kidx[slot_of(tid, x, v_wave)]);
+    r.x[x] = *reinterpret_cast<const u32x4*>(base + (size_t)row * rs2 + db);
+  }
+}
+
+// Window tile: keys k0 .. k0+63 (keys past N read key N-1; masked).
+__device__ __forceinline__ void load_window(Regs& r, const char* __restrict__ base, int k0, int N, int rs2, int tid,
+                                            bool v_wave) {
+  const int db = dbyte_of(tid, v_wave);
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int row = min(k0 + slot_of(tid, x, v_wave), N - 1);
     r.x[x] = *reinterpret_cast<const u32x4*>(base + (size_t)row * rs2 + db);
   }
 }
@@ -479,9 +502,13 @@ __device__ __forceinline__ void store(const Regs& r, uint16_t* buf, int* kposb, 
   }
 }
 
-// The whole tile (both key halves) against the wave's 32 rows.
+// The whole tile (both key halves) against the wave's 32 rows (this lane's
+// row i).  Gathered tile: key of slot s is kpos[s], visible iff j >= 0 and
+// i - j >= w.  Window tile (keys k0 + s): visible iff 0 <= i - j < w; the
+// mask is skipped when every key is visible to every row of the wave.
 __device__ __forceinline__ void compute(const uint16_t* __restrict__ buf, const int* __restrict__ kpos,
-                                        const bf16x8 (&qf)[8], Acc& acc, int lane, int i, int w, float c) {
+                                        bool gathered, int k0, bool full, const bf16x8 (&qf)[8], Acc& acc,
+                                        int lane, int i, int w, float c) {
   const uint16_t* Ks = buf;
   const uint16_t* Vt = buf + K_ELEMS;
   const int lr = lane & 31, lh = lane >> 5;
@@ -497,20 +524,36 @@ __device__ __forceinline__ void compute(const uint16_t* __restrict__ buf, const 
       const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + (kb * 32 + lr) * KSTR + t * 16 + lh * 8);
       s[kb] = mfma(kf, qf[t], s[kb]);
     }
+  if (gathered) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int4 jv = *reinterpret_cast<const int4*>(kpos + kb * 32 + lh * 4 + q * 8);
+        const int js[4] = {jv.x, jv.y, jv.z, jv.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool vis = (js[e] >= 0) & (i - js[e] >= w);
+          s[kb][q * 4 + e] = vis ? s[kb][q * 4 + e] : kNegInf;
+        }
+      }
+  } else if (!full) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int dd = i - (k0 + kb * 32 + lh * 4);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int d = dd - ((e >> 2) * 8 + (e & 3));
+        const bool vis = (d >= 0) & (d < w);
+        s[kb][e] = vis ? s[kb][e] : kNegInf;
+      }
+    }
+  }
   float mx = kNegInf;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int4 jv = *reinterpret_cast<const int4*>(kpos + kb * 32 + lh * 4 + q * 8);
-      const int js[4] = {jv.x, jv.y, jv.z, jv.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool vis = (js[e] >= 0) & (i - js[e] >= w);
-        s[kb][q * 4 + e] = vis ? s[kb][q * 4 + e] : kNegInf;
-        mx = fmaxf(mx, s[kb][q * 4 + e]);
-      }
-    }
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
   mx = dev::pair32_max(mx);
   if (__any((mx - acc.m) * c > kSlack)) {
     const float mnew = fmaxf(acc.m, mx);
@@ -552,10 +595,10 @@ __device__ __forceinline__ void compute(const uint16_t* __restrict__ buf, const 
 
 }  // namespace grp
 
-__global__ __launch_bounds__(grp::NT8, 1) void attn_selected_group_kernel(AttnParams p, PackTable packs) {
+__global__ __launch_bounds__(grp::NT8, 1) void attn_retrieval_group_kernel(AttnParams p, PackTable packs) {
   using namespace grp;
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * BUF_ELEMS];
-  __shared__ __attribute__((aligned(16))) int kidx[kRing][BK];   // row each slot loads
+  __shared__ __attribute__((aligned(16))) int kidx[kRing][BK];   // rows of gathered tiles
   __shared__ __attribute__((aligned(16))) int kposb[2][BK];      // key positions of the staged tiles
   __shared__ int ent[kMaxTopk + 1];     // block id (block mode) or CSR start (cluster mode)
   __shared__ int ehi[kMaxTopk + 1];     // cluster mode: end of the member range
@@ -572,11 +615,14 @@ __global__ __launch_bounds__(grp::NT8, 1) void attn_selected_group_kernel(AttnPa
   const int hs = wave & 3;
   const int h = (pw >> (8 * hs)) & 0xFF;
   const int g = (int)(pw & 0xFF) / p.G;
-  const int slot = (packs.slots[pk] >> (8 * hs)) & 0xFF;
   const int srow = packs.sel_row[pk];
   const int q0 = b * BK;
-  const int lim = min(p.N, q0 + BK) - 1 - p.window;   // keys j <= lim can be visible
+  const int lim = min(p.N, q0 + BK) - 1 - p.window;   // keys j <= lim can be selected
   const int32_t* mem = p.csr_mem ? p.csr_mem + (size_t)g * p.N : nullptr;
+
+  // window tiles: keys max(0, q0 - w + 1) .. min(N - 1, q0 + 63)
+  const int wlo = max(0, q0 - p.window + 1) >> 6;
+  const int T_win = (min(p.N - 1, q0 + 63) >> 6) - wlo + 1;
 
   // entries: forced block 0 + the selection; count of keys j <= lim in each
   const int ne = p.topk + (p.force_block0 ? 1 : 0);
@@ -587,12 +633,12 @@ __global__ __launch_bounds__(grp::NT8, 1) void attn_selected_group_kernel(AttnPa
   if (tid < ne) pre[tid] = excl;
   if (tid == 0) pre[ne] = total;
   __syncthreads();
-  const int T = (total + BK - 1) / BK;
-  if (T == 0) return;
+  const int T_sel = (total + BK - 1) / BK;
+  const int T = T_win + T_sel;
 
-  // row of slot s of tile idx (flat index f = 64 idx + s): key position
-  // (block mode) or CSR index (cluster mode); slot s of every tile is looked
-  // up by thread 8 s, whose entry index only moves forward from tile to tile
+  // row of slot s of gathered tile idx (flat index f = 64 idx + s): key
+  // position (block mode) or CSR index (cluster mode); slot s of every tile
+  // is looked up by thread 8 s, whose entry index only moves forward
   const bool owner = (tid & 7) == 0;
   const int kslot = tid >> 3;
   int cur_e = 0;
@@ -603,6 +649,7 @@ __global__ __launch_bounds__(grp::NT8, 1) void attn_selected_group_kernel(AttnPa
     const int r = f - pre[cur_e];
     return p.M > 0 ? ent[cur_e] + r : ent[cur_e] * BK + r;
   };
+
   const int lr = lane & 31, lh = lane >> 5;
   const int qw = q0 + QW * (wave >> 2);
   const int i = qw + lr;
@@ -629,55 +676,64 @@ __global__ __launch_bounds__(grp::NT8, 1) void attn_selected_group_kernel(AttnPa
 
   const bool v_wave = wave < 4;
   const bool clus = p.M > 0;
-  const int rs2 = (clus ? D : p.Hkv * D) * 2;   // bytes between consecutive rows
-  const uint16_t* src = clus ? (v_wave ? p.Vc : p.Kc) + (size_t)g * p.N * D : (v_wave ? p.V : p.K) + g * D;
-  const char* base = reinterpret_cast<const char*>(src);
+  const int rs2w = p.Hkv * D * 2;                       // bytes between keys of K / V
+  const int rs2 = clus ? D * 2 : rs2w;                  // ... of the gathered rows
+  const char* wbase = reinterpret_cast<const char*>((v_wave ? p.V : p.K) + g * D);
+  const char* gbase = clus ? reinterpret_cast<const char*>((v_wave ? p.Vc : p.Kc) + (size_t)g * p.N * D) : wbase;
   const int32_t* cmem = clus ? mem : nullptr;
   const bool pos_wave = wave == 0;
+  auto load_tile = [&](Regs& r, int u) {
+    if (u < T_win) load_window(r, wbase, (wlo + u) * BK, p.N, rs2w, tid, v_wave);
+    else load_gathered(r, gbase, kidx[(u - T_win) % kRing], rs2, tid, v_wave, cmem);
+  };
+  // every earlier global read (Q fragments, entry table) is complete here, so
+  // the waits inside the loop count only the tile loads
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   if (owner) {
 #pragma unroll
-    for (int x = 0; x < 3; ++x) kidx[x][kslot] = x < T ? lookup(x) : -1;
+    for (int x = 0; x < 3; ++x) kidx[x][kslot] = x < T_sel ? lookup(x) : -1;
   }
   __syncthreads();
   Regs r;
-  load(r, base, kidx[0], rs2, tid, v_wave, cmem);
+  load_tile(r, 0);
   store(r, smem, kposb[0], tid, v_wave, pos_wave, clus);
-  if (T > 1) load(r, base, kidx[1], rs2, tid, v_wave, cmem);
+  if (T > 1) load_tile(r, 1);
   __syncthreads();
   for (int t = 0; t < T; ++t) {
     if (t + 1 < T) {
       store(r, smem + ((t + 1) & 1) * BUF_ELEMS, kposb[(t + 1) & 1], tid, v_wave, pos_wave, clus);
-      if (t + 2 < T) load(r, base, kidx[(t + 2) % kRing], rs2, tid, v_wave, cmem);
+      if (t + 2 < T) load_tile(r, t + 2);
     }
-    const bool prep = owner && t + 3 < T;
-    const int nrow = prep ? lookup(t + 3) : -1;
-    if (active) compute(smem + (t & 1) * BUF_ELEMS, kposb[t & 1], qf, acc, lane, i, p.window, p.c);
-    if (prep) kidx[(t + 3) % kRing][kslot] = nrow;
+    const int gt = t + 3 - T_win;   // gathered tile looked up in this step
+    const bool prep = owner && gt >= 3 && gt < T_sel;
+    const int nrow = prep ? lookup(gt) : -1;
+    if (active) {
+      const bool gathered = t >= T_win;
+      const int k0 = (wlo + t) * BK;
+      // window tile: all keys visible to every row of the wave / to none
+      const bool full = !gathered && k0 + 63 <= qw && qw + QW - 1 - k0 < p.window;
+      const bool empty = !gathered && (k0 > qw + QW - 1 || qw - (k0 + 63) >= p.window);
+      if (!empty) compute(smem + (t & 1) * BUF_ELEMS, kposb[t & 1], gathered, k0, full, qf, acc, lane, i, p.window,
+                          p.c);
+    }
+    if (prep) kidx[gt % kRing][kslot] = nrow;
     __syncthreads();
   }
 
-  // merge with the window result of the row
-  if (!active) return;
+  if (!active || i >= p.N) return;
   const float lt = dev::pair32_sum(acc.l);
-  if (i >= p.N || !(lt > 0.f)) return;
-  const float lse_s = acc.m * p.c + __log2f(lt);
-  const float lse_w = p.lse[(size_t)slot * p.N + i];
-  const float M = fmaxf(lse_s, lse_w);
-  const float ws = exp2f(lse_s - M), ww = exp2f(lse_w - M);
-  const float inv = 1.f / (ws + ww);
-  const float fs = ws * inv / lt, fw = ww * inv;
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
   float* row = p.O + ((size_t)i * p.Hq + h) * D;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
-      float4* dst = reinterpret_cast<float4*>(row + db * 32 + lh * 4 + r4 * 8);
-      float4 v = *dst;
-      v.x = fmaf(v.x, fw, acc.o[db][r4 * 4 + 0] * fs);
-      v.y = fmaf(v.y, fw, acc.o[db][r4 * 4 + 1] * fs);
-      v.z = fmaf(v.z, fw, acc.o[db][r4 * 4 + 2] * fs);
-      v.w = fmaf(v.w, fw, acc.o[db][r4 * 4 + 3] * fs);
-      *dst = v;
+      float4 v;
+      v.x = acc.o[db][r4 * 4 + 0] * inv;
+      v.y = acc.o[db][r4 * 4 + 1] * inv;
+      v.z = acc.o[db][r4 * 4 + 2] * inv;
+      v.w = acc.o[db][r4 * 4 + 3] * inv;
+      *reinterpret_cast<float4*>(row + db * 32 + lh * 4 + r4 * 8) = v;
     }
 }
 
@@ -713,10 +769,10 @@ hipError_t launch_attn_selected(const AttnParams& p, const SelList& sl, hipStrea
   return hipGetLastError();
 }
 
-hipError_t launch_attn_selected_group(const AttnParams& p, const PackTable& packs, hipStream_t s) {
+hipError_t launch_attn_retrieval_group(const AttnParams& p, const PackTable& packs, hipStream_t s) {
   const int nwg = packs.n * p.n_qt;
-  if (nwg == 0 || (p.topk == 0 && !p.force_block0)) return hipSuccess;
-  hipLaunchKernelGGL(attn_selected_group_kernel, dim3(nwg), dim3(grp::NT8), 0, s, p, packs);
+  if (nwg == 0) return hipSuccess;
+  hipLaunchKernelGGL(attn_retrieval_group_kernel, dim3(nwg), dim3(grp::NT8), 0, s, p, packs);
   return hipGetLastError();
 }
 
