@@ -17,6 +17,17 @@ Block mode (one selection per query head and query block b of Bq rows):
 Cluster mode replaces key blocks by k-means clusters of the low-rank keys:
   E_b = {m : cluster m has a member j <= qe - w}
   s_{b,m} = max_{i in R_b} qlow_i . C_m
+
+Cheaper block scores ([TriangleMix] interview, top-k matching: a block is
+represented by one point; the representatives named are the mean of its keys
+and a point built from each dimension's largest and smallest key value).
+With the block's keys K_c = {j in block c, j < N}:
+  mean:    s_{b,c} = max_{i in R_b} qlow_i . mean_{j in K_c} klow_j
+  min/max: s_{b,c} = max_{i in R_b} sum_d max(q_d kmax_{c,d}, q_d kmin_{c,d}),
+           kmax / kmin = per-dimension max / min over K_c: the largest dot
+           product any point of the box spanned by the block's keys can
+           reach, so it bounds every key's score from above.
+Causality inside a block is not applied by either representative.
 """
 from __future__ import annotations
 
@@ -50,6 +61,39 @@ def block_scores(qlow_rows: np.ndarray, row_ids: np.ndarray, klow: np.ndarray,
         causal = keys[None, :] <= row_ids[:, None]
         out[t] = np.max(np.where(causal, dots, -np.inf))
     return out
+
+
+def block_means(klow: np.ndarray, Bk: int) -> np.ndarray:
+    """Mean low-rank key of every key block (keys c*Bk .. min(N, (c+1)*Bk)-1)."""
+    N = klow.shape[0]
+    n_kb = (N + Bk - 1) // Bk
+    return np.stack([np.mean(klow[c * Bk: min(N, (c + 1) * Bk)], axis=0) for c in range(n_kb)])
+
+
+def block_extremes(klow: np.ndarray, Bk: int):
+    """Per-dimension (max, min) of the low-rank keys of every key block."""
+    N = klow.shape[0]
+    n_kb = (N + Bk - 1) // Bk
+    kmax = np.stack([np.max(klow[c * Bk: min(N, (c + 1) * Bk)], axis=0) for c in range(n_kb)])
+    kmin = np.stack([np.min(klow[c * Bk: min(N, (c + 1) * Bk)], axis=0) for c in range(n_kb)])
+    return kmax, kmin
+
+
+def block_scores_mean(qlow_rows: np.ndarray, means: np.ndarray, blocks: np.ndarray) -> np.ndarray:
+    """max_{i in block} qlow_i . mean_c for each candidate block c."""
+    if blocks.size == 0:
+        return np.zeros(0)
+    return np.max(qlow_rows @ means[blocks].T, axis=0)
+
+
+def block_scores_minmax(qlow_rows: np.ndarray, kmax: np.ndarray, kmin: np.ndarray,
+                        blocks: np.ndarray) -> np.ndarray:
+    """max_{i in block} sum_d max(q_id kmax_cd, q_id kmin_cd) per candidate block c."""
+    if blocks.size == 0:
+        return np.zeros(0)
+    q = qlow_rows[:, None, :]                                   # [rows, 1, r]
+    bound = np.maximum(q * kmax[blocks][None], q * kmin[blocks][None]).sum(axis=2)
+    return np.max(bound, axis=0)
 
 
 def topk_order(scores: np.ndarray, ids: np.ndarray, k: int) -> np.ndarray:

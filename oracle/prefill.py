@@ -11,7 +11,10 @@ With group-shared selection ([TriangleMix] interview, GQA answer: the queries
 of one GQA group share the same keys, and sharing work across the group is
 the usual practice), S_b is chosen once per (KV head, query block) from the
 group score max over the group's retrieval heads of the head scores, and
-every retrieval head of the group uses it.
+every retrieval head of the group uses it.  Block mode scores candidates by
+the max over causal (query, key) pairs, or, with `block_score` 1 / 2, by the
+block's mean key / the bound from its per-dimension key extremes
+(oracle.indexer).
 [RTPurbo]: exact softmax over the selected candidates in full dimension, with
 the local window of the head's own neighbourhood.
 
@@ -29,8 +32,8 @@ from typing import Callable, Dict, Optional, Sequence
 import numpy as np
 
 from .attention import attend_rows, softmax_attention, visible_dense, visible_swa, visible_triangle
-from .indexer import (cluster_scores, eligible_blocks, eligible_clusters, block_scores,
-                      project, topk_order)
+from .indexer import (block_extremes, block_means, block_scores, block_scores_mean, block_scores_minmax,
+                      cluster_scores, eligible_blocks, eligible_clusters, project, topk_order)
 from .kmeans import lloyd
 
 SWA, RETRIEVAL, TRIANGLE, DENSE = 0, 1, 2, 3
@@ -148,6 +151,7 @@ def layer_prefill(w, q_rows: Callable[[int, int], np.ndarray], K: np.ndarray, V:
 
     eligible_memo = {}   # (KV head, block) -> eligible clusters (shared by the group's heads)
     group_memo = {}      # (KV head, block) -> (eligible, group scores, selection)
+    rep_memo = {}        # block representatives per KV head
     ret_of_group = {}
     for hh in range(Hq):   # all of a group's retrieval heads, even outside `heads`
         if w.head_kind[hh] == RETRIEVAL:
@@ -163,7 +167,18 @@ def layer_prefill(w, q_rows: Callable[[int, int], np.ndarray], K: np.ndarray, V:
             E = eligible_memo[(g, b)]
             return ql, E, cluster_scores(ql, C, E)
         E = eligible_blocks(qe, w.window, w.force_block0, Bk)
-        return ql, E, (block_scores(ql, rows, res.klow[g], E, Bk) if E.size else np.zeros(0))
+        if not E.size:
+            return ql, E, np.zeros(0)
+        if w.block_score == 1:
+            if ("mean", g) not in rep_memo:
+                rep_memo[("mean", g)] = block_means(res.klow[g], Bk)
+            return ql, E, block_scores_mean(ql, rep_memo[("mean", g)], E)
+        if w.block_score == 2:
+            if ("ext", g) not in rep_memo:
+                rep_memo[("ext", g)] = block_extremes(res.klow[g], Bk)
+            kmax, kmin = rep_memo[("ext", g)]
+            return ql, E, block_scores_minmax(ql, kmax, kmin, E)
+        return ql, E, block_scores(ql, rows, res.klow[g], E, Bk)
 
     off = 0
     for b in blocks:

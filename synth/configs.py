@@ -45,6 +45,10 @@ class Workload:
     # 1: one selection per (KV head, query block), scored by the max over the
     # group's retrieval heads and shared by them (GQA-group-shared selection)
     group_select: int = 0
+    # block-mode candidate score: 0 max over causal (query, key) pairs,
+    # 1 the block's mean key (representative), 2 the bound from the block's
+    # per-dimension key maxima and minima
+    block_score: int = 0
     # input recipe: "plain", "planted_lowfreq" (keys carry per-segment topic
     # vectors on the low-frequency dims), "needles" (planted key/query pairs)
     recipe: str = "plain"
@@ -72,7 +76,7 @@ class Workload:
             force_block0=self.force_block0, n_clusters=self.n_clusters,
             kmeans_iters=self.kmeans_iters, kmeans_stride=self.kmeans_stride,
             sink=self.sink, last_q=self.last_q, n_out=self.n_out,
-            group_select=self.group_select,
+            group_select=self.group_select, block_score=self.block_score,
         )
 
 
