@@ -171,7 +171,7 @@ class Layer:
         self.desc = ha.make_desc(N, Hq, Hkv, D, window=w.window, topk=w.topk, force_block0=w.force_block0,
                                  n_clusters=w.n_clusters, kmeans_iters=w.kmeans_iters,
                                  kmeans_stride=w.kmeans_stride, sink=w.sink, last_q=w.last_q, n_out=w.n_out,
-                                 group_select=w.group_select)
+                                 group_select=w.group_select, block_score=w.block_score)
         self.kinds = list(w.head_kind)
         self.O = torch.empty((N, Hq, D), dtype=torch.float32, device=dev)
         self.O_out = torch.empty((w.n_out, Hq, D), dtype=torch.float32, device=dev) if w.n_out else None
@@ -205,7 +205,7 @@ class Layer:
                     self.O, self.ws)))
             else:
                 st.append(("select_blocks", lambda: ha.ha_select_blocks(self.desc, self.kinds, self.qlow,
-                                                                         self.klow, self.sel)))
+                                                                         self.klow, self.sel, self.ws)))
                 st.append(("attn_gather", lambda: ha.ha_attn_gather(self.desc, self.kinds, self.Q, self.K, self.V,
                                                                      self.sel, None, None, self.O, self.ws)))
         if self.has_band:

@@ -34,6 +34,8 @@ int check_desc(const ha_layer_desc* d, const int32_t* kinds, Heads* out) {
   if (d->n_out < 0 || d->n_out > d->n_tokens) return HA_ERR_ARG;
   if (!kinds) return HA_ERR_ARG;
   if (d->group_select != 0 && d->group_select != 1) return HA_ERR_ARG;
+  if (d->block_score < 0 || d->block_score > 2) return HA_ERR_ARG;
+  if (d->block_score != 0 && d->n_clusters > 0) return HA_ERR_ARG;   // a block-mode option
   Heads h;
   h.ret_slot.assign(d->n_q_heads, -1);
   bool need_window = false, any_tri = false;
@@ -105,8 +107,14 @@ size_t cross_ws_bytes(const ha_layer_desc* d) {
 }
 
 struct Layout {
-  size_t qlow, klow, sel, lse, cent, assign, csr_off, csr_mem, km_scratch, kvc, cross, total;
+  size_t qlow, klow, sel, lse, cent, assign, csr_off, csr_mem, km_scratch, kvc, rep, cross, total;
 };
+
+// Block mode with a representative score: the key blocks' representatives.
+size_t rep_bytes(const ha_layer_desc* d) {
+  if (d->n_clusters > 0 || d->block_score == 0) return 0;
+  return align_up(select_block_reps_scratch_bytes(n_qb_of(d), d->n_kv_heads, d->block_score));
+}
 
 // Cluster mode: K and V copied into CSR order for the selected-key kernels.
 size_t kvc_bytes(const ha_layer_desc* d) {
@@ -140,6 +148,8 @@ Layout layout_of(const ha_layer_desc* d, const Heads& h) {
            : 0;
   L.kvc = off;
   off += Hret ? kvc_bytes(d) : 0;
+  L.rep = off;
+  off += Hret ? rep_bytes(d) : 0;
   L.cross = off;
   off += cross_ws_bytes(d);
   L.total = off;
@@ -271,7 +281,7 @@ void fill_units(const ha_layer_desc* d, const Heads& h, SelectParams* sp) {
 }
 
 int run_select_blocks(const ha_layer_desc* d, const Heads& h, const float* qlow, const float* klow,
-                      int32_t* sel, hipStream_t s) {
+                      int32_t* sel, void* rep, hipStream_t s) {
   const int G = d->n_q_heads / d->n_kv_heads;
   SelectParams sp{};
   sp.qlow = qlow;
@@ -285,7 +295,14 @@ int run_select_blocks(const ha_layer_desc* d, const Heads& h, const float* qlow,
   sp.n_ret = (int)h.ret.size();
   for (int t = 0; t < sp.n_ret; ++t) sp.group_of_ret[t] = h.ret[t] / G;
   fill_units(d, h, &sp);
-  return dev_status(launch_select_blocks(sp, s));
+  if (d->block_score == 0) return dev_status(launch_select_blocks(sp, s));
+  // representatives: scored like centroids, candidate m = key block m
+  const size_t nparts = (size_t)d->n_kv_heads * sp.n_qb * kRank * (d->block_score == 2 ? 2 : 1);
+  sp.M = sp.n_qb;
+  sp.c_hi = static_cast<__bf16*>(rep);
+  sp.c_lo = sp.c_hi + nparts;
+  sp.first_mem = reinterpret_cast<int32_t*>(sp.c_lo + nparts);
+  return dev_status(launch_select_block_reps(sp, d->n_kv_heads, d->block_score, s));
 }
 
 // Retrieval heads: the window part through the banded kernel (which also
@@ -461,7 +478,7 @@ int ha_prefill(const ha_layer_desc* desc, const int32_t* head_kind, const void* 
       off = co;
       mem = cm;
     } else {
-      st = run_select_blocks(desc, h, qlow, klow, sel, s);
+      st = run_select_blocks(desc, h, qlow, klow, sel, ws_at(workspace, L.rep), s);
       if (st != HA_OK) return st;
     }
     st = run_gather(desc, head_kind, h, Q, K, V, sel, off, mem, O, reinterpret_cast<float*>(ws_at(workspace, L.lse)),
@@ -490,13 +507,14 @@ int ha_index_project(const ha_layer_desc* desc, const int32_t* head_kind, const 
 }
 
 int ha_select_blocks(const ha_layer_desc* desc, const int32_t* head_kind, const float* qlow, const float* klow,
-                     int32_t* sel, void* stream) {
+                     int32_t* sel, void* workspace, size_t ws_bytes, void* stream) {
   Heads h;
   int st = check_desc(desc, head_kind, &h);
   if (st != HA_OK) return st;
   if (h.ret.empty() || desc->n_clusters != 0) return HA_ERR_ARG;
   if (!qlow || !klow || !sel) return HA_ERR_ARG;
-  return run_select_blocks(desc, h, qlow, klow, sel, static_cast<hipStream_t>(stream));
+  if (!ws_ok(workspace, ws_bytes, rep_bytes(desc))) return HA_ERR_WORKSPACE;
+  return run_select_blocks(desc, h, qlow, klow, sel, workspace, static_cast<hipStream_t>(stream));
 }
 
 int ha_kmeans(const ha_layer_desc* desc, const float* klow, float* centroids, int32_t* assign, int32_t* csr_off,

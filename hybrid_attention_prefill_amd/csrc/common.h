@@ -91,9 +91,9 @@ struct SelectParams {
   const int32_t* csr_off;  // [Hkv, M+1]
   const int32_t* csr_mem;  // [Hkv, N]
   int32_t* sel;        // [Hret, n_qb, topk]
-  __bf16* c_hi;        // cluster mode scratch: [Hkv, M, r] split centroids
+  __bf16* c_hi;        // scratch: [Hkv, M, parts * r] split centroids / block representatives
   __bf16* c_lo;
-  int32_t* first_mem;  // [Hkv, M] smallest member position (INT_MAX if empty)
+  int32_t* first_mem;  // [Hkv, M] smallest member position (INT_MAX if empty or not a candidate)
   int N, n_qb, window, topk, force_block0, M;
   int n_ret;
   int32_t group_of_ret[kMaxHeads];
@@ -123,6 +123,11 @@ size_t kmeans_scratch_bytes(int N, int M, int Hkv);
 hipError_t launch_kmeans(KmeansParams p, int Hkv, int iters, hipStream_t s);
 hipError_t launch_select_clusters(const SelectParams& p, int Hkv, hipStream_t s);
 size_t select_clusters_scratch_bytes(int M, int Hkv);
+// Block mode with a representative score (mode 1 mean key, 2 per-dimension
+// extremes): representatives of the M = n_kb key blocks into c_hi / c_lo /
+// first_mem, then the cluster-scoring kernel over them.
+hipError_t launch_select_block_reps(const SelectParams& p, int Hkv, int mode, hipStream_t s);
+size_t select_block_reps_scratch_bytes(int n_kb, int Hkv, int mode);
 
 // Orthros cross-attention rows: flash attention of q' = q * s + o over keys
 // 0..p on the matrix cores (q' split into two bf16 parts), packs of 4 heads

@@ -313,6 +313,38 @@ __global__ __launch_bounds__(NT) void cluster_prep_kernel(SelectParams p) {
   p.first_mem[(size_t)g * p.M + m] = hi_i > lo_i ? p.csr_mem[(size_t)g * p.N + lo_i] : INT_MAX;
 }
 
+// Per layer, once, for block mode with a representative score: each key
+// block's representative (NPART 1: the mean of its low-rank keys; NPART 2:
+// the per-dimension maxima as part 0 and minima as part 1) split into bf16
+// hi/lo parts, and its first key as the "first member" (INT_MAX for block 0
+// when it is attended anyway).  One thread per (block, dimension).
+template <int NPART>
+__global__ __launch_bounds__(NT) void block_prep_kernel(SelectParams p) {
+  const int g = blockIdx.y;
+  const int t = blockIdx.x * NT + threadIdx.x;
+  const int c = t / R, d = t % R;
+  if (c >= p.M) return;
+  const int j0 = c * kBlock, j1 = min(p.N, j0 + kBlock);
+  const float* kl = p.klow + (size_t)g * p.N * R + d;
+  __bf16* hi = p.c_hi + ((size_t)g * p.M + c) * R * NPART;
+  __bf16* lo = p.c_lo + ((size_t)g * p.M + c) * R * NPART;
+  if (NPART == 1) {
+    float s = 0.f;
+    for (int j = j0; j < j1; ++j) s += kl[(size_t)j * R];
+    dev::split2(s / (float)(j1 - j0), hi[d], lo[d]);
+  } else {
+    float a = -__builtin_inff(), b = __builtin_inff();
+    for (int j = j0; j < j1; ++j) {
+      const float v = kl[(size_t)j * R];
+      a = fmaxf(a, v);
+      b = fminf(b, v);
+    }
+    dev::split2(a, hi[d], lo[d]);
+    dev::split2(b, hi[R + d], lo[R + d]);
+  }
+  if (d == 0) p.first_mem[(size_t)g * p.M + c] = (p.force_block0 && c == 0) ? INT_MAX : j0;
+}
+
 // One workgroup per (retrieval head, query block).  S[i][m] = qlow_i . C_m on
 // MFMA (32 rows x 32 centroids per instruction, k = r = 16), split operands;
 // a lane ends with 16 rows of one centroid, so the row max is a lane-local
@@ -332,10 +364,18 @@ __global__ __launch_bounds__(NT) void cluster_prep_kernel(SelectParams p) {
 // each slot and keeps the max key per cluster (the order key is monotone);
 // a lane owns the same clusters for every slot, so the lane maxima and the
 // prefilter hold for the max scores as they do for one slot.
+//
+// The same kernel scores key-block representatives (block mode with a
+// representative score): candidate m = key block m, "first member" = its
+// first key.  NPART = 2 scores the per-dimension extremes bound as a 32-dim
+// dot product: sum_d max(q_d a_d, q_d b_d) with a >= b equals
+// max(q, 0) . a + min(q, 0) . b, so part 0 pairs max(q, 0) with the block
+// maxima and part 1 pairs min(q, 0) with the minima.
 constexpr int kSelBlocks = 1;
 constexpr int kGroups = 128;      // scoring lanes (4 waves x 32)
 constexpr int kCapW = 192;        // candidate slots per wave
 
+template <int NPART>
 __global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
   static_assert(kSelBlocks == 1, "the prefilter handles one query block per workgroup");
   __shared__ uint32_t keys[kSelBlocks][kMaxSelCand];
@@ -365,31 +405,33 @@ __global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
     nrow[bi] = bi < nb ? min(kBlock, p.N - qs0) : 0;
     lim[bi] = bi < nb ? qs0 + nrow[bi] - 1 - p.window : -1;
   }
-  // split query rows of slot t; rows past the end of a ragged last block
-  // repeat the block's first row, so the row max needs no mask
-  dev::bf16x8 qh[kSelBlocks][2], ql[kSelBlocks][2];
+  // split query rows of slot t (parts as above); rows past the end of a
+  // ragged last block repeat the block's first row, so the row max needs no
+  // mask
+  dev::bf16x8 qh[NPART][2], ql[NPART][2];
   auto load_q = [&](int t) {
+    const int qs0 = b0 * kBlock;
 #pragma unroll
-    for (int bi = 0; bi < kSelBlocks; ++bi) {
-      const int qs0 = (b0 + bi) * kBlock;
+    for (int rt = 0; rt < 2; ++rt) {
+      const int i = rt * 32 + lr;
+      const int row = nb > 0 ? qs0 + (i < nrow[0] ? i : 0) : 0;
+      const float* qp = p.qlow + ((size_t)t * p.N + row) * R + lh * 8;
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        const int i = rt * 32 + lr;
-        const int row = bi < nb ? qs0 + (i < nrow[bi] ? i : 0) : 0;
-        const float* qp = p.qlow + ((size_t)t * p.N + row) * R + lh * 8;
+      for (int e = 0; e < 8; ++e) {
+        const float v = qp[e];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float v = qp[e];
+        for (int part = 0; part < NPART; ++part) {
+          const float vp = NPART == 1 ? v : (part == 0 ? fmaxf(v, 0.f) : fminf(v, 0.f));
           __bf16 hh, ll;
-          dev::split2(v, hh, ll);
-          qh[bi][rt][e] = hh;
-          ql[bi][rt][e] = ll;
+          dev::split2(vp, hh, ll);
+          qh[part][rt][e] = hh;
+          ql[part][rt][e] = ll;
         }
       }
     }
   };
-  const __bf16* chi = p.c_hi + (size_t)g * p.M * R;
-  const __bf16* clo = p.c_lo + (size_t)g * p.M * R;
+  const __bf16* chi = p.c_hi + (size_t)g * p.M * R * NPART;
+  const __bf16* clo = p.c_lo + (size_t)g * p.M * R * NPART;
   const int32_t* fm = p.first_mem + (size_t)g * p.M;
   // eligibility bitmask (cluster m has a member <= lim), from coalesced reads
   // of the first members, one ballot per 64 clusters
@@ -412,12 +454,15 @@ __global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
   // A wave's tiles are x = wave + 4 i.  Operands are loaded kPre tiles ahead
   // (register ring, static slots: the loop is unrolled by kPre).
   constexpr int kPre = 4;
-  auto ld = [&](int x, dev::bf16x8& bh, dev::bf16x8& bl) {
+  auto ld = [&](int x, dev::bf16x8 (&bh)[NPART], dev::bf16x8 (&bl)[NPART]) {
     const int m = min(p.M - 1, x * 32 + lr);
-    bh = *reinterpret_cast<const dev::bf16x8*>(chi + (size_t)m * R + lh * 8);
-    bl = *reinterpret_cast<const dev::bf16x8*>(clo + (size_t)m * R + lh * 8);
+#pragma unroll
+    for (int part = 0; part < NPART; ++part) {
+      bh[part] = *reinterpret_cast<const dev::bf16x8*>(chi + ((size_t)m * NPART + part) * R + lh * 8);
+      bl[part] = *reinterpret_cast<const dev::bf16x8*>(clo + ((size_t)m * NPART + part) * R + lh * 8);
+    }
   };
-  dev::bf16x8 rbh[kPre], rbl[kPre];
+  dev::bf16x8 rbh[kPre][NPART], rbl[kPre][NPART];
   for (int s = 0; s < ns; ++s) {
     load_q(t0 + s);
     // slot order, as in the loop body, so the first group waits only for its own slot
@@ -440,9 +485,12 @@ __global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
           dev::f32x16 acc = {};
-          acc = dev::mfma32(ql[0][rt], rbh[u], acc);
-          acc = dev::mfma32(qh[0][rt], rbl[u], acc);
-          acc = dev::mfma32(qh[0][rt], rbh[u], acc);
+#pragma unroll
+          for (int part = 0; part < NPART; ++part) {
+            acc = dev::mfma32(ql[part][rt], rbh[u][part], acc);
+            acc = dev::mfma32(qh[part][rt], rbl[u][part], acc);
+            acc = dev::mfma32(qh[part][rt], rbh[u][part], acc);
+          }
 #pragma unroll
           for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[e]);
         }
@@ -561,13 +609,31 @@ hipError_t launch_kmeans(KmeansParams p, int Hkv, int iters, hipStream_t s) {
 hipError_t launch_select_clusters(const SelectParams& p, int Hkv, hipStream_t s) {
   if (p.n_ret == 0 || p.n_qb == 0) return hipSuccess;
   hipLaunchKernelGGL(cluster_prep_kernel, dim3((p.M + NT - 1) / NT, Hkv), dim3(NT), 0, s, p);
-  hipLaunchKernelGGL(select_clusters_kernel, dim3((p.n_qb + kSelBlocks - 1) / kSelBlocks, p.n_units), dim3(NT),
+  hipLaunchKernelGGL(select_clusters_kernel<1>, dim3((p.n_qb + kSelBlocks - 1) / kSelBlocks, p.n_units), dim3(NT),
                      0, s, p);
   return hipGetLastError();
 }
 
 size_t select_clusters_scratch_bytes(int M, int Hkv) {
   return (size_t)Hkv * M * (2 * R * sizeof(__bf16) + sizeof(int32_t));
+}
+
+hipError_t launch_select_block_reps(const SelectParams& p, int Hkv, int mode, hipStream_t s) {
+  if (p.n_units == 0 || p.n_qb == 0) return hipSuccess;
+  const dim3 prep((p.M * R + NT - 1) / NT, Hkv), grid((p.n_qb + kSelBlocks - 1) / kSelBlocks, p.n_units);
+  if (mode == 2) {
+    hipLaunchKernelGGL(block_prep_kernel<2>, prep, dim3(NT), 0, s, p);
+    hipLaunchKernelGGL(select_clusters_kernel<2>, grid, dim3(NT), 0, s, p);
+  } else {
+    hipLaunchKernelGGL(block_prep_kernel<1>, prep, dim3(NT), 0, s, p);
+    hipLaunchKernelGGL(select_clusters_kernel<1>, grid, dim3(NT), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+size_t select_block_reps_scratch_bytes(int n_kb, int Hkv, int mode) {
+  const size_t npart = mode == 2 ? 2 : 1;
+  return (size_t)Hkv * n_kb * (2 * R * npart * sizeof(__bf16) + sizeof(int32_t));
 }
 
 }  // namespace ha

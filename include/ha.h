@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define HA_VERSION 2
+#define HA_VERSION 3
 
 typedef enum {
   HA_SWA = 0,        /* causal sliding window: keys i-w < j <= i */
@@ -94,6 +94,17 @@ typedef struct {
                           *    (36kr interview, GQA answer: the queries of one GQA
                           *    group share their keys); every retrieval head's row
                           *    of `sel` then holds its group's selection */
+  int32_t block_score;   /* block mode only (0 when n_clusters > 0): the score of
+                          * candidate key block c for query block b
+                          * 0: max over causal (i, j) of qlow_i . klow_j
+                          * 1: max_i qlow_i . (mean of the block's klow)
+                          * 2: max_i sum_d max(q_id kmax_cd, q_id kmin_cd), kmax /
+                          *    kmin the block's per-dimension key extremes (an
+                          *    upper bound on every key's dot product)
+                          *    (36kr interview, top-k matching answer: a block is
+                          *    represented by its mean key or by a point built
+                          *    from per-dimension extremes; both representatives
+                          *    ignore causality inside the block) */
 } ha_layer_desc;
 
 /* Optional copies of the indexer's intermediate results (caller-owned device
@@ -147,11 +158,15 @@ int ha_index_project(const ha_layer_desc* desc, const int32_t* head_kind,
 
 /* Stage: block scoring + top-k (RTPurbo scout; TriangleMix interview top-k).
  * For retrieval head t and query block b: eligible blocks c >= force_block0
- * with c*k_block <= qe_b - window; score = max over causal (i, j) of
- * qlow_i . klow_j; keeps the topk best by (score desc, block asc).
- *   sel  int32 [Hret, n_qb, topk], ascending, -1 padded. */
+ * with c*k_block <= qe_b - window; score as desc->block_score says; keeps the
+ * topk best by (score desc, block asc).
+ *   sel  int32 [Hret, n_qb, topk], ascending, -1 padded.
+ *   workspace  block_score 1 or 2: >= ha_workspace_bytes(desc, head_kind)
+ *              bytes, 256-byte aligned (the block representatives); may be
+ *              NULL with ws_bytes 0 when block_score = 0. */
 int ha_select_blocks(const ha_layer_desc* desc, const int32_t* head_kind,
-                     const float* qlow, const float* klow, int32_t* sel, void* stream);
+                     const float* qlow, const float* klow, int32_t* sel,
+                     void* workspace, size_t ws_bytes, void* stream);
 
 /* Stage: Lloyd k-means of klow per KV head (RTPurboV2 clustering passage).
  * M = n_clusters, kmeans_iters iterations, C0_m = klow_{m*stride}; ties go to

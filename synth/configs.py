@@ -117,6 +117,11 @@ ORTHROS_8B_128K = Workload(
 # length is this suite's choice; the pages give none.
 ORTHROS_8B_128K_SFT = ORTHROS_8B_128K.with_(name="orthros_8b_128k_sft8k", n_out=8192)
 
+# The 32K hybrid layer with the cheaper block scores: each key block scored by
+# its mean low-rank key, or by the bound from its per-dimension extremes.
+QWEN3_30B_32K_MEAN = QWEN3_30B_32K.with_(name="qwen3_30b_a3b_32k_mean", block_score=1)
+QWEN3_30B_32K_MINMAX = QWEN3_30B_32K.with_(name="qwen3_30b_a3b_32k_minmax", block_score=2)
+
 # 1M-token all-sparse layer: every head is a retrieval head, the low-rank keys
 # are clustered (16384 centroids, 10 Lloyd iterations, seeds every 64th key),
 # each query block takes its top-64 clusters plus a 4096 window.
@@ -134,7 +139,7 @@ ALLSPARSE_1M_GQA = ALLSPARSE_1M.with_(name="allsparse_1m_gqa", group_select=1)
 TRIANGLE_LAYER_SPLIT = (12, 20)
 
 WORKLOADS = {w.name: w for w in (
-    TINY_HYBRID_2K, QWEN3_30B_32K, TRIANGLE_8B_128K, DENSE_8B_128K,
+    TINY_HYBRID_2K, QWEN3_30B_32K, QWEN3_30B_32K_MEAN, QWEN3_30B_32K_MINMAX, TRIANGLE_8B_128K, DENSE_8B_128K,
     ORTHROS_8B_128K, ORTHROS_8B_128K_SFT, ALLSPARSE_1M, ALLSPARSE_1M_GQA)}
 
 

@@ -23,7 +23,7 @@ def test_header_and_binding_agree_and_library_exports_all():
     L = ha.lib()
     for name in decl:
         assert hasattr(L, name), name
-    assert L.ha_version() == 2
+    assert L.ha_version() == 3
 
 
 def test_status_strings():
@@ -135,7 +135,12 @@ def test_stage_argument_checks():
     kinds = ha._kinds([1, 1] + [0] * 6)
     assert L.ha_index_project(ctypes.byref(d), kinds, FAKE, FAKE, None, FAKE, FAKE, None) == ha.HA_ERR_ARG
     assert L.ha_index_project(ctypes.byref(d), ha._kinds([0] * 8), FAKE, FAKE, FAKE, FAKE, FAKE, None) == ha.HA_ERR_ARG
-    assert L.ha_select_blocks(ctypes.byref(d), kinds, FAKE, None, FAKE, None) == ha.HA_ERR_ARG
+    assert L.ha_select_blocks(ctypes.byref(d), kinds, FAKE, None, FAKE, None, 0, None) == ha.HA_ERR_ARG
+    # block representatives need their workspace
+    d_rep = _desc(topk=8, block_score=1)
+    assert L.ha_select_blocks(ctypes.byref(d_rep), kinds, FAKE, FAKE, FAKE, None, 0, None) == ha.HA_ERR_WORKSPACE
+    assert L.ha_select_blocks(ctypes.byref(_desc(topk=8, block_score=3)), kinds, FAKE, FAKE, FAKE, None, 0,
+                              None) == ha.HA_ERR_ARG
     assert L.ha_attn_gather(ctypes.byref(d), kinds, FAKE, FAKE, FAKE, None, None, None, FAKE, None, 0, None) == ha.HA_ERR_ARG
     dc = _desc(n_out=1)
     assert L.ha_attn_cross(ctypes.byref(dc), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == ha.HA_ERR_WORKSPACE

@@ -72,6 +72,35 @@ def test_qwen3_30b_layer_32k_group_select():
     _run("qwen3_30b_a3b_32k", group_select=1)
 
 
+@pytest.mark.parametrize("name", ["qwen3_30b_a3b_32k_mean", "qwen3_30b_a3b_32k_minmax"])
+def test_qwen3_30b_layer_32k_block_representatives(name):
+    _run(name)
+
+
+def test_block_representative_selection_agreement_32k():
+    """Informational: how many of the max-pair selection's blocks the cheaper
+    scores keep on the 32K layer (printed, not graded: the scores differ by
+    design)."""
+    import torch
+    w0 = synth.WORKLOADS["qwen3_30b_a3b_32k"]
+    li = synth.make_layer_inputs(w0)
+    sels = {}
+    for name in ("qwen3_30b_a3b_32k", "qwen3_30b_a3b_32k_mean", "qwen3_30b_a3b_32k_minmax"):
+        w = synth.WORKLOADS[name]
+        _, _, aux = _gpu.run_gpu(w, li)
+        sels[w.block_score] = aux["sel"].cpu().numpy()
+    base = sels[0]
+    for m in (1, 2):
+        kept = tot = 0
+        for t in range(base.shape[0]):
+            for b in range(base.shape[1]):
+                a = set(int(x) for x in base[t, b] if x >= 0)
+                kept += len(a & set(int(x) for x in sels[m][t, b] if x >= 0))
+                tot += len(a)
+        print(f"block_score {m}: keeps {kept / max(tot, 1):.3f} of the max-pair selection ({tot} selected blocks)")
+        assert tot > 0
+
+
 def test_trianglemix_layer_128k():
     w = synth.WORKLOADS["trianglemix_llama8b_128k"]
     _run("trianglemix_llama8b_128k", heads=list(range(0, 32, 3)),

@@ -89,6 +89,15 @@ def test_group_select_block_mode(N, window, topk, f0):
     _compare(_layer(kinds, N, window=window, topk=topk, force_block0=f0, group_select=1))
 
 
+@pytest.mark.parametrize("score", [1, 2])
+@pytest.mark.parametrize("N,window,topk,f0,gs", [(1000, 100, 3, 0, 0), (1337, 64, 8, 1, 0), (700, 1, 2, 0, 0),
+                                                 (640, 50, 100, 0, 0), (300, 5000, 4, 1, 0), (1000, 100, 3, 1, 1)])
+def test_block_representative_scores(score, N, window, topk, f0, gs):
+    kinds = [HEAD_RETRIEVAL, HEAD_SWA, HEAD_RETRIEVAL, HEAD_RETRIEVAL, HEAD_SWA, HEAD_RETRIEVAL, HEAD_RETRIEVAL,
+             HEAD_RETRIEVAL]
+    _compare(_layer(kinds, N, window=window, topk=topk, force_block0=f0, group_select=gs, block_score=score))
+
+
 def test_group_select_pack_shapes():
     # G = 8, all retrieval: two full packs per group
     _compare(_layer([HEAD_RETRIEVAL] * 16, 900, Hkv=2, window=70, topk=4, group_select=1))
@@ -134,11 +143,13 @@ def test_deterministic_rerun():
     assert torch.equal(a[2]["sel"], b[2]["sel"])
 
 
+@pytest.mark.parametrize("score", [0, 1, 2])
 @pytest.mark.parametrize("f0", [0, 1])
-def test_block_selection_exact_ties_keep_lowest_ids(f0):
+def test_block_selection_exact_ties_keep_lowest_ids(f0, score):
     # every key block holds the same low-rank keys and the window (128) keeps
-    # every eligible pair causal, so all eligible blocks score exactly alike:
-    # the selection must be the k lowest eligible block ids
+    # every eligible pair causal, so all eligible blocks score exactly alike
+    # (pairs, means and extremes alike): the selection must be the k lowest
+    # eligible block ids
     import torch
     import hybrid_attention_prefill_amd as ha
     N, k, w = 4096, 5, 128
@@ -146,11 +157,12 @@ def test_block_selection_exact_ties_keep_lowest_ids(f0):
     kl = np.tile(rng.standard_normal((64, 16)).astype(np.float32), (N // 64, 1))
     ql = rng.standard_normal((N, 16)).astype(np.float32)
     kinds = [HEAD_RETRIEVAL] + [HEAD_SWA] * 3
-    d = ha.make_desc(N, 4, 1, 128, window=w, topk=k, force_block0=f0)
+    d = ha.make_desc(N, 4, 1, 128, window=w, topk=k, force_block0=f0, block_score=score)
     klow = torch.from_numpy(kl[None]).cuda()
     qlow = torch.from_numpy(ql[None]).cuda()
     sel = torch.full((1, N // 64, k), -7, dtype=torch.int32, device="cuda")
-    ha.ha_select_blocks(d, kinds, qlow, klow, sel)
+    ws = torch.empty(max(256, ha.ha_workspace_bytes(d, kinds)), dtype=torch.uint8, device="cuda")
+    ha.ha_select_blocks(d, kinds, qlow, klow, sel, ws)
     torch.cuda.synchronize()
     sel = sel.cpu().numpy()[0]
     for b in range(N // 64):
