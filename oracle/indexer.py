@@ -28,6 +28,13 @@ With the block's keys K_c = {j in block c, j < N}:
            product any point of the box spanned by the block's keys can
            reach, so it bounds every key's score from above.
 Causality inside a block is not applied by either representative.
+
+8-bit indexer ([p5] hybrid-attention article, mixed-precision index: the
+indexer is stored in 8 bits): each low-rank key is kept as int8 codes with
+one fp32 scale, scale_j = max_d |k_jd| / 127 and code_jd = k_jd / scale_j
+rounded to nearest (ties to even); block scores use the dequantized keys
+scale_j * code_j.  The float-to-integer step is taken in fp32, as the
+kernel takes it.
 """
 from __future__ import annotations
 
@@ -94,6 +101,24 @@ def block_scores_minmax(qlow_rows: np.ndarray, kmax: np.ndarray, kmin: np.ndarra
     q = qlow_rows[:, None, :]                                   # [rows, 1, r]
     bound = np.maximum(q * kmax[blocks][None], q * kmin[blocks][None]).sum(axis=2)
     return np.max(bound, axis=0)
+
+
+def quantize_keys_int8(klow32: np.ndarray):
+    """Per-key symmetric 8-bit codes [n, r] int8 and scales [n] fp32, computed
+    in fp32 (IEEE division, round half to even); an all-zero key gets scale 0
+    and zero codes."""
+    k = np.asarray(klow32, dtype=np.float32)
+    amax = np.max(np.abs(k), axis=1)
+    scale = (amax / np.float32(127.0)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    codes = np.rint(k / safe[:, None])
+    codes = np.where(scale[:, None] > 0, codes, 0.0)
+    return codes.astype(np.int8), scale
+
+
+def dequantize_keys(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """scale_j * code_j in fp64."""
+    return codes.astype(np.float64) * np.asarray(scale, dtype=np.float64)[:, None]
 
 
 def topk_order(scores: np.ndarray, ids: np.ndarray, k: int) -> np.ndarray:

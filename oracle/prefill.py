@@ -33,7 +33,8 @@ import numpy as np
 
 from .attention import attend_rows, softmax_attention, visible_dense, visible_swa, visible_triangle
 from .indexer import (block_extremes, block_means, block_scores, block_scores_mean, block_scores_minmax,
-                      cluster_scores, eligible_blocks, eligible_clusters, project, topk_order)
+                      cluster_scores, dequantize_keys, eligible_blocks, eligible_clusters, project,
+                      quantize_keys_int8, topk_order)
 from .kmeans import lloyd
 
 SWA, RETRIEVAL, TRIANGLE, DENSE = 0, 1, 2, 3
@@ -93,6 +94,7 @@ class OracleResult:
     centroids: Dict[int, np.ndarray]
     assign: Dict[int, np.ndarray]
     out_rows: Optional[np.ndarray] = None  # output positions t (row N - n_out + t) held in O_out
+    kcodes: Optional[Dict[int, tuple]] = None  # 8-bit indexer: KV head -> (codes, scales)
 
 
 def orthros_cross(q: np.ndarray, s: np.ndarray, o: np.ndarray, K: np.ndarray,
@@ -111,6 +113,7 @@ def layer_prefill(w, q_rows: Callable[[int, int], np.ndarray], K: np.ndarray, V:
                   heads: Optional[Sequence[int]] = None,
                   sel_override: Optional[Dict[int, Dict[int, np.ndarray]]] = None,
                   kmeans_override: Optional[Dict[int, tuple]] = None,
+                  klow32_override: Optional[Dict[int, np.ndarray]] = None,
                   scale: Optional[float] = None,
                   with_out: bool = True,
                   out_rows: Optional[Sequence[int]] = None) -> OracleResult:
@@ -124,6 +127,9 @@ def layer_prefill(w, q_rows: Callable[[int, int], np.ndarray], K: np.ndarray, V:
     sel_override  head -> block -> selection to use instead of the oracle's own
                   (to grade attention given a validated GPU selection)
     kmeans_override  KV head -> (centroids, assign) to use instead of Lloyd
+    klow32_override  8-bit indexer: KV head -> fp32 low-rank keys to quantize
+                  (the GPU's, so the float-to-integer step is taken on the same
+                  fp32 values); default: the oracle's keys rounded to fp32
     out_rows   Orthros output positions t in [0, n_out) to compute (default: all)
     """
     N, Hq, Hkv, D = w.n_tokens, w.n_q_heads, w.n_kv_heads, w.head_dim
@@ -138,6 +144,7 @@ def layer_prefill(w, q_rows: Callable[[int, int], np.ndarray], K: np.ndarray, V:
     res = OracleResult(rows_all, O, None, {}, {}, {}, {}, {}, {})
 
     ret = [h for h in heads if w.head_kind[h] == RETRIEVAL]
+    rep_klow = {}        # 8-bit indexer: dequantized keys used for block scores
     for g in sorted({head_group(h, Hq, Hkv) for h in ret}):
         res.klow[g] = project(K[:, g], P[g])
         if w.n_clusters > 0:
@@ -148,6 +155,14 @@ def layer_prefill(w, q_rows: Callable[[int, int], np.ndarray], K: np.ndarray, V:
             else:
                 C, a, _ = lloyd(res.klow[g], w.n_clusters, w.kmeans_stride, w.kmeans_iters)
             res.centroids[g], res.assign[g] = C, a
+        elif w.index_bits == 8:
+            k32 = (klow32_override[g] if klow32_override is not None and g in klow32_override
+                   else res.klow[g].astype(np.float32))
+            codes, s = quantize_keys_int8(k32)
+            if res.kcodes is None:
+                res.kcodes = {}
+            res.kcodes[g] = (codes, s)
+            rep_klow[g] = dequantize_keys(codes, s)
 
     eligible_memo = {}   # (KV head, block) -> eligible clusters (shared by the group's heads)
     group_memo = {}      # (KV head, block) -> (eligible, group scores, selection)
@@ -178,7 +193,7 @@ def layer_prefill(w, q_rows: Callable[[int, int], np.ndarray], K: np.ndarray, V:
                 rep_memo[("ext", g)] = block_extremes(res.klow[g], Bk)
             kmax, kmin = rep_memo[("ext", g)]
             return ql, E, block_scores_minmax(ql, kmax, kmin, E)
-        return ql, E, block_scores(ql, rows, res.klow[g], E, Bk)
+        return ql, E, block_scores(ql, rows, rep_klow.get(g, res.klow[g]), E, Bk)
 
     off = 0
     for b in blocks:

@@ -49,6 +49,9 @@ class Workload:
     # 1 the block's mean key (representative), 2 the bound from the block's
     # per-dimension key maxima and minima
     block_score: int = 0
+    # low-rank key storage of the block scores: 0 fp32, 8 int8 codes with one
+    # fp32 scale per key (max-pair block scores only)
+    index_bits: int = 0
     # input recipe: "plain", "planted_lowfreq" (keys carry per-segment topic
     # vectors on the low-frequency dims), "needles" (planted key/query pairs)
     recipe: str = "plain"
@@ -76,7 +79,7 @@ class Workload:
             force_block0=self.force_block0, n_clusters=self.n_clusters,
             kmeans_iters=self.kmeans_iters, kmeans_stride=self.kmeans_stride,
             sink=self.sink, last_q=self.last_q, n_out=self.n_out,
-            group_select=self.group_select, block_score=self.block_score,
+            group_select=self.group_select, block_score=self.block_score, index_bits=self.index_bits,
         )
 
 
@@ -121,6 +124,8 @@ ORTHROS_8B_128K_SFT = ORTHROS_8B_128K.with_(name="orthros_8b_128k_sft8k", n_out=
 # its mean low-rank key, or by the bound from its per-dimension extremes.
 QWEN3_30B_32K_MEAN = QWEN3_30B_32K.with_(name="qwen3_30b_a3b_32k_mean", block_score=1)
 QWEN3_30B_32K_MINMAX = QWEN3_30B_32K.with_(name="qwen3_30b_a3b_32k_minmax", block_score=2)
+# ... and with the low-rank keys of the block scores stored as 8-bit codes
+QWEN3_30B_32K_INT8 = QWEN3_30B_32K.with_(name="qwen3_30b_a3b_32k_int8", index_bits=8)
 
 # 1M-token all-sparse layer: every head is a retrieval head, the low-rank keys
 # are clustered (16384 centroids, 10 Lloyd iterations, seeds every 64th key),
@@ -139,7 +144,8 @@ ALLSPARSE_1M_GQA = ALLSPARSE_1M.with_(name="allsparse_1m_gqa", group_select=1)
 TRIANGLE_LAYER_SPLIT = (12, 20)
 
 WORKLOADS = {w.name: w for w in (
-    TINY_HYBRID_2K, QWEN3_30B_32K, QWEN3_30B_32K_MEAN, QWEN3_30B_32K_MINMAX, TRIANGLE_8B_128K, DENSE_8B_128K,
+    TINY_HYBRID_2K, QWEN3_30B_32K, QWEN3_30B_32K_MEAN, QWEN3_30B_32K_MINMAX, QWEN3_30B_32K_INT8,
+    TRIANGLE_8B_128K, DENSE_8B_128K,
     ORTHROS_8B_128K, ORTHROS_8B_128K_SFT, ALLSPARSE_1M, ALLSPARSE_1M_GQA)}
 
 

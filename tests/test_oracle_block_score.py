@@ -117,3 +117,48 @@ def test_topk_all_is_dense_for_every_score():
     dense = layer_prefill(w.with_(head_kind=(3, 3)), q, K, V, P)
     for m in (1, 2):
         np.testing.assert_allclose(layer_prefill(w.with_(block_score=m), q, K, V, P).O, dense.O, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# 8-bit indexer keys
+
+from oracle.indexer import dequantize_keys, quantize_keys_int8  # noqa: E402
+
+
+def test_quantize_hand_worked_codes():
+    # max |k| = 127 -> scale exactly 1: the codes are the keys rounded to
+    # nearest with ties to even (0.5 -> 0, 1.5 -> 2, -2.5 -> -2)
+    k = np.zeros((2, 16), dtype=np.float32)
+    k[0, :6] = [127.0, -3.4, 2.6, 0.5, 1.5, -2.5]
+    codes, s = quantize_keys_int8(k)
+    assert s[0] == np.float32(1.0)
+    assert list(codes[0, :6]) == [127, -3, 3, 0, 2, -2]
+    assert s[1] == 0.0 and not codes[1].any()        # an all-zero key
+
+
+def test_quantize_bounds_and_round_trip():
+    rng = np.random.default_rng(7)
+    k = (rng.standard_normal((500, 16)) * rng.uniform(0.01, 30, (500, 1))).astype(np.float32)
+    codes, s = quantize_keys_int8(k)
+    assert codes.dtype == np.int8 and np.abs(codes.astype(int)).max() <= 127
+    assert np.all(np.abs(codes.astype(int)).max(axis=1) == 127)   # the largest component maps to +-127
+    err = np.abs(dequantize_keys(codes, s) - k.astype(np.float64))
+    assert np.all(err <= s[:, None].astype(np.float64) * 0.5000001 + 1e-12)
+
+
+def test_int8_scores_use_the_dequantized_keys():
+    # the layer's block scores with 8-bit keys are the max-pair scores of the
+    # dequantized keys; exactly representable keys (scale 1) change nothing
+    w = Workload(name="q8", n_tokens=512, n_q_heads=2, n_kv_heads=1, head_dim=D,
+                 head_kind=(HEAD_RETRIEVAL, HEAD_SWA), window=64, topk=2)
+    q, K, V, P, _, _ = oracle_arrays(w)
+    r = layer_prefill(w.with_(index_bits=8), q, K, V, P)
+    codes, s = r.kcodes[0]
+    kq = dequantize_keys(codes, s)
+    for b, (E, sc) in r.scored[0].items():
+        rows = np.arange(b * 64, min(512, b * 64 + 64))
+        np.testing.assert_allclose(sc, block_scores(r.qlow[0][b], rows, kq, E, 64), atol=1e-12)
+    qf, Kf, Vf, Pf = _fixture()
+    a = layer_prefill(_w(), qf, Kf, Vf, Pf)
+    b8 = layer_prefill(_w(index_bits=8), qf, Kf, Vf, Pf)
+    np.testing.assert_array_equal(a.O, b8.O)
