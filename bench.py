@@ -171,7 +171,8 @@ class Layer:
         self.desc = ha.make_desc(N, Hq, Hkv, D, window=w.window, topk=w.topk, force_block0=w.force_block0,
                                  n_clusters=w.n_clusters, kmeans_iters=w.kmeans_iters,
                                  kmeans_stride=w.kmeans_stride, sink=w.sink, last_q=w.last_q, n_out=w.n_out,
-                                 group_select=w.group_select, block_score=w.block_score)
+                                 group_select=w.group_select, block_score=w.block_score,
+                                 index_bits=w.index_bits)
         self.kinds = list(w.head_kind)
         self.O = torch.empty((N, Hq, D), dtype=torch.float32, device=dev)
         self.O_out = torch.empty((w.n_out, Hq, D), dtype=torch.float32, device=dev) if w.n_out else None

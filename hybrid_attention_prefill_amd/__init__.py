@@ -23,7 +23,7 @@ HA_SWA, HA_RETRIEVAL, HA_TRIANGLE, HA_DENSE = 0, 1, 2, 3
 HA_OK, HA_ERR_ARG, HA_ERR_UNSUPPORTED, HA_ERR_WORKSPACE, HA_ERR_DEVICE = range(5)
 
 EXPORTS = ("ha_status_string", "ha_version", "ha_workspace_bytes", "ha_prefill",
-           "ha_index_project", "ha_select_blocks", "ha_kmeans", "ha_select_clusters",
+           "ha_index_project", "ha_select_blocks", "ha_quantize_keys", "ha_kmeans", "ha_select_clusters",
            "ha_attn_band", "ha_attn_gather", "ha_attn_cross")
 
 
@@ -37,7 +37,7 @@ class LayerDesc(ctypes.Structure):
         ("n_clusters", ctypes.c_int32), ("kmeans_iters", ctypes.c_int32),
         ("kmeans_stride", ctypes.c_int32), ("sink", ctypes.c_int32),
         ("last_q", ctypes.c_int32), ("n_out", ctypes.c_int32),
-        ("group_select", ctypes.c_int32), ("block_score", ctypes.c_int32),
+        ("group_select", ctypes.c_int32), ("block_score", ctypes.c_int32), ("index_bits", ctypes.c_int32),
     ]
 
 
@@ -78,6 +78,8 @@ def lib():
         L.ha_index_project.argtypes = [dp, i32p, vp, vp, vp, vp, vp, vp]
         L.ha_select_blocks.restype = ctypes.c_int
         L.ha_select_blocks.argtypes = [dp, i32p, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.ha_quantize_keys.restype = ctypes.c_int
+        L.ha_quantize_keys.argtypes = [dp, vp, vp, vp, vp]
         L.ha_kmeans.restype = ctypes.c_int
         L.ha_kmeans.argtypes = [dp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.ha_select_clusters.restype = ctypes.c_int
@@ -127,10 +129,11 @@ def _stream(stream) -> Optional[int]:
 
 def make_desc(n_tokens, n_q_heads, n_kv_heads, head_dim=128, *, softmax_scale=0.0, window=0, rank=16,
               q_block=64, k_block=64, topk=0, force_block0=0, n_clusters=0, kmeans_iters=0,
-              kmeans_stride=0, sink=0, last_q=0, n_out=0, group_select=0, block_score=0) -> LayerDesc:
+              kmeans_stride=0, sink=0, last_q=0, n_out=0, group_select=0, block_score=0,
+              index_bits=0) -> LayerDesc:
     return LayerDesc(n_tokens, n_q_heads, n_kv_heads, head_dim, float(softmax_scale or 0.0), window, rank,
                      q_block, k_block, topk, int(force_block0), n_clusters, kmeans_iters, kmeans_stride,
-                     sink, last_q, n_out, int(group_select), int(block_score))
+                     sink, last_q, n_out, int(group_select), int(block_score), int(index_bits))
 
 
 def _kinds(head_kind: Sequence[int]):
@@ -165,6 +168,10 @@ def ha_select_blocks(desc, head_kind, qlow, klow, sel, workspace=None, ws_bytes=
         ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().ha_select_blocks(ctypes.byref(desc), _kinds(head_kind), _ptr(qlow), _ptr(klow), _ptr(sel),
                                   _ptr(workspace), int(ws_bytes), _stream(stream)))
+
+
+def ha_quantize_keys(desc, klow, codes, scales, stream=None):
+    _check(lib().ha_quantize_keys(ctypes.byref(desc), _ptr(klow), _ptr(codes), _ptr(scales), _stream(stream)))
 
 
 def ha_kmeans(desc, klow, centroids, assign, csr_off, csr_mem, workspace=None, ws_bytes=None, stream=None):
@@ -212,8 +219,8 @@ def ha_attn_cross(desc, Q, K, V, xa_scale, xa_offset, O_out, workspace=None, ws_
 
 def hybrid_attn_prefill(Q, K, V, head_kind, window, P_idx=None, topk=0, block=64, *, force_block0=False,
                         n_clusters=0, kmeans_iters=10, kmeans_stride=64, sink=0, last_q=0, n_out=0,
-                        group_select=False, block_score=0, xa_scale=None, xa_offset=None, softmax_scale=None,
-                        out=None, out_cross=None, workspace=None, return_aux=False):
+                        group_select=False, block_score=0, index_bits=0, xa_scale=None, xa_offset=None,
+                        softmax_scale=None, out=None, out_cross=None, workspace=None, return_aux=False):
     """One layer's hybrid attention prefill on the current HIP stream.
 
     Q [N, Hq, D], K/V [N, Hkv, D] bf16 CUDA tensors; head_kind a sequence of
@@ -229,7 +236,8 @@ def hybrid_attn_prefill(Q, K, V, head_kind, window, P_idx=None, topk=0, block=64
                      q_block=block, k_block=block, force_block0=int(bool(force_block0)),
                      n_clusters=n_clusters, kmeans_iters=kmeans_iters if n_clusters else 0,
                      kmeans_stride=kmeans_stride if n_clusters else 0, sink=sink, last_q=last_q, n_out=n_out,
-                     group_select=int(bool(group_select)), block_score=int(block_score))
+                     group_select=int(bool(group_select)), block_score=int(block_score),
+                     index_bits=int(index_bits))
     dev = Q.device
     O = out if out is not None else torch.empty((N, Hq, D), dtype=torch.float32, device=dev)
     O_out = None

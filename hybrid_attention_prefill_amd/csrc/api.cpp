@@ -36,6 +36,9 @@ int check_desc(const ha_layer_desc* d, const int32_t* kinds, Heads* out) {
   if (d->group_select != 0 && d->group_select != 1) return HA_ERR_ARG;
   if (d->block_score < 0 || d->block_score > 2) return HA_ERR_ARG;
   if (d->block_score != 0 && d->n_clusters > 0) return HA_ERR_ARG;   // a block-mode option
+  if (d->index_bits != 0 && d->index_bits != 8 && d->index_bits != 32) return HA_ERR_ARG;
+  // 8-bit keys are built for the max-pair block scores
+  if (d->index_bits == 8 && (d->n_clusters > 0 || d->block_score != 0)) return HA_ERR_UNSUPPORTED;
   Heads h;
   h.ret_slot.assign(d->n_q_heads, -1);
   bool need_window = false, any_tri = false;
@@ -107,8 +110,15 @@ size_t cross_ws_bytes(const ha_layer_desc* d) {
 }
 
 struct Layout {
-  size_t qlow, klow, sel, lse, cent, assign, csr_off, csr_mem, km_scratch, kvc, rep, cross, total;
+  size_t qlow, klow, sel, lse, cent, assign, csr_off, csr_mem, km_scratch, kvc, rep, kq, cross, total;
 };
+
+// 8-bit indexer keys: int8 codes [Hkv, N, r] then fp32 scales [Hkv, N].
+size_t kq_bytes(const ha_layer_desc* d) {
+  if (d->index_bits != 8) return 0;
+  const size_t rows = (size_t)d->n_kv_heads * d->n_tokens;
+  return align_up(rows * kRank) + align_up(rows * sizeof(float));
+}
 
 // Block mode with a representative score: the key blocks' representatives.
 size_t rep_bytes(const ha_layer_desc* d) {
@@ -150,6 +160,8 @@ Layout layout_of(const ha_layer_desc* d, const Heads& h) {
   off += Hret ? kvc_bytes(d) : 0;
   L.rep = off;
   off += Hret ? rep_bytes(d) : 0;
+  L.kq = off;
+  off += Hret ? kq_bytes(d) : 0;
   L.cross = off;
   off += cross_ws_bytes(d);
   L.total = off;
@@ -281,7 +293,7 @@ void fill_units(const ha_layer_desc* d, const Heads& h, SelectParams* sp) {
 }
 
 int run_select_blocks(const ha_layer_desc* d, const Heads& h, const float* qlow, const float* klow,
-                      int32_t* sel, void* rep, hipStream_t s) {
+                      int32_t* sel, void* rep, void* kq, hipStream_t s) {
   const int G = d->n_q_heads / d->n_kv_heads;
   SelectParams sp{};
   sp.qlow = qlow;
@@ -295,6 +307,15 @@ int run_select_blocks(const ha_layer_desc* d, const Heads& h, const float* qlow,
   sp.n_ret = (int)h.ret.size();
   for (int t = 0; t < sp.n_ret; ++t) sp.group_of_ret[t] = h.ret[t] / G;
   fill_units(d, h, &sp);
+  if (d->index_bits == 8) {
+    const size_t rows = (size_t)d->n_kv_heads * d->n_tokens;
+    int8_t* codes = static_cast<int8_t*>(kq);
+    float* scales = reinterpret_cast<float*>(static_cast<char*>(kq) + align_up(rows * kRank));
+    const int st = dev_status(launch_quantize_keys(klow, codes, scales, rows, s));
+    if (st != HA_OK) return st;
+    sp.kcodes = codes;
+    sp.kscale = scales;
+  }
   if (d->block_score == 0) return dev_status(launch_select_blocks(sp, s));
   // representatives: scored like centroids, candidate m = key block m
   const size_t nparts = (size_t)d->n_kv_heads * sp.n_qb * kRank * (d->block_score == 2 ? 2 : 1);
@@ -478,7 +499,7 @@ int ha_prefill(const ha_layer_desc* desc, const int32_t* head_kind, const void* 
       off = co;
       mem = cm;
     } else {
-      st = run_select_blocks(desc, h, qlow, klow, sel, ws_at(workspace, L.rep), s);
+      st = run_select_blocks(desc, h, qlow, klow, sel, ws_at(workspace, L.rep), ws_at(workspace, L.kq), s);
       if (st != HA_OK) return st;
     }
     st = run_gather(desc, head_kind, h, Q, K, V, sel, off, mem, O, reinterpret_cast<float*>(ws_at(workspace, L.lse)),
@@ -513,8 +534,20 @@ int ha_select_blocks(const ha_layer_desc* desc, const int32_t* head_kind, const 
   if (st != HA_OK) return st;
   if (h.ret.empty() || desc->n_clusters != 0) return HA_ERR_ARG;
   if (!qlow || !klow || !sel) return HA_ERR_ARG;
-  if (!ws_ok(workspace, ws_bytes, rep_bytes(desc))) return HA_ERR_WORKSPACE;
-  return run_select_blocks(desc, h, qlow, klow, sel, workspace, static_cast<hipStream_t>(stream));
+  // representatives first, then the 8-bit keys
+  const size_t rb = rep_bytes(desc);
+  if (!ws_ok(workspace, ws_bytes, rb + kq_bytes(desc))) return HA_ERR_WORKSPACE;
+  return run_select_blocks(desc, h, qlow, klow, sel, workspace, ws_at(workspace, rb),
+                           static_cast<hipStream_t>(stream));
+}
+
+int ha_quantize_keys(const ha_layer_desc* desc, const float* klow, int8_t* codes, float* scales, void* stream) {
+  if (!desc) return HA_ERR_ARG;
+  if (desc->n_tokens < 1 || desc->n_kv_heads < 1) return HA_ERR_ARG;
+  if (desc->rank != kRank) return desc->rank < 1 ? HA_ERR_ARG : HA_ERR_UNSUPPORTED;
+  if (!klow || !codes || !scales) return HA_ERR_ARG;
+  return dev_status(launch_quantize_keys(klow, codes, scales, (size_t)desc->n_kv_heads * desc->n_tokens,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 int ha_kmeans(const ha_layer_desc* desc, const float* klow, float* centroids, int32_t* assign, int32_t* csr_off,

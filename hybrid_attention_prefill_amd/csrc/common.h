@@ -94,6 +94,8 @@ struct SelectParams {
   __bf16* c_hi;        // scratch: [Hkv, M, parts * r] split centroids / block representatives
   __bf16* c_lo;
   int32_t* first_mem;  // [Hkv, M] smallest member position (INT_MAX if empty or not a candidate)
+  const int8_t* kcodes;  // 8-bit indexer keys [Hkv, N, r] (nullptr: fp32 klow)
+  const float* kscale;   // [Hkv, N] their scales
   int N, n_qb, window, topk, force_block0, M;
   int n_ret;
   int32_t group_of_ret[kMaxHeads];
@@ -105,6 +107,8 @@ struct SelectParams {
   uint32_t unit[kMaxHeads];
 };
 hipError_t launch_select_blocks(const SelectParams& p, hipStream_t s);
+// 8-bit indexer keys from fp32 low-rank keys (n_rows rows of r values).
+hipError_t launch_quantize_keys(const float* klow, int8_t* codes, float* scales, size_t n_rows, hipStream_t s);
 
 struct KmeansParams {
   const float* klow;   // [Hkv, N, r]

@@ -126,7 +126,13 @@ __device__ __forceinline__ float wave_max(float v) {
 // per slot and keeps the max (the order key is monotone, so the max of keys
 // is the key of the max); a wave owns the same blocks for every slot.
 //
+// kInt8 (8-bit indexer keys): the keys are int8 codes (exact in bf16) with one
+// scale per key; S = Q K^T is formed with the queries as the A operand, so a
+// lane holds one key column and applies its scale once to the max of its
+// column (scale >= 0): two passes (hi, lo parts of q) instead of three.
+//
 // keys: dynamic LDS of n_qb words (the eligible blocks of one query block)
+template <bool kInt8>
 __global__ __launch_bounds__(NT) void select_blocks_kernel(SelectParams p) {
   extern __shared__ uint32_t keys[];
   __shared__ int hist[dev::kHistWords];
@@ -160,6 +166,67 @@ __global__ __launch_bounds__(NT) void select_blocks_kernel(SelectParams p) {
       const int i = rt * 32 + lr;
       const int row = qs + (i < nrow ? i : 0);
       split_row8(p.qlow + ((size_t)t * p.N + row) * R + lh * 8, qh[rt], ql[rt]);
+    }
+    if constexpr (kInt8) {
+      const int8_t* cbase = p.kcodes + (size_t)g * p.N * R;
+      const float* sbase = p.kscale + (size_t)g * p.N;
+      // keys j0 + 32 kt + lr of block c as B operands (8 codes per lane) and
+      // their scales; rows past N read key N-1 (masked below); the next
+      // block is loaded one iteration ahead
+      auto kload8 = [&](int c, uint2 (&v)[2], float (&sc)[2]) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          const int j = min(c * kBlock + kt * 32 + lr, p.N - 1);
+          v[kt] = *reinterpret_cast<const uint2*>(cbase + (size_t)j * R + lh * 8);
+          sc[kt] = sbase[j];
+        }
+      };
+      uint2 nk[2];
+      float ns[2];
+      kload8(c_lo + min(wave, nE - 1), nk, ns);
+      for (int x = wave; x < nE; x += 4) {
+        const int c = c_lo + x;
+        const int j0 = c * kBlock;
+        dev::bf16x8 kq[2];
+        float ks[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          const uint32_t w2[2] = {nk[kt].x, nk[kt].y};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) kq[kt][e] = (__bf16)(float)(int8_t)(w2[e >> 2] >> (8 * (e & 3)));
+          ks[kt] = ns[kt];
+        }
+        kload8(c_lo + min(x + 4, nE - 1), nk, ns);
+        const bool edge = j0 + kBlock - 1 > qs;     // some pair may have j > i or j >= N
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          // column j = j0 + 32 kt + lr; element e: row qs + 32 rt + 4 lh + 8 (e/4) + e%4
+          const int j = j0 + kt * 32 + lr;
+          float m = -__builtin_inff();
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt) {
+            dev::f32x16 acc = {};
+            acc = dev::mfma32(ql[rt], kq[kt], acc);
+            acc = dev::mfma32(qh[rt], kq[kt], acc);
+            if (edge) {
+#pragma unroll
+              for (int e = 0; e < 16; ++e) {
+                const int ii = rt * 32 + lh * 4 + (e >> 2) * 8 + (e & 3);
+                const bool vis = (ii < nrow) & (j <= qs + ii) & (j < p.N);
+                m = fmaxf(m, vis ? acc[e] : -__builtin_inff());
+              }
+            } else {
+#pragma unroll
+              for (int e = 0; e < 16; ++e) m = fmaxf(m, acc[e]);
+            }
+          }
+          mx = fmaxf(mx, m == -__builtin_inff() ? m : m * ks[kt]);
+        }
+        mx = wave_max(mx);
+        if (lane == 0) keys[x] = s == 0 ? dev::order_key(mx) : max(keys[x], dev::order_key(mx));
+      }
+      continue;
     }
     const float* kbase = p.klow + (size_t)g * p.N * R;
     // B operands: keys j0 + 32 kt + lr of block c (rows past N read key N-1,
@@ -237,7 +304,50 @@ __global__ __launch_bounds__(NT) void select_blocks_kernel(SelectParams p) {
   }
 }
 
+// 8-bit indexer keys: one thread per key row; scale = max |k| / 127 (IEEE
+// fp32 division), code = k / scale rounded to nearest, ties to even; an
+// all-zero key gets scale 0 and zero codes.
+__global__ __launch_bounds__(NT) void quantize_keys_kernel(const float* __restrict__ klow, int8_t* __restrict__ codes,
+                                                           float* __restrict__ scales, size_t n_rows) {
+  const size_t row = (size_t)blockIdx.x * NT + threadIdx.x;
+  if (row >= n_rows) return;
+  const float4* src = reinterpret_cast<const float4*>(klow + row * R);
+  float v[R];
+#pragma unroll
+  for (int q = 0; q < R / 4; ++q) {
+    const float4 a = src[q];
+    v[4 * q] = a.x;
+    v[4 * q + 1] = a.y;
+    v[4 * q + 2] = a.z;
+    v[4 * q + 3] = a.w;
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int d = 0; d < R; ++d) amax = fmaxf(amax, fabsf(v[d]));
+  const float sc = amax / 127.0f;
+  uint32_t w[R / 4];
+#pragma unroll
+  for (int q = 0; q < R / 4; ++q) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int c = sc > 0.f ? (int)__builtin_rintf(v[4 * q + e] / sc) : 0;
+      word |= (uint32_t)(uint8_t)(int8_t)c << (8 * e);
+    }
+    w[q] = word;
+  }
+  *reinterpret_cast<uint4*>(codes + row * R) = make_uint4(w[0], w[1], w[2], w[3]);
+  scales[row] = sc;
+}
+
 }  // namespace
+
+hipError_t launch_quantize_keys(const float* klow, int8_t* codes, float* scales, size_t n_rows, hipStream_t s) {
+  if (n_rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(quantize_keys_kernel, dim3((unsigned)((n_rows + NT - 1) / NT)), dim3(NT), 0, s, klow, codes,
+                     scales, n_rows);
+  return hipGetLastError();
+}
 
 hipError_t launch_project(const ProjParams& p, hipStream_t s) {
   if (p.n_entries == 0 || p.N == 0) return hipSuccess;
@@ -252,12 +362,14 @@ hipError_t launch_project(const ProjParams& p, hipStream_t s) {
 hipError_t launch_select_blocks(const SelectParams& p, hipStream_t s) {
   if (p.n_ret == 0 || p.n_qb == 0) return hipSuccess;
   const size_t lds = (size_t)p.n_qb * sizeof(uint32_t);
+  const void* fn = p.kcodes ? reinterpret_cast<const void*>(select_blocks_kernel<true>)
+                            : reinterpret_cast<const void*>(select_blocks_kernel<false>);
   if (lds > 32 * 1024) {   // large tables: allow the dynamic size explicitly
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(select_blocks_kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(select_blocks_kernel, dim3(p.n_qb, p.n_units), dim3(NT), lds, s, p);
+  if (p.kcodes) hipLaunchKernelGGL(select_blocks_kernel<true>, dim3(p.n_qb, p.n_units), dim3(NT), lds, s, p);
+  else hipLaunchKernelGGL(select_blocks_kernel<false>, dim3(p.n_qb, p.n_units), dim3(NT), lds, s, p);
   return hipGetLastError();
 }
 

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define HA_VERSION 3
+#define HA_VERSION 4
 
 typedef enum {
   HA_SWA = 0,        /* causal sliding window: keys i-w < j <= i */
@@ -105,6 +105,12 @@ typedef struct {
                           *    represented by its mean key or by a point built
                           *    from per-dimension extremes; both representatives
                           *    ignore causality inside the block) */
+  int32_t index_bits;    /* 0 or 32: fp32 low-rank keys; 8: the block scores read
+                          * the keys as int8 codes with one fp32 scale per key
+                          * (scale = max |k| / 127, code = k / scale rounded to
+                          * nearest, ties to even; hybrid-attention article,
+                          * mixed-precision index: an 8-bit indexer).  8 is built
+                          * for block mode with block_score = 0 only. */
 } ha_layer_desc;
 
 /* Optional copies of the indexer's intermediate results (caller-owned device
@@ -158,15 +164,23 @@ int ha_index_project(const ha_layer_desc* desc, const int32_t* head_kind,
 
 /* Stage: block scoring + top-k (RTPurbo scout; TriangleMix interview top-k).
  * For retrieval head t and query block b: eligible blocks c >= force_block0
- * with c*k_block <= qe_b - window; score as desc->block_score says; keeps the
- * topk best by (score desc, block asc).
+ * with c*k_block <= qe_b - window; score as desc->block_score says (with
+ * index_bits = 8 the keys are first quantized as ha_quantize_keys does);
+ * keeps the topk best by (score desc, block asc).
  *   sel  int32 [Hret, n_qb, topk], ascending, -1 padded.
- *   workspace  block_score 1 or 2: >= ha_workspace_bytes(desc, head_kind)
- *              bytes, 256-byte aligned (the block representatives); may be
- *              NULL with ws_bytes 0 when block_score = 0. */
+ *   workspace  block_score 1 or 2, or index_bits 8: >= ha_workspace_bytes(desc,
+ *              head_kind) bytes, 256-byte aligned (block representatives, 8-bit
+ *              keys); may be NULL with ws_bytes 0 otherwise. */
 int ha_select_blocks(const ha_layer_desc* desc, const int32_t* head_kind,
                      const float* qlow, const float* klow, int32_t* sel,
                      void* workspace, size_t ws_bytes, void* stream);
+
+/* Stage: 8-bit indexer keys (hybrid-attention article, mixed-precision index).
+ * For every row of klow [Hkv, N, r]: scale = max_d |k_d| / 127 (IEEE fp32
+ * division), code_d = k_d / scale rounded to nearest with ties to even; an
+ * all-zero row gets scale 0 and zero codes.
+ *   codes int8 [Hkv, N, r]; scales fp32 [Hkv, N]. */
+int ha_quantize_keys(const ha_layer_desc* desc, const float* klow, int8_t* codes, float* scales, void* stream);
 
 /* Stage: Lloyd k-means of klow per KV head (RTPurboV2 clustering passage).
  * M = n_clusters, kmeans_iters iterations, C0_m = klow_{m*stride}; ties go to

@@ -37,7 +37,7 @@ def run_gpu(w, li, return_aux=True):
     res = ha.hybrid_attn_prefill(
         Q, K, V, w.head_kind, w.window, P, topk=w.topk, block=w.q_block, force_block0=w.force_block0,
         n_clusters=w.n_clusters, kmeans_iters=w.kmeans_iters, kmeans_stride=w.kmeans_stride,
-        sink=w.sink, last_q=w.last_q, n_out=w.n_out, group_select=w.group_select, block_score=w.block_score, xa_scale=xs, xa_offset=xo,
+        sink=w.sink, last_q=w.last_q, n_out=w.n_out, group_select=w.group_select, block_score=w.block_score, index_bits=w.index_bits, xa_scale=xs, xa_offset=xo,
         return_aux=return_aux and bool(w.ret_heads))
     torch.cuda.synchronize()
     if not isinstance(res, tuple):

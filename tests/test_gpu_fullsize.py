@@ -37,7 +37,11 @@ def _run(name, heads=None, blocks=None, out_rows=None, **changes):
     def q_rows(a, b):
         return si.bf16_to_f64(li.Q[a:b])
 
-    ref = layer_prefill(w, q_rows, K, V, P, xs, xo, blocks=blocks, heads=heads, out_rows=out_rows)
+    k32 = None
+    if w.index_bits == 8:   # the oracle quantizes the GPU's validated fp32 keys
+        k32 = {g: aux["klow"][g].cpu().numpy() for g in range(w.n_kv_heads)}
+    ref = layer_prefill(w, q_rows, K, V, P, xs, xo, blocks=blocks, heads=heads, out_rows=out_rows,
+                        klow32_override=k32)
     if w.ret_heads:
         sel = aux["sel"].cpu().numpy()
         _gpu.check_group_rows(sel, w)
@@ -52,7 +56,7 @@ def _run(name, heads=None, blocks=None, out_rows=None, **changes):
                 override[h][b] = np.array([x for x in sel[t, b] if x >= 0], dtype=np.int64)
         print(f"selection differences inside the tie band: {n_diff}")
         ref = layer_prefill(w, q_rows, K, V, P, xs, xo, blocks=blocks, heads=heads, sel_override=override,
-                            out_rows=out_rows)
+                            out_rows=out_rows, klow32_override=k32)
     Og = O.cpu().numpy()[ref.rows]
     hs = list(range(w.n_q_heads)) if heads is None else list(heads)
     mx, mean = _gpu.assert_close_out(Og[:, hs], ref.O[:, hs], name)
@@ -72,7 +76,7 @@ def test_qwen3_30b_layer_32k_group_select():
     _run("qwen3_30b_a3b_32k", group_select=1)
 
 
-@pytest.mark.parametrize("name", ["qwen3_30b_a3b_32k_mean", "qwen3_30b_a3b_32k_minmax"])
+@pytest.mark.parametrize("name", ["qwen3_30b_a3b_32k_mean", "qwen3_30b_a3b_32k_minmax", "qwen3_30b_a3b_32k_int8"])
 def test_qwen3_30b_layer_32k_block_representatives(name):
     _run(name)
 
@@ -85,19 +89,20 @@ def test_block_representative_selection_agreement_32k():
     w0 = synth.WORKLOADS["qwen3_30b_a3b_32k"]
     li = synth.make_layer_inputs(w0)
     sels = {}
-    for name in ("qwen3_30b_a3b_32k", "qwen3_30b_a3b_32k_mean", "qwen3_30b_a3b_32k_minmax"):
+    for name in ("qwen3_30b_a3b_32k", "qwen3_30b_a3b_32k_mean", "qwen3_30b_a3b_32k_minmax", "qwen3_30b_a3b_32k_int8"):
         w = synth.WORKLOADS[name]
         _, _, aux = _gpu.run_gpu(w, li)
-        sels[w.block_score] = aux["sel"].cpu().numpy()
+        sels[w.block_score + (10 if w.index_bits == 8 else 0)] = aux["sel"].cpu().numpy()
     base = sels[0]
-    for m in (1, 2):
+    for m in (1, 2, 10):
         kept = tot = 0
         for t in range(base.shape[0]):
             for b in range(base.shape[1]):
                 a = set(int(x) for x in base[t, b] if x >= 0)
                 kept += len(a & set(int(x) for x in sels[m][t, b] if x >= 0))
                 tot += len(a)
-        print(f"block_score {m}: keeps {kept / max(tot, 1):.3f} of the max-pair selection ({tot} selected blocks)")
+        label = "8-bit keys" if m == 10 else f"block_score {m}"
+        print(f"{label}: keeps {kept / max(tot, 1):.3f} of the max-pair selection ({tot} selected blocks)")
         assert tot > 0
 
 

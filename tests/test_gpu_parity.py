@@ -29,6 +29,12 @@ def _compare(w, blocks=None, check_sel=True):
         klow = aux["klow"].cpu().numpy()
         for g, kl in ref.klow.items():
             _gpu.assert_lowrank(klow[g], kl, f"klow[{g}]")
+        k32 = None
+        if w.index_bits == 8:
+            # 8-bit keys: the oracle quantizes the GPU's validated fp32 keys, so
+            # both sides take the float-to-integer step on the same values
+            k32 = {g: klow[g] for g in range(w.n_kv_heads)}
+            ref = layer_prefill(w, q, K, V, P, xs, xo, blocks=blocks, klow32_override=k32)
         override = {}
         for t, h in enumerate(w.ret_heads):
             override[h] = {}
@@ -36,7 +42,7 @@ def _compare(w, blocks=None, check_sel=True):
                 _gpu.check_selection(sel[t, b], E, s, w.topk, f"head {h} block {b}")
                 override[h][b] = np.array([x for x in sel[t, b] if x >= 0], dtype=np.int64)
         # grade attention given the validated GPU selection
-        ref = layer_prefill(w, q, K, V, P, xs, xo, blocks=blocks, sel_override=override)
+        ref = layer_prefill(w, q, K, V, P, xs, xo, blocks=blocks, sel_override=override, klow32_override=k32)
     _gpu.assert_close_out(Og, ref.O, w.name)
     if w.n_out:
         _gpu.assert_close_out(O_out.cpu().numpy(), ref.O_out, w.name + " O_out")
@@ -96,6 +102,38 @@ def test_block_representative_scores(score, N, window, topk, f0, gs):
     kinds = [HEAD_RETRIEVAL, HEAD_SWA, HEAD_RETRIEVAL, HEAD_RETRIEVAL, HEAD_SWA, HEAD_RETRIEVAL, HEAD_RETRIEVAL,
              HEAD_RETRIEVAL]
     _compare(_layer(kinds, N, window=window, topk=topk, force_block0=f0, group_select=gs, block_score=score))
+
+
+@pytest.mark.parametrize("N,window,topk,f0,gs", [(1000, 100, 3, 0, 0), (1337, 64, 8, 1, 0), (700, 1, 2, 0, 0),
+                                                 (640, 50, 100, 0, 0), (1000, 100, 3, 1, 1)])
+def test_int8_indexer_keys(N, window, topk, f0, gs):
+    kinds = [HEAD_RETRIEVAL, HEAD_SWA, HEAD_RETRIEVAL, HEAD_RETRIEVAL, HEAD_SWA, HEAD_RETRIEVAL, HEAD_RETRIEVAL,
+             HEAD_RETRIEVAL]
+    _compare(_layer(kinds, N, window=window, topk=topk, force_block0=f0, group_select=gs, index_bits=8))
+
+
+def test_quantize_keys_bit_exact():
+    # codes and scales equal the oracle's fp32 quantizer bit for bit: random
+    # keys of many magnitudes, all-zero keys, and keys with max |k| = 127
+    # (scale 1) holding exact .5 values, which round to even
+    import torch
+    import hybrid_attention_prefill_amd as ha
+    from oracle.indexer import quantize_keys_int8
+    rng = np.random.default_rng(11)
+    Hkv, N = 2, 3000
+    k = (rng.standard_normal((Hkv * N, 16)) * rng.uniform(1e-3, 50, (Hkv * N, 1))).astype(np.float32)
+    k[5] = 0.0
+    k[7] = 0.0
+    k[100] = [127.0, 0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 126.5, -126.5, 3.5, 0.0, -0.0, 10.5, -10.5, 64.5, 1.0]
+    d = ha.make_desc(N, 2, Hkv, 128, window=64, topk=4, index_bits=8)
+    codes = torch.empty((Hkv, N, 16), dtype=torch.int8, device="cuda")
+    scales = torch.empty((Hkv, N), dtype=torch.float32, device="cuda")
+    ha.ha_quantize_keys(d, torch.from_numpy(k.reshape(Hkv, N, 16)).cuda(), codes, scales)
+    torch.cuda.synchronize()
+    want_c, want_s = quantize_keys_int8(k)
+    np.testing.assert_array_equal(scales.cpu().numpy().reshape(-1).view(np.uint32), want_s.view(np.uint32))
+    np.testing.assert_array_equal(codes.cpu().numpy().reshape(-1, 16), want_c)
+    assert list(want_c[100]) == [127, 0, 2, 2, 0, -2, -2, 126, -126, 4, 0, 0, 10, -10, 64, 1]
 
 
 def test_group_select_pack_shapes():
