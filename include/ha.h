@@ -8,7 +8,8 @@
  *     softmax attention runs over the selected keys plus the local window;
  *   - TriangleMix heads: sink keys + local band, dense attention for the last rows;
  *   - dense heads: plain causal attention;
- *   - Orthros output positions: full cross-attention of a scale-offset query.
+ *   - Orthros output positions: full cross-attention of a scale-offset query
+ *     (one output row in prefill, many in SFT / pre-training).
  *
  * Sources (page title, passage):
  *   "RTPurbo" post (tchannels.org, Анализ данных): most heads work locally, a
@@ -20,7 +21,10 @@
  *   36kr interview "Agent 的注意力系统" (TriangleMix introduction): streaming
  *     region + last Q-K region in deep layers; top-k over key blocks.
  *   Same interview, GQA answer: queries of one GQA group share their keys, so
- *     one selection can serve the group (group_select).
+ *     one selection can serve the group (group_select); top-k matching answer:
+ *     block representatives, mean or per-dimension extremes (block_score).
+ *   Baidu developer article "深度解析：超长上下文注意力架构的分层优化策略",
+ *     mixed-precision index section: an 8-bit quantized indexer (index_bits).
  *   "一个 Attention,两种工作模式" (Orthros), "Prefilling" and design sections:
  *     SWA for all tokens, full cross-attention for output positions, a light
  *     scale-offset separating the two query roles.
@@ -65,7 +69,10 @@ typedef enum {
 typedef enum {
   HA_OK = 0,
   HA_ERR_ARG = 1,          /* null pointer, inconsistent sizes, bad head kind */
-  HA_ERR_UNSUPPORTED = 2,  /* valid but not built: D != 128, r != 16, blocks != 64 */
+  HA_ERR_UNSUPPORTED = 2,  /* valid but not built: D != 128, r != 16, blocks != 64,
+                            * Hq > 256, topk > 255, more than 16384 candidate blocks
+                            * or clusters, force_block0 with clusters, index_bits 8
+                            * outside block mode with block_score 0 */
   HA_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than ha_workspace_bytes() */
   HA_ERR_DEVICE = 4        /* a HIP launch or query failed */
 } ha_status;
@@ -108,9 +115,10 @@ typedef struct {
   int32_t index_bits;    /* 0 or 32: fp32 low-rank keys; 8: the block scores read
                           * the keys as int8 codes with one fp32 scale per key
                           * (scale = max |k| / 127, code = k / scale rounded to
-                          * nearest, ties to even; hybrid-attention article,
-                          * mixed-precision index: an 8-bit indexer).  8 is built
-                          * for block mode with block_score = 0 only. */
+                          * nearest, ties to even; Baidu developer article on
+                          * long-context attention, mixed-precision index
+                          * section: an 8-bit indexer).  8 is built for block
+                          * mode with block_score = 0 only. */
 } ha_layer_desc;
 
 /* Optional copies of the indexer's intermediate results (caller-owned device
@@ -175,7 +183,8 @@ int ha_select_blocks(const ha_layer_desc* desc, const int32_t* head_kind,
                      const float* qlow, const float* klow, int32_t* sel,
                      void* workspace, size_t ws_bytes, void* stream);
 
-/* Stage: 8-bit indexer keys (hybrid-attention article, mixed-precision index).
+/* Stage: 8-bit indexer keys (Baidu developer article on long-context
+ * attention, mixed-precision index section).
  * For every row of klow [Hkv, N, r]: scale = max_d |k_d| / 127 (IEEE fp32
  * division), code_d = k_d / scale rounded to nearest with ties to even; an
  * all-zero row gets scale 0 and zero codes.

@@ -29,8 +29,8 @@ With the block's keys K_c = {j in block c, j < N}:
            reach, so it bounds every key's score from above.
 Causality inside a block is not applied by either representative.
 
-8-bit indexer ([p5] hybrid-attention article, mixed-precision index: the
-indexer is stored in 8 bits): each low-rank key is kept as int8 codes with
+8-bit indexer (Baidu developer article "深度解析：超长上下文注意力架构的分层优化策略",
+mixed-precision index section: the indexer is stored in 8 bits): each low-rank key is kept as int8 codes with
 one fp32 scale, scale_j = max_d |k_jd| / 127 and code_jd = k_jd / scale_j
 rounded to nearest (ties to even); block scores use the dequantized keys
 scale_j * code_j.  The float-to-integer step is taken in fp32, as the
