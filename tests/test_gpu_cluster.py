@@ -168,6 +168,14 @@ def test_group_select_cluster_layer(N, M, window, topk):
     _layer_cluster(w)
 
 
+@pytest.mark.parametrize("N,M,gs", [(64, 4, 0), (65, 4, 1), (130, 8, 0), (200, 3, 1)])
+def test_cluster_tiny_sequences(N, M, gs):
+    base = synth.WORKLOADS["allsparse_1m"]
+    w = synth.configs.shrink(base, N, n_clusters=M, window=64, n_needles=1)
+    w = w.with_(kmeans_stride=N // M, topk=2, kmeans_iters=2, group_select=gs)
+    _layer_cluster(w)
+
+
 def test_group_select_cluster_mixed_with_swa_heads():
     base = synth.WORKLOADS["allsparse_1m_gqa"]
     kinds = tuple(1 if h % 3 == 0 else 0 for h in range(16))

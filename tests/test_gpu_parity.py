@@ -136,6 +136,18 @@ def test_quantize_keys_bit_exact():
     assert list(want_c[100]) == [127, 0, 2, 2, 0, -2, -2, 126, -126, 4, 0, 0, 10, -10, 64, 1]
 
 
+@pytest.mark.parametrize("N", [1, 63, 64, 65, 130])
+@pytest.mark.parametrize("mode", ["blocks", "group", "mean", "extremes", "int8"])
+def test_retrieval_tiny_sequences(N, mode):
+    # sequences shorter than, equal to and just past one block: no eligible
+    # block at all, then the first one
+    kinds = [HEAD_RETRIEVAL, HEAD_RETRIEVAL, HEAD_SWA, HEAD_RETRIEVAL]
+    kw = dict(window=64, topk=3)
+    kw.update({"group": dict(group_select=1), "mean": dict(block_score=1), "extremes": dict(block_score=2),
+               "int8": dict(index_bits=8)}.get(mode, {}))
+    _compare(_layer(kinds, N, Hkv=1, **kw))
+
+
 def test_group_select_pack_shapes():
     # G = 8, all retrieval: two full packs per group
     _compare(_layer([HEAD_RETRIEVAL] * 16, 900, Hkv=2, window=70, topk=4, group_select=1))
