@@ -311,7 +311,7 @@ def main():
                     help="first run one plain device copy of 1 GiB (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
               "(each layer's kernels run on one GPU's share; see the sharding notes in the design document).",
               file=sys.stderr)
         sys.exit(2)

@@ -451,7 +451,7 @@ const char* ha_status_string(int status) {
   switch (status) {
     case HA_OK: return "HA_OK";
     case HA_ERR_ARG: return "HA_ERR_ARG: invalid argument";
-    case HA_ERR_UNSUPPORTED: return "HA_ERR_UNSUPPORTED: configuration not supported by this build";
+    case HA_ERR_UNSUPPORTED: return "HA_ERR_UNSUPPORTED: configuration not supported by this library";
     case HA_ERR_WORKSPACE: return "HA_ERR_WORKSPACE: workspace missing, misaligned or too small";
     case HA_ERR_DEVICE: return "HA_ERR_DEVICE: HIP launch failed";
     default: return "unknown ha_status";
