@@ -387,7 +387,6 @@ __global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
   __shared__ uint32_t gmax[kGroups];
   __shared__ uint32_t tau_s;
   __shared__ int ovf;
-  __shared__ uint64_t elmask[kMaxSelCand / 64];   // bit m: cluster m eligible for this block
   __shared__ uint32_t sink_word;                  // store target of padding lanes
   const int t0 = (int)(p.unit[blockIdx.y] & 0xFFFFu), ns = (int)(p.unit[blockIdx.y] >> 16);
   const int tid = threadIdx.x;
@@ -433,44 +432,58 @@ __global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
   const __bf16* chi = p.c_hi + (size_t)g * p.M * R * NPART;
   const __bf16* clo = p.c_lo + (size_t)g * p.M * R * NPART;
   const int32_t* fm = p.first_mem + (size_t)g * p.M;
-  // eligibility bitmask (cluster m has a member <= lim), from coalesced reads
-  // of the first members, one ballot per 64 clusters
-  // (16 loads in flight per batch)
-  for (int c0 = wave * 64; c0 < p.M; c0 += 16 * 4 * 64) {
-    int f[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) f[j] = fm[min(c0 + j * 256 + lane, p.M - 1)];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int c = c0 + j * 256 + lane;
-      const uint64_t b = __ballot(c < p.M && lim[0] >= 0 && f[j] <= lim[0]);
-      if (lane == 0 && c0 + j * 256 < p.M) elmask[(c0 + j * 256) >> 6] = b;
-    }
-  }
-  __syncthreads();
   int n_el[kSelBlocks] = {};
   uint32_t gmx = 0;                 // largest key this lane wrote
   const int n_tiles = (p.M + 31) / 32;
   // A wave's tiles are x = wave + 4 i.  Operands are loaded kPre tiles ahead
   // (register ring, static slots: the loop is unrolled by kPre).
   constexpr int kPre = 4;
-  auto ld = [&](int x, dev::bf16x8 (&bh)[NPART], dev::bf16x8 (&bl)[NPART]) {
+  // A ring slot holds a tile's split centroids and, per lane, the first
+  // member of its cluster (eligibility: a member <= lim).
+  auto ld = [&](int x, dev::bf16x8 (&bh)[NPART], dev::bf16x8 (&bl)[NPART], int& f) {
     const int m = min(p.M - 1, x * 32 + lr);
 #pragma unroll
     for (int part = 0; part < NPART; ++part) {
       bh[part] = *reinterpret_cast<const dev::bf16x8*>(chi + ((size_t)m * NPART + part) * R + lh * 8);
       bl[part] = *reinterpret_cast<const dev::bf16x8*>(clo + ((size_t)m * NPART + part) * R + lh * 8);
     }
+    f = fm[m];
   };
   dev::bf16x8 rbh[kPre][NPART], rbl[kPre][NPART];
+  int rfm[kPre];
+  const int lim0 = lim[0];
   for (int s = 0; s < ns; ++s) {
     load_q(t0 + s);
     // slot order, as in the loop body, so the first group waits only for its own slot
 #pragma unroll
     for (int u = 0; u < kPre; ++u) {
-      ld(min(n_tiles - 1, wave + 4 * u), rbh[u], rbl[u]);
+      ld(min(n_tiles - 1, wave + 4 * u), rbh[u], rbl[u], rfm[u]);
       __builtin_amdgcn_sched_barrier(0);
     }
+    // The keys of tile x are finished one tile later, after the products of
+    // the next tile are issued, so the matrix-result reads never wait on the
+    // products just issued.  Key of a cluster: order key of the row max, 0 if
+    // ineligible (no member <= lim); padding lanes store to a dummy word.
+    dev::f32x16 pacc[2];
+    int pm = INT_MAX, pf = 0;
+    auto finish = [&]() {
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, pacc[rt][e]);
+      mx = dev::pair32_max(mx);
+      const bool mok = pm < p.M;
+      const bool el = mok & (lim0 >= 0) & (pf <= lim0);
+      const uint32_t key = el ? dev::order_key(mx) : 0u;
+      uint32_t* dst = mok ? &keys[0][pm] : &sink_word;
+      // later slots of a unit keep the max with what this lane stored before
+      if (s > 0) *dst = max(*dst, key);
+      else *dst = key;
+      gmx = max(gmx, key);
+      n_el[0] += (int)(el & (lh == 0) & (s == 0));
+    };
+    bool have = false;
     // Groups of kPre tiles run whole (tiles past the end compute on the last
     // tile and store nothing: their centroid index is >= M), so the body has no
     // branches around loads.  A slot is refilled right after its MFMAs have
@@ -479,37 +492,30 @@ __global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
 #pragma unroll
       for (int u = 0; u < kPre; ++u) {
         const int x = x0 + 4 * u;
-        const int m = x * 32 + lr;
-        const bool mok = m < p.M;
-        float mx = -__builtin_inff();
+        dev::f32x16 acc[2];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-          dev::f32x16 acc = {};
+          acc[rt] = dev::f32x16{};
 #pragma unroll
           for (int part = 0; part < NPART; ++part) {
-            acc = dev::mfma32(ql[part][rt], rbh[u][part], acc);
-            acc = dev::mfma32(qh[part][rt], rbl[u][part], acc);
-            acc = dev::mfma32(qh[part][rt], rbh[u][part], acc);
+            acc[rt] = dev::mfma32(ql[part][rt], rbh[u][part], acc[rt]);
+            acc[rt] = dev::mfma32(qh[part][rt], rbl[u][part], acc[rt]);
+            acc[rt] = dev::mfma32(qh[part][rt], rbh[u][part], acc[rt]);
           }
-#pragma unroll
-          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[e]);
         }
+        const int fx = rfm[u];
         // keep the refill after the slot's last reads (no register rotation)
         __builtin_amdgcn_sched_barrier(0);
-        ld(min(x + 4 * kPre, n_tiles - 1), rbh[u], rbl[u]);
-        mx = dev::pair32_max(mx);
-        // branch-free: both lane halves store the same key; padding lanes store
-        // to a dummy word and count nothing
-        const int mc = min(m, p.M - 1);
-        const bool el = (bool)((elmask[mc >> 6] >> (mc & 63)) & 1ull) & mok;
-        const uint32_t key = el ? dev::order_key(mx) : 0u;
-        uint32_t* dst = mok ? &keys[0][mc] : &sink_word;
-        // later slots of a unit keep the max with what this lane stored before
-        *dst = s > 0 ? max(*dst, key) : key;
-        gmx = max(gmx, key);
-        n_el[0] += (int)(el & (lh == 0) & (s == 0));
+        ld(min(x + 4 * kPre, n_tiles - 1), rbh[u], rbl[u], rfm[u]);
+        if (have) finish();
+        pacc[0] = acc[0];
+        pacc[1] = acc[1];
+        pm = x * 32 + lr;
+        pf = fx;
+        have = true;
       }
     }
+    if (have) finish();
   }
   if (lh == 0) gmax[wave * 32 + lr] = gmx;
   if (tid == 0) {
