@@ -55,15 +55,14 @@ __global__ __launch_bounds__(NT) void km_prep_kernel(KmeansParams p) {
 }
 
 // Assignment: each wave owns 32*KT keys (KT column blocks of 32), the
-// workgroup 4 waves.  Centroids are staged in LDS 256 at a time as three
-// 16-bit rows each: the two fp16 parts of C_m and the bf16 (hi, mid, lo) of
-// |C_m|^2.  For every tile of 32 centroids and key block, one chain of four
-// MFMAs gives
+// workgroup 4 waves.  Centroids are staged in LDS 256 at a time: the two fp16
+// parts of C_m as 16-bit rows, and |C_m|^2 in fp32.  For every tile of 32
+// centroids and key block, one chain of three MFMAs gives
 //   d^T[m][j] = |C_m|^2 - 2 C_m . k_j
-// directly: three fp16 passes over the split operands (keys pre-scaled by -2,
-// exact; ~2^-21 relative to |C||k|), and a bf16 pass that adds the norm parts
-// against a (1, 1, 1) operand (bf16 keeps fp32's exponent range for large
-// norms).  The |k_j|^2 term does not change the argmin.  A lane holds one key
+// directly: the chain's accumulator starts at the norms (a lane's 16 rows,
+// shared by the KT chains), and three fp16 passes over the split operands add
+// -2 C_m . k_j (keys pre-scaled by -2, exact; ~2^-21 relative to |C||k|).
+// The |k_j|^2 term does not change the argmin.  A lane holds one key
 // and 16 of the tile's centroids in increasing order; the tile minimum is a
 // min3 chain; only when some lane of a key block improves on its best does
 // the wave look up the index (the lowest element equal to the tile minimum;
@@ -77,7 +76,8 @@ constexpr int KT = 4;             // 32-key blocks per wave
 constexpr float kPadNorm = 1e30f; // norm of the padding rows of a partial tile
 
 __global__ __launch_bounds__(NT) void km_assign_kernel(KmeansParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t cs[3][kCChunk * kCStr];
+  __shared__ __attribute__((aligned(16))) uint16_t cs[2][kCChunk * kCStr];
+  __shared__ __attribute__((aligned(16))) float cns[kCChunk];   // |C_m|^2 of the staged centroids
   const int g = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, lr = lane & 31, lh = lane >> 5;
@@ -95,9 +95,6 @@ __global__ __launch_bounds__(NT) void km_assign_kernel(KmeansParams p) {
       kl[kt][e] = l;
     }
   }
-  dev::bf16x8 ones;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)((lh == 0 && e < 3) ? 1.f : 0.f);
   float best[KT];
   int arg[KT];
 #pragma unroll
@@ -122,19 +119,7 @@ __global__ __launch_bounds__(NT) void km_assign_kernel(KmeansParams p) {
         dst[0] = v0;
         dst[1] = v1;
       }
-      dev::bf16x8 nr0, nr1;
-      __bf16 h, md, l;
-      dev::split3(ok ? cn[m] : kPadNorm, h, md, l);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        nr0[e] = (__bf16)0.f;
-        nr1[e] = (__bf16)0.f;
-      }
-      nr0[0] = h;
-      nr0[1] = md;
-      nr0[2] = l;
-      *reinterpret_cast<dev::bf16x8*>(&cs[2][tid * kCStr]) = nr0;
-      *reinterpret_cast<dev::bf16x8*>(&cs[2][tid * kCStr + 8]) = nr1;
+      cns[tid] = ok ? cn[m] : kPadNorm;
     }
     __syncthreads();
     const int n_tiles = (nc + 31) / 32;
@@ -142,21 +127,26 @@ __global__ __launch_bounds__(NT) void km_assign_kernel(KmeansParams p) {
       const int r0 = x * 32;
       const dev::f16x8 ah = *reinterpret_cast<const dev::f16x8*>(&cs[0][(r0 + lr) * kCStr + lh * 8]);
       const dev::f16x8 al = *reinterpret_cast<const dev::f16x8*>(&cs[1][(r0 + lr) * kCStr + lh * 8]);
-      const dev::bf16x8 an = *reinterpret_cast<const dev::bf16x8*>(&cs[2][(r0 + lr) * kCStr + lh * 8]);
+      // the lane's 16 centroid rows lh*4 + 8q + (0..3): their norms seed
+      // every chain's accumulator
+      dev::f32x16 nv;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(&cns[r0 + lh * 4 + 8 * q]);
+        nv[4 * q + 0] = v.x;
+        nv[4 * q + 1] = v.y;
+        nv[4 * q + 2] = v.z;
+        nv[4 * q + 3] = v.w;
+      }
       const int m0 = c0 + r0;
       // KT independent MFMA chains, interleaved pass by pass
       dev::f32x16 acc[KT];
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        acc[kt] = {};
-        acc[kt] = dev::mfma32_f16(al, kh[kt], acc[kt]);
-      }
+      for (int kt = 0; kt < KT; ++kt) acc[kt] = dev::mfma32_f16(al, kh[kt], nv);
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) acc[kt] = dev::mfma32_f16(ah, kl[kt], acc[kt]);
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) acc[kt] = dev::mfma32_f16(ah, kh[kt], acc[kt]);
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) acc[kt] = dev::mfma32(an, ones, acc[kt]);
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
         float tmin = acc[kt][0];
