@@ -209,6 +209,46 @@ void build_packs(const ha_layer_desc* d, const int32_t* kinds, int kind, const s
   }
 }
 
+// Band kernel packs by head count: 4-head packs, then 2-head, then 1-head
+// (a 3-head pack becomes a 2-head and a 1-head pack), with the class sizes
+// in p->band_np.
+void order_band_packs(PackTable* pt, AttnParams* p) {
+  uint32_t h[3][kMaxHeads], sl[3][kMaxHeads];
+  int32_t row[3][kMaxHeads];
+  int n[3] = {0, 0, 0};
+  auto put = [&](int c, uint32_t w, uint32_t s, int32_t r) {
+    h[c][n[c]] = w;
+    sl[c][n[c]] = s;
+    row[c][n[c]] = r;
+    ++n[c];
+  };
+  for (int i = 0; i < pt->n; ++i) {
+    const uint32_t w = pt->heads[i], s = pt->slots[i];
+    int cnt = 0;
+    while (cnt < 4 && ((w >> (8 * cnt)) & 0xFFu) != 0xFFu) ++cnt;
+    if (cnt == 4) {
+      put(0, w, s, pt->sel_row[i]);
+    } else if (cnt == 3) {
+      put(1, w | 0xFFFF0000u, s & 0xFFFFu, pt->sel_row[i]);
+      put(2, ((w >> 16) & 0xFFu) | 0xFFFFFF00u, (s >> 16) & 0xFFu, pt->sel_row[i]);
+    } else if (cnt == 2) {
+      put(1, w, s, pt->sel_row[i]);
+    } else if (cnt == 1) {
+      put(2, w, s, pt->sel_row[i]);
+    }
+  }
+  int k = 0;
+  for (int c = 0; c < 3; ++c) {
+    for (int i = 0; i < n[c]; ++i, ++k) {
+      pt->heads[k] = h[c][i];
+      pt->slots[k] = sl[c][i];
+      pt->sel_row[k] = row[c][i];
+    }
+    p->band_np[c] = n[c];
+  }
+  pt->n = k;
+}
+
 AttnParams attn_params(const ha_layer_desc* d, const void* Q, const void* K, const void* V, float* O) {
   AttnParams p{};
   p.Q = static_cast<const uint16_t*>(Q);
@@ -237,6 +277,7 @@ int run_band(const ha_layer_desc* d, const int32_t* kinds, const void* Q, const 
     PackTable pt;
     build_packs(d, kinds, kind, {}, &pt);
     if (pt.n == 0) continue;
+    order_band_packs(&pt, &p);
     p.kind = kind;
     const int st = dev_status(launch_attn_band(p, pt, s));
     if (st != HA_OK) return st;
@@ -352,7 +393,9 @@ int run_gather(const ha_layer_desc* d, const int32_t* kinds, const Heads& h, con
   if (d->group_select) return dev_status(launch_attn_retrieval_group(p, pt, s));
   p.kind = SWA;
   p.lse = lse;
-  st = dev_status(launch_attn_band(p, pt, s));
+  PackTable bt = pt;
+  order_band_packs(&bt, &p);
+  st = dev_status(launch_attn_band(p, bt, s));
   if (st != HA_OK) return st;
   p.kind = RETRIEVAL;
   SelList sl;

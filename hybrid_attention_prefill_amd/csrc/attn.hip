@@ -452,18 +452,35 @@ __device__ __forceinline__ void run_tiles(const AttnParams& p, uint16_t* smem, i
 __global__ __launch_bounds__(NT, 1) void attn_band_kernel(AttnParams p, PackTable packs) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM_ELEMS];
   const int wave = threadIdx.x >> 6;
-  const int hs = wave & 3;                 // head slot in the pack
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int pk = lid / p.n_qt;
-  int qt = lid % p.n_qt;
-  if (p.kind != SWA) qt = p.n_qt - 1 - qt;   // long causal rows first
+  // pack class c (workgroup-uniform): packs of 4 >> c heads, 64 << c query
+  // rows per workgroup; wave w takes head slot w % (4 >> c) and the 32 rows
+  // of row group w / (4 >> c)
+  int c = 0, pk = 0, qt = 0, nq = 1;
+  {
+    int rem = lid, base = 0;
+    for (; c < 3; ++c) {
+      nq = (p.N + (BK << c) - 1) / (BK << c);
+      const int nwg = p.band_np[c] * nq;
+      if (rem < nwg) break;
+      rem -= nwg;
+      base += p.band_np[c];
+    }
+    if (c == 3) return;   // past the last class (the grid is sized exactly)
+    pk = base + rem / nq;
+    qt = rem % nq;
+  }
+  if (p.kind != SWA) qt = nq - 1 - qt;     // long causal rows first
+  const int sh = 2 - c;                    // log2 of the heads per pack
+  const int hs = wave & ((1 << sh) - 1);   // head slot in the pack
+  const int rows = BK << c;                // query rows of the workgroup
   const uint32_t pw = packs.heads[pk];
   const int h = (pw >> (8 * hs)) & 0xFF;
   const int g = (int)(pw & 0xFF) / p.G;
-  const int qt0 = qt * BK;                 // first row of the workgroup's tile
-  const int q0 = qt0 + QW * (wave >> 2);   // first row of this wave
+  const int qt0 = qt * rows;               // first row of the workgroup
+  const int q0 = qt0 + QW * (wave >> sh);  // first row of this wave
   const bool active = h != 0xFF && q0 < p.N;
-  const int hi_t = min(p.N - 1, qt0 + 63) >> 6;
+  const int hi_t = min(p.N - 1, qt0 + rows - 1) >> 6;
 
   MaskSpec ms;
   int bl = 0, st = 0;
@@ -474,7 +491,7 @@ __global__ __launch_bounds__(NT, 1) void attn_band_kernel(AttnParams p, PackTabl
     bl = max(0, qt0 - p.window + 1) >> 6;
   } else {  // TRIANGLE
     ms = {0, p.window, p.sink, p.dense_from};
-    if (qt0 + 63 < p.dense_from) {
+    if (qt0 + rows - 1 < p.dense_from) {
       bl = max(0, qt0 - p.window + 1) >> 6;
       st = min((p.sink + 63) >> 6, bl);
     }
@@ -543,7 +560,9 @@ __global__ __launch_bounds__(D) void cross_merge_kernel(AttnParams p) {
 }  // namespace
 
 hipError_t launch_attn_band(const AttnParams& p, const PackTable& packs, hipStream_t s) {
-  const int nwg = packs.n * p.n_qt;
+  if (p.band_np[0] + p.band_np[1] + p.band_np[2] != packs.n) return hipErrorInvalidValue;
+  int nwg = 0;
+  for (int c = 0; c < 3; ++c) nwg += p.band_np[c] * ((p.N + (BK << c) - 1) / (BK << c));
   if (nwg == 0) return hipSuccess;
   hipLaunchKernelGGL(attn_band_kernel, dim3(nwg), dim3(NT), 0, s, p, packs);
   return hipGetLastError();

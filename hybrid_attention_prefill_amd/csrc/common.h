@@ -37,6 +37,11 @@ struct AttnParams {
   int window, sink, dense_from;   // dense_from = N - last_q (TRIANGLE)
   int kind;            // SWA, DENSE, TRIANGLE (band kernel) or RETRIEVAL (gather)
   int n_qt;            // query tiles of 64 rows
+  // band kernel: the pack table holds band_np[0] packs of 4 heads (a
+  // workgroup takes 64 query rows of each), then band_np[1] packs of 2 heads
+  // (128 rows each), then band_np[2] single heads (256 rows): the 8 waves of
+  // a workgroup always have rows to compute
+  int band_np[3];
   // gather only
   const int32_t* sel;      // [Hret, n_qb, topk]
   int topk, force_block0;
