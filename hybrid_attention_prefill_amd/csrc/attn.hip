@@ -8,10 +8,11 @@
 // QK^T and PV on v_mfma_f32_32x32x16_bf16, softmax statistics and the output
 // accumulator in fp32, P rounded to bf16 for the PV product.
 //
-// Workgroup = 8 waves, two per SIMD.  A workgroup serves the 64 query rows of
-// one query tile for the (up to) 4 heads of a "pack" (heads of one KV head),
-// so every 64-key K/V tile staged in LDS serves 256 query rows; wave w takes
-// head slot w % 4 and query rows 32 * (w / 4) .. +31.  A wave needs about 200
+// Workgroup = 8 waves, two per SIMD.  A workgroup serves a "pack" of heads of
+// one KV head: 64 query rows of 4 heads, 128 rows of 2 heads or 256 rows of
+// one head, so every 64-key K/V tile staged in LDS serves 256 query rows;
+// wave w takes head slot w % n and query rows 32 * (w / n) .. +31 of the
+// workgroup's rows (n = heads in the pack).  A wave needs about 200
 // registers (Q fragments, a 64 x 32 score tile and a 128 x 32 output
 // accumulator), so two waves share each SIMD and the hardware overlaps one
 // wave's softmax with the other's matrix products and LDS reads.  Tiles are
