@@ -77,6 +77,21 @@ def test_gqa_group_sizes():
     _compare(_layer([HEAD_SWA] * 5, 300, Hkv=1, window=40))       # partial pack
 
 
+@pytest.mark.parametrize("kind", [HEAD_SWA, HEAD_DENSE, HEAD_TRIANGLE])
+def test_band_pack_classes(kind):
+    # 7 heads of one role on one KV head: a 4-head pack (64 rows per
+    # workgroup) and a 3-head remainder split into 2 heads (128 rows) + 1
+    # head (256 rows); N = 333 leaves every class a ragged last tile
+    _compare(_layer([kind] * 7, 333, Hkv=1, window=90, sink=5, last_q=40))
+
+
+def test_band_pack_classes_retrieval_window():
+    # 3 retrieval heads + 4 SWA heads on one KV head: the retrieval heads'
+    # window pass runs as a 2-head and a 1-head pack
+    kinds = [HEAD_RETRIEVAL, HEAD_SWA, HEAD_RETRIEVAL, HEAD_SWA, HEAD_SWA, HEAD_RETRIEVAL, HEAD_SWA]
+    _compare(_layer(kinds, 700, Hkv=1, window=100, topk=3))
+
+
 @pytest.mark.parametrize("N,window,topk,f0", [(1000, 100, 3, 0), (1000, 100, 3, 1), (1337, 64, 8, 1),
                                               (700, 1, 2, 0), (640, 50, 0, 1), (640, 50, 100, 0),
                                               (300, 5000, 4, 0)])
