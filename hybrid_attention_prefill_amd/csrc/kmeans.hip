@@ -238,35 +238,42 @@ __global__ __launch_bounds__(NT) void km_offsets_kernel(KmeansParams p) {
 // stable scatter of key positions into CSR order, one workgroup per chunk
 __global__ __launch_bounds__(NT) void km_scatter_kernel(KmeansParams p) {
   __shared__ int base[kMaxSelCand];       // [M] next free slot per cluster
-  __shared__ int batch[NT];
+  __shared__ int owner[kMaxSelCand];      // [M] lowest thread still to place a key of the cluster
   const int g = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
   const int32_t* pre = p.hist + ((size_t)g * p.n_chunks + ch) * p.M;
   const int32_t* off = p.csr_off + (size_t)g * (p.M + 1);
-  for (int m = tid; m < p.M; m += NT) base[m] = off[m] + pre[m];
+  for (int m = tid; m < p.M; m += NT) {
+    base[m] = off[m] + pre[m];
+    owner[m] = INT_MAX;
+  }
   __syncthreads();
   const int a = ch * kChunk, b = min(p.N, a + kChunk);
   const int32_t* as = p.assign + (size_t)g * p.N;
   int32_t* mem = p.csr_mem + (size_t)g * p.N;
+  // Keys in position order, NT at a time.  In each round the lowest thread
+  // still holding a key of cluster c (the earliest position) takes c's next
+  // slot, so every cluster's members stay in ascending position; a round
+  // places one key per distinct cluster, and a batch rarely holds the same
+  // cluster twice.
   for (int j0 = a; j0 < b; j0 += NT) {
     const int j = j0 + tid;
     const int c = j < b ? as[j] : -1;
-    batch[tid] = c;
-    __syncthreads();
-    int rank = 0, after = 0;
-    const int nb = min(NT, b - j0);
-    for (int t = 0; t < nb; ++t) {
-      const int ct = batch[t];
-      rank += (t < tid) & (ct == c);
-      after += (t > tid) & (ct == c);
+    bool left = c >= 0;
+    while (__syncthreads_or(left)) {
+      if (left) atomicMin(&owner[c], tid);
+      __syncthreads();
+      const bool win = left && owner[c] == tid;
+      if (win) {
+        mem[base[c]] = j;
+        base[c] += 1;
+        left = false;
+      }
+      __syncthreads();
+      if (c >= 0) owner[c] = INT_MAX;
     }
-    if (c >= 0) mem[base[c] + rank] = j;
-    __syncthreads();
-    if (c >= 0 && after == 0) base[c] += rank + 1;
-    __syncthreads();
   }
 }
 
-// centroid = mean of members in CSR order; 16 lanes per cluster, lane = dim
 __global__ __launch_bounds__(NT) void km_update_kernel(KmeansParams p) {
   const int g = blockIdx.y;
   const int m = blockIdx.x * (NT / R) + threadIdx.x / R;
