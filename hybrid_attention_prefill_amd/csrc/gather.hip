@@ -280,7 +280,11 @@ __global__ __launch_bounds__(NT, 2) void attn_selected_kernel(AttnParams p, SelL
   __shared__ int tmp4[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  const int b = lid / sl.n_ret, t = lid % sl.n_ret;
+  // head-major order: each XCD (a contiguous range of lid) takes whole heads,
+  // so the workgroups resident on it at a time are consecutive query blocks
+  // of one head, which select mostly the same clusters / blocks: their
+  // gathered rows are shared in that XCD's L2.  Late (long) blocks first.
+  const int t = lid / p.n_qt, b = p.n_qt - 1 - lid % p.n_qt;
   const int h = sl.head[t];
   const int g = h / p.G;
   const int q0 = b * BK;
