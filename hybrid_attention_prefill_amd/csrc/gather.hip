@@ -610,11 +610,14 @@ __global__ __launch_bounds__(grp::NT8, 1) void attn_retrieval_group_kernel(AttnP
   __shared__ int tmp8[8];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  // packs fastest: the packs of a KV group (same selection, same rows) run
-  // side by side on one XCD and share its L2; long key lists first
-  const int pk = lid % packs.n;
-  const int b = p.n_qt - 1 - lid / packs.n;
+  // XCD k (workgroup id mod 8) takes the query blocks b = k mod 8, long key
+  // lists first, and the packs of a query block side by side: every XCD gets
+  // a share of short and long blocks, and its resident workgroups are nearby
+  // query blocks (similar selections) of the same packs, sharing rows in L2
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int pk = slot % packs.n;
+  const int b = p.n_qt - 1 - ((slot / packs.n) * 8 + xcd);
+  if (b < 0) return;   // padding of n_qt to a multiple of 8
   const uint32_t pw = packs.heads[pk];
   const int hs = wave & 3;
   const int h = (pw >> (8 * hs)) & 0xFF;
@@ -774,7 +777,7 @@ hipError_t launch_attn_selected(const AttnParams& p, const SelList& sl, hipStrea
 }
 
 hipError_t launch_attn_retrieval_group(const AttnParams& p, const PackTable& packs, hipStream_t s) {
-  const int nwg = packs.n * p.n_qt;
+  const int nwg = packs.n * ((p.n_qt + 7) / 8 * 8);
   if (nwg == 0) return hipSuccess;
   hipLaunchKernelGGL(attn_retrieval_group_kernel, dim3(nwg), dim3(grp::NT8), 0, s, p, packs);
   return hipGetLastError();
