@@ -279,12 +279,16 @@ __global__ __launch_bounds__(NT, 2) void attn_selected_kernel(AttnParams p, SelL
   __shared__ int pre[kMaxTopk + 2];     // prefix of visible key counts per entry
   __shared__ int tmp4[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  // head-major order: each XCD (a contiguous range of lid) takes whole heads,
-  // so the workgroups resident on it at a time are consecutive query blocks
-  // of one head, which select mostly the same clusters / blocks: their
-  // gathered rows are shared in that XCD's L2.  Late (long) blocks first.
-  const int t = lid / p.n_qt, b = p.n_qt - 1 - lid % p.n_qt;
+  // XCD k (workgroup id mod 8) takes the query blocks b = k mod 8 of every
+  // head, head after head, long blocks first: the workgroups resident on an
+  // XCD are blocks of one head (which select mostly the same clusters /
+  // blocks, so the rows they share come from that XCD's L2), and every XCD
+  // gets a share of short and long blocks of every head
+  const int xcd = blockIdx.x & 7, wg_slot = blockIdx.x >> 3;
+  const int nq8 = (p.n_qt + 7) / 8;
+  const int t = wg_slot / nq8;
+  const int b = p.n_qt - 1 - ((wg_slot % nq8) * 8 + xcd);
+  if (b < 0) return;   // padding of n_qt to a multiple of 8
   const int h = sl.head[t];
   const int g = h / p.G;
   const int q0 = b * BK;
@@ -770,7 +774,7 @@ hipError_t launch_permute_kv(const AttnParams& p, hipStream_t s) {
 }
 
 hipError_t launch_attn_selected(const AttnParams& p, const SelList& sl, hipStream_t s) {
-  const int nwg = sl.n_ret * p.n_qt;
+  const int nwg = sl.n_ret * ((p.n_qt + 7) / 8 * 8);
   if (nwg == 0 || (p.topk == 0 && !p.force_block0)) return hipSuccess;
   hipLaunchKernelGGL(attn_selected_kernel, dim3(nwg), dim3(NT), 0, s, p, sl);
   return hipGetLastError();
