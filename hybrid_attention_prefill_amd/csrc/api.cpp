@@ -28,7 +28,8 @@ int check_desc(const ha_layer_desc* d, const int32_t* kinds, Heads* out) {
   if (d->n_tokens < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1) return HA_ERR_ARG;
   if (d->n_q_heads % d->n_kv_heads != 0) return HA_ERR_ARG;
   if (d->head_dim < 1 || d->q_block < 1 || d->k_block < 1) return HA_ERR_ARG;
-  if (d->n_q_heads > kMaxHeads) return HA_ERR_UNSUPPORTED;
+  // head ids travel as bytes in the pack tables, 0xFF marking an empty slot
+  if (d->n_q_heads > kMaxHeads - 1) return HA_ERR_UNSUPPORTED;
   if (d->head_dim != kHeadDim) return HA_ERR_UNSUPPORTED;
   if (d->q_block != kBlock || d->k_block != kBlock) return HA_ERR_UNSUPPORTED;
   if (d->n_out < 0 || d->n_out > d->n_tokens) return HA_ERR_ARG;
@@ -654,7 +655,7 @@ int ha_attn_cross(const ha_layer_desc* desc, const void* Q, const void* K, const
       desc->n_q_heads % desc->n_kv_heads != 0 || desc->n_out < 1 || desc->n_out > desc->n_tokens)
     return HA_ERR_ARG;
   if (desc->head_dim != kHeadDim) return desc->head_dim < 1 ? HA_ERR_ARG : HA_ERR_UNSUPPORTED;
-  if (desc->n_q_heads > kMaxHeads) return HA_ERR_UNSUPPORTED;
+  if (desc->n_q_heads > kMaxHeads - 1) return HA_ERR_UNSUPPORTED;
   if (!Q || !K || !V || !xa_scale || !xa_offset || !O_out) return HA_ERR_ARG;
   if (!ws_ok(workspace, ws_bytes, cross_ws_bytes(desc))) return HA_ERR_WORKSPACE;
   return run_cross(desc, Q, K, V, xa_scale, xa_offset, O_out, static_cast<float*>(workspace),

@@ -11,7 +11,7 @@ namespace ha {
 constexpr int kHeadDim = 128;   // D
 constexpr int kRank = 16;       // r
 constexpr int kBlock = 64;      // q_block = k_block
-constexpr int kMaxHeads = 256;  // Hq limit (packs fit in a kernel argument)
+constexpr int kMaxHeads = 256;  // table size; Hq <= 255 (0xFF marks an empty pack slot)
 constexpr int kMaxTopk = 255;   // topk limit (the selected-key kernel keeps topk + 1 entries)
 constexpr int kMaxSelCand = 16384;  // eligible blocks/clusters scored per query block in LDS
 

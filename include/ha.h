@@ -70,7 +70,7 @@ typedef enum {
   HA_OK = 0,
   HA_ERR_ARG = 1,          /* null pointer, inconsistent sizes, bad head kind */
   HA_ERR_UNSUPPORTED = 2,  /* valid but not built: D != 128, r != 16, blocks != 64,
-                            * Hq > 256, topk > 255, more than 16384 candidate blocks
+                            * Hq > 255, topk > 255, more than 16384 candidate blocks
                             * or clusters, force_block0 with clusters, index_bits 8
                             * outside block mode with block_score 0 */
   HA_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than ha_workspace_bytes() */

@@ -56,6 +56,7 @@ def _band(desc, kinds, Q=FAKE, K=FAKE, V=FAKE, O=FAKE):
     (dict(window=0), [0] * 8, ha.HA_ERR_ARG),                             # SWA needs w >= 1
     (dict(sink=-1), [2] * 8, ha.HA_ERR_ARG),
     (dict(n_q_heads=512, n_kv_heads=2), [0] * 512, ha.HA_ERR_UNSUPPORTED),
+    (dict(n_q_heads=256, n_kv_heads=2), [0] * 256, ha.HA_ERR_UNSUPPORTED),  # head ids are bytes, 0xFF = empty
 ])
 def test_band_rejects(kw, kinds, code):
     assert _band(_desc(**kw), kinds) == code
