@@ -147,20 +147,26 @@ __global__ __launch_bounds__(NT) void km_assign_kernel(KmeansParams p) {
       for (int kt = 0; kt < KT; ++kt) acc[kt] = dev::mfma32_f16(ah, kl[kt], acc[kt]);
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) acc[kt] = dev::mfma32_f16(ah, kh[kt], acc[kt]);
+      float tmin[KT];
+      bool imp = false;
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
-        float tmin = acc[kt][0];
+        float tm = acc[kt][0];
 #pragma unroll
-        for (int e = 1; e < 15; e += 2) tmin = __builtin_fminf(__builtin_fminf(tmin, acc[kt][e]), acc[kt][e + 1]);
-        tmin = fminf(tmin, acc[kt][15]);
-        // rare once the scan is under way: some lane of this key block
-        // improves; its index is the lowest e holding the tile minimum
-        if (__any(tmin < best[kt])) {
+        for (int e = 1; e < 15; e += 2) tm = __builtin_fminf(__builtin_fminf(tm, acc[kt][e]), acc[kt][e + 1]);
+        tmin[kt] = fminf(tm, acc[kt][15]);
+        imp |= tmin[kt] < best[kt];
+      }
+      // rare once the scan is under way: some lane improves in some key
+      // block; its index is the lowest e holding the tile minimum
+      if (__any(imp)) {
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
           int idx = 15;
 #pragma unroll
-          for (int e = 14; e >= 0; --e) idx = acc[kt][e] == tmin ? e : idx;
-          if (tmin < best[kt]) {
-            best[kt] = tmin;
+          for (int e = 14; e >= 0; --e) idx = acc[kt][e] == tmin[kt] ? e : idx;
+          if (tmin[kt] < best[kt]) {
+            best[kt] = tmin[kt];
             arg[kt] = m0 + lh * 4 + (idx >> 2) * 8 + (idx & 3);
           }
         }
