@@ -94,6 +94,10 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
   return base + inc - v;
 }
 
+// Word 3 of a raw buffer resource on gfx9 parts (gfx950 included): 32-bit
+// data format, no swizzle.  Offsets at or past num_records read zeros.
+constexpr int kBufWord3 = 0x00020000;
+
 __device__ __forceinline__ uint32_t order_key(float f) {
   const uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);

@@ -443,14 +443,25 @@ __global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
   constexpr int kPre = 4;
   // A ring slot holds a tile's split centroids and, per lane, the first
   // member of its cluster (eligibility: a member <= lim).
+  // Buffer loads: the lane's offset inside a tile is fixed and the tile's
+  // offset is wave-uniform (scalar), so a load needs no vector address
+  // arithmetic.  Lanes of the last tile past cluster M-1 fall outside the
+  // resource's range and read zeros; their keys go to the dummy word.
+  const __amdgpu_buffer_rsrc_t rs_hi = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<__bf16*>(chi), 0, p.M * NPART * R * 2, dev::kBufWord3);
+  const __amdgpu_buffer_rsrc_t rs_lo = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<__bf16*>(clo), 0, p.M * NPART * R * 2, dev::kBufWord3);
+  const __amdgpu_buffer_rsrc_t rs_fm = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int32_t*>(fm), 0, p.M * 4, dev::kBufWord3);
   auto ld = [&](int x, dev::bf16x8 (&bh)[NPART], dev::bf16x8 (&bl)[NPART], int& f) {
-    const int m = min(p.M - 1, x * 32 + lr);
 #pragma unroll
     for (int part = 0; part < NPART; ++part) {
-      bh[part] = *reinterpret_cast<const dev::bf16x8*>(chi + ((size_t)m * NPART + part) * R + lh * 8);
-      bl[part] = *reinterpret_cast<const dev::bf16x8*>(clo + ((size_t)m * NPART + part) * R + lh * 8);
+      const int vo = (lr * NPART + part) * R * 2 + lh * 16;
+      const int so = x * 32 * NPART * R * 2;
+      bh[part] = __builtin_bit_cast(dev::bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs_hi, vo, so, 0));
+      bl[part] = __builtin_bit_cast(dev::bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs_lo, vo, so, 0));
     }
-    f = fm[m];
+    f = (int)__builtin_amdgcn_raw_buffer_load_b32(rs_fm, lr * 4, x * 32 * 4, 0);
   };
   dev::bf16x8 rbh[kPre][NPART], rbl[kPre][NPART];
   int rfm[kPre];
@@ -468,7 +479,8 @@ __global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
     // products just issued.  Key of a cluster: order key of the row max, 0 if
     // ineligible (no member <= lim); padding lanes store to a dummy word.
     dev::f32x16 pacc[2];
-    int pm = INT_MAX, pf = 0;
+    int pm = INT_MAX;
+    bool pel = false;
     auto finish = [&]() {
       float mx = -__builtin_inff();
 #pragma unroll
@@ -477,7 +489,7 @@ __global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
         for (int e = 0; e < 16; ++e) mx = fmaxf(mx, pacc[rt][e]);
       mx = dev::pair32_max(mx);
       const bool mok = pm < p.M;
-      const bool el = mok & (lim0 >= 0) & (pf <= lim0);
+      const bool el = mok & pel;
       const uint32_t key = el ? dev::order_key(mx) : 0u;
       uint32_t* dst = mok ? &keys[0][pm] : &sink_word;
       // later slots of a unit keep the max with what this lane stored before
@@ -506,7 +518,12 @@ __global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
             acc[rt] = dev::mfma32(qh[part][rt], rbh[u][part], acc[rt]);
           }
         }
-        const int fx = rfm[u];
+        // eligibility of the slot's cluster, taken before the slot's refill
+        // is issued (the empty asm orders the two), so the refill lands in the
+        // slot's own registers: no ring rotation copies, which would wait for
+        // the newest loads
+        const bool fel = (lim0 >= 0) & (rfm[u] <= lim0);
+        { const int fi = fel; asm volatile("" ::"v"(fi) : "memory"); }
         // keep the refill after the slot's last reads (no register rotation)
         __builtin_amdgcn_sched_barrier(0);
         ld(min(x + 4 * kPre, n_tiles - 1), rbh[u], rbl[u], rfm[u]);
@@ -514,7 +531,7 @@ __global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
         pacc[0] = acc[0];
         pacc[1] = acc[1];
         pm = x * 32 + lr;
-        pf = fx;
+        pel = fel;
         have = true;
       }
     }
