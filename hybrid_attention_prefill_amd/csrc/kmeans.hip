@@ -20,6 +20,8 @@
 
 #include <limits.h>
 
+#include <type_traits>
+
 namespace ha {
 namespace {
 
@@ -478,64 +480,79 @@ __global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
     // the next tile are issued, so the matrix-result reads never wait on the
     // products just issued.  Key of a cluster: order key of the row max, 0 if
     // ineligible (no member <= lim); padding lanes store to a dummy word.
-    dev::f32x16 pacc[2];
-    int pm = INT_MAX;
+    dev::f32x16 pacc[2] = {dev::f32x16{}, dev::f32x16{}};
+    int pm = INT_MAX;                 // the first finish stores 0 to the dummy word
     bool pel = false;
-    auto finish = [&]() {
-      float mx = -__builtin_inff();
+    // The loop is instantiated once for the first slot of a unit (plain
+    // store) and once for later slots (max with the stored key), so its body
+    // is one basic block and the previous tile's vector work can be placed
+    // between the current tile's matrix products.
+    auto run = [&](auto later_slot) {
+      constexpr bool kLater = decltype(later_slot)::value;
+      auto finish = [&]() {
+        float mx = -__builtin_inff();
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
+        for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, pacc[rt][e]);
-      mx = dev::pair32_max(mx);
-      const bool mok = pm < p.M;
-      const bool el = mok & pel;
-      const uint32_t key = el ? dev::order_key(mx) : 0u;
-      uint32_t* dst = mok ? &keys[0][pm] : &sink_word;
-      // later slots of a unit keep the max with what this lane stored before
-      if (s > 0) *dst = max(*dst, key);
-      else *dst = key;
-      gmx = max(gmx, key);
-      n_el[0] += (int)(el & (lh == 0) & (s == 0));
-    };
-    bool have = false;
-    // Groups of kPre tiles run whole (tiles past the end compute on the last
-    // tile and store nothing: their centroid index is >= M), so the body has no
-    // branches around loads.  A slot is refilled right after its MFMAs have
-    // consumed it, so the ring needs no register copies.
-    for (int x0 = wave; x0 < n_tiles; x0 += 4 * kPre) {
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, pacc[rt][e]);
+        mx = dev::pair32_max(mx);
+        const bool mok = pm < p.M;
+        const bool el = mok & pel;
+        const uint32_t key = el ? dev::order_key(mx) : 0u;
+        uint32_t* dst = mok ? &keys[0][pm] : &sink_word;
+        if constexpr (kLater) {
+          *dst = max(*dst, key);
+        } else {
+          *dst = key;
+          n_el[0] += (int)(el & (lh == 0));
+        }
+        gmx = max(gmx, key);
+      };
+      // Groups of kPre tiles run whole (tiles past the end compute on the
+      // last tile and store nothing: their centroid index is >= M), so the
+      // body has no branches around loads.
+      for (int x0 = wave; x0 < n_tiles; x0 += 4 * kPre) {
 #pragma unroll
-      for (int u = 0; u < kPre; ++u) {
-        const int x = x0 + 4 * u;
-        dev::f32x16 acc[2];
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-          acc[rt] = dev::f32x16{};
+        for (int u = 0; u < kPre; ++u) {
+          const int x = x0 + 4 * u;
+          // the two row tiles' chains alternate, so no product waits on the
+          // one just issued
+          dev::f32x16 acc[2] = {dev::f32x16{}, dev::f32x16{}};
 #pragma unroll
           for (int part = 0; part < NPART; ++part) {
-            acc[rt] = dev::mfma32(ql[part][rt], rbh[u][part], acc[rt]);
-            acc[rt] = dev::mfma32(qh[part][rt], rbl[u][part], acc[rt]);
-            acc[rt] = dev::mfma32(qh[part][rt], rbh[u][part], acc[rt]);
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) acc[rt] = dev::mfma32(ql[part][rt], rbh[u][part], acc[rt]);
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) acc[rt] = dev::mfma32(qh[part][rt], rbl[u][part], acc[rt]);
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) acc[rt] = dev::mfma32(qh[part][rt], rbh[u][part], acc[rt]);
           }
+          // eligibility of the slot's cluster, taken before the slot's refill
+          // is issued (the empty asm orders the two), so the refill lands in
+          // the slot's own registers: no ring rotation copies, which would
+          // wait for the newest loads
+          const bool fel = (lim0 >= 0) & (rfm[u] <= lim0);
+          { const int fi = fel; asm volatile("" ::"v"(fi) : "memory"); }
+          ld(min(x + 4 * kPre, n_tiles - 1), rbh[u], rbl[u], rfm[u]);
+          finish();
+          pacc[0] = acc[0];
+          pacc[1] = acc[1];
+          pm = x * 32 + lr;
+          pel = fel;
+          // products of this tile, the previous tile's vector work between
+          // them, then the slot's refill
+#pragma unroll
+          for (int i = 0; i < 6 * NPART; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x020, 2 * NPART + 1, 0);
         }
-        // eligibility of the slot's cluster, taken before the slot's refill
-        // is issued (the empty asm orders the two), so the refill lands in the
-        // slot's own registers: no ring rotation copies, which would wait for
-        // the newest loads
-        const bool fel = (lim0 >= 0) & (rfm[u] <= lim0);
-        { const int fi = fel; asm volatile("" ::"v"(fi) : "memory"); }
-        // keep the refill after the slot's last reads (no register rotation)
-        __builtin_amdgcn_sched_barrier(0);
-        ld(min(x + 4 * kPre, n_tiles - 1), rbh[u], rbl[u], rfm[u]);
-        if (have) finish();
-        pacc[0] = acc[0];
-        pacc[1] = acc[1];
-        pm = x * 32 + lr;
-        pel = fel;
-        have = true;
       }
-    }
-    if (have) finish();
+      finish();
+    };
+    if (s == 0) run(std::integral_constant<bool, false>{});
+    else run(std::integral_constant<bool, true>{});
   }
   if (lh == 0) gmax[wave * 32 + lr] = gmx;
   if (tid == 0) {
