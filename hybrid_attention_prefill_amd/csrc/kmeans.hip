@@ -153,10 +153,10 @@ __global__ __launch_bounds__(NT) void km_assign_kernel(KmeansParams p) {
       bool imp = false;
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
-        float tm = acc[kt][0];
+        float tm = __builtin_inff();
 #pragma unroll
-        for (int e = 1; e < 15; e += 2) tm = __builtin_fminf(__builtin_fminf(tm, acc[kt][e]), acc[kt][e + 1]);
-        tmin[kt] = fminf(tm, acc[kt][15]);
+        for (int e = 0; e < 16; e += 2) tm = __builtin_fminf(__builtin_fminf(tm, acc[kt][e]), acc[kt][e + 1]);
+        tmin[kt] = tm;
         imp |= tmin[kt] < best[kt];
       }
       // rare once the scan is under way: some lane improves in some key
