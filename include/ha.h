@@ -145,7 +145,15 @@ int ha_version(void);
  * head_kind (host) [Hq]. */
 size_t ha_workspace_bytes(const ha_layer_desc* desc, const int32_t* head_kind);
 
-/* Whole-layer prefill.  Runs, on `stream`: the indexer projection and
+/* Whole-layer prefill.
+ * Sources: "RTPurbo" post (most heads attend locally and run SWA; retrieval
+ * heads use a cheap 16-dim indexer to pick candidates and then exact
+ * attention over them in full dimension); "RTPurboV2" article (~15% retrieval
+ * heads, the rest SWA; all heads sparse when most are retrieval heads);
+ * TriangleMix introduction in the 36kr interview (streaming region + last Q-K
+ * region); Orthros page, "Prefilling" (all tokens SWA, output positions add
+ * full cross-attention).
+ * Runs, on `stream`: the indexer projection and
  * selection for retrieval heads (k-means first in cluster mode), the banded /
  * dense / triangle kernels for the other heads, the gather kernel for the
  * retrieval heads, and Orthros cross-attention for the last n_out rows.
@@ -202,19 +210,37 @@ int ha_kmeans(const ha_layer_desc* desc, const float* klow, float* centroids,
               int32_t* assign, int32_t* csr_off, int32_t* csr_mem,
               void* workspace, size_t ws_bytes, void* stream);
 
-/* Stage: cluster scoring + top-k.  Eligible clusters have a member
- * j <= qe_b - window; score = max over the block's rows of qlow_i . C_m. */
+/* Stage: cluster scoring + top-k ("RTPurboV2" article, clustering passage:
+ * whole clusters of semantically unrelated keys are skipped; 36kr interview,
+ * top-k matching answer: candidates are scored through a representative and
+ * the top-k kept).  Eligible clusters have a member j <= qe_b - window;
+ * score = max over the block's rows of qlow_i . C_m; keeps the topk best by
+ * (score desc, cluster asc), written ascending, -1 padded.
+ *   centroids [Hkv, M, r]; csr_off, csr_mem as ha_kmeans writes them;
+ *   sel [Hret, n_qb, topk];
+ *   workspace >= ha_workspace_bytes(desc, head_kind) bytes, 256-byte aligned
+ *             (split centroids and each cluster's first member). */
 int ha_select_clusters(const ha_layer_desc* desc, const int32_t* head_kind,
                        const float* qlow, const float* centroids,
                        const int32_t* csr_off, const int32_t* csr_mem,
                        int32_t* sel, void* workspace, size_t ws_bytes, void* stream);
 
-/* Stage: SWA, dense and TriangleMix heads of head_kind (others untouched). */
+/* Stage: SWA, dense and TriangleMix heads of head_kind (others untouched).
+ * Sources: "RTPurboV2" article (streaming heads use a sliding window, 8192 in
+ * deployment); Orthros page, "Prefilling" (every prompt token runs SWA);
+ * TriangleMix introduction in the 36kr interview (sink keys + local band,
+ * and the last query rows attend to every earlier key).  Key sets as in
+ * ha_head_kind; exact softmax, bf16 products, fp32 statistics and output.
+ *   workspace  unused (may be NULL). */
 int ha_attn_band(const ha_layer_desc* desc, const int32_t* head_kind,
                  const void* Q, const void* K, const void* V, float* O,
                  void* workspace, size_t ws_bytes, void* stream);
 
 /* Stage: retrieval heads: window U selected keys (U key block 0 when forced).
+ * Sources: "RTPurbo" post (after the indexer's scouting, exact softmax
+ * attention over the candidate keys in full dimension); "RTPurboV2" article,
+ * clustering passage (a selected cluster brings all its member keys); 36kr
+ * interview, GQA answer (one selection can serve a GQA group).
  * Block mode reads sel only; cluster mode also reads assign/csr.
  *   csr_off, csr_mem: NULL in block mode; in cluster mode a valid CSR (each
  *              cluster's members ascending, positions in [0, N)).

@@ -34,9 +34,9 @@ from .attention import (  # noqa: F401
 )
 from .indexer import (  # noqa: F401
     project, eligible_blocks, block_scores, topk_order, select_blocks,
-    eligible_clusters, cluster_scores, select_clusters,
+    eligible_clusters, cluster_scores,
 )
 from .kmeans import lloyd, assign_step, update_step, kmeans_objective  # noqa: F401
 from .prefill import (  # noqa: F401
-    head_group, retrieval_key_set, layer_prefill, orthros_cross, OracleResult,
+    head_group, static_key_candidates, retrieval_key_set, layer_prefill, orthros_cross, OracleResult,
 )

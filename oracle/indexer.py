@@ -161,21 +161,3 @@ def cluster_scores(qlow_rows: np.ndarray, C: np.ndarray, clusters: np.ndarray) -
     if clusters.size == 0:
         return np.zeros(0)
     return np.max(qlow_rows @ C[clusters].T, axis=0)
-
-
-def select_clusters(qlow_h: np.ndarray, C: np.ndarray, assign: np.ndarray, N: int,
-                    w: int, Bq: int, k: int, blocks=None):
-    """Per query block (all, or the listed ones): selected clusters and the
-    scores of the eligible ones."""
-    M = C.shape[0]
-    n_qb = (N + Bq - 1) // Bq
-    blocks = range(n_qb) if blocks is None else blocks
-    sel, scored = {}, {}
-    for b in blocks:
-        rows = np.arange(b * Bq, min(N, (b + 1) * Bq), dtype=np.int64)
-        qe = int(rows[-1])
-        E = eligible_clusters(assign, M, qe, w)
-        s = cluster_scores(qlow_h[rows], C, E)
-        sel[b] = topk_order(s, E, k)
-        scored[b] = (E, s)
-    return sel, scored

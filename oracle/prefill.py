@@ -45,6 +45,25 @@ def head_group(h: int, Hq: int, Hkv: int) -> int:
     return h // (Hq // Hkv)
 
 
+def static_key_candidates(kind: int, r0: int, r1: int, N: int, w: int, sink: int, last: int) -> np.ndarray:
+    """Key ids that can be visible to some query row in [r0, r1) under a static
+    mask (a superset of each row's key set; the exact mask is applied on top):
+      DENSE     0 .. r1-1
+      SWA(w)    r0-w+1 .. r1-1 (clipped at 0)
+      TRIANGLE  rows reaching the last L rows: 0 .. r1-1; otherwise the sink
+                keys 0 .. sink-1 and the band r0-w+1 .. r1-1.
+    Pinned by a layer-level N x N brute force against the masks' definitions
+    (tests/test_oracle_prefill.py)."""
+    if kind == DENSE or (kind == TRIANGLE and r1 > N - last):
+        return np.arange(0, r1, dtype=np.int64)
+    band = np.arange(max(0, r0 - w + 1), r1, dtype=np.int64)
+    if kind == SWA:
+        return band
+    if kind == TRIANGLE:
+        return np.unique(np.r_[np.arange(0, min(sink, r1), dtype=np.int64), band])
+    raise ValueError(f"no static key set for head kind {kind}")
+
+
 def retrieval_key_set(rows: np.ndarray, w: int, Bk: int, f0: int, *,
                       blocks: Optional[np.ndarray] = None,
                       clusters: Optional[np.ndarray] = None,
@@ -100,7 +119,10 @@ class OracleResult:
 def orthros_cross(q: np.ndarray, s: np.ndarray, o: np.ndarray, K: np.ndarray,
                   V: np.ndarray, p: int, scale: float) -> np.ndarray:
     """Cross-attention of the scale-offset query at output position p over
-    keys {0..p}.  Pinned: s = 1, o = 0 gives the dense causal row p."""
+    keys {0..p}.  Pinned: s = 1, o = 0 gives the dense causal row p; a
+    hand-worked two-key case; Q = 0 gives the softmax of o over the keys; s = 2,
+    o = 0 gives the dense row at twice the scale (planted "q * s" and
+    "(q + o) * s" fail these)."""
     qp = np.asarray(q, np.float64) * np.asarray(s, np.float64) + np.asarray(o, np.float64)
     keys = np.arange(p + 1)
     vis = np.ones((1, p + 1), dtype=bool)
@@ -206,18 +228,14 @@ def layer_prefill(w, q_rows: Callable[[int, int], np.ndarray], K: np.ndarray, V:
             kind = w.head_kind[h]
             q = Qb[:, h]
             if kind == DENSE:
-                keys = np.arange(0, r1)
+                keys = static_key_candidates(DENSE, r0, r1, N, w.window, w.sink, w.last_q)
                 o = attend_rows(q, rows, K[:, g], V[:, g], keys, visible_dense, sc)
             elif kind == SWA:
-                keys = np.arange(max(0, r0 - w.window + 1), r1)
+                keys = static_key_candidates(SWA, r0, r1, N, w.window, w.sink, w.last_q)
                 o = attend_rows(q, rows, K[:, g], V[:, g], keys,
                                 lambda ri, kj: visible_swa(ri, kj, w.window), sc)
             elif kind == TRIANGLE:
-                if r1 > N - w.last_q:
-                    keys = np.arange(0, r1)
-                else:
-                    keys = np.unique(np.r_[np.arange(0, min(w.sink, r1)),
-                                           np.arange(max(0, r0 - w.window + 1), r1)])
+                keys = static_key_candidates(TRIANGLE, r0, r1, N, w.window, w.sink, w.last_q)
                 o = attend_rows(q, rows, K[:, g], V[:, g], keys,
                                 lambda ri, kj: visible_triangle(ri, kj, N, w.sink, w.window, w.last_q), sc)
             elif kind == RETRIEVAL:
