@@ -121,6 +121,30 @@ def dequantize_keys(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
     return codes.astype(np.float64) * np.asarray(scale, dtype=np.float64)[:, None]
 
 
+def topk_adaptive(scores: np.ndarray, ids: np.ndarray, k: int, mass: float, scale: float) -> np.ndarray:
+    """Adaptive budget ([RTPurboV2], fixed-top-k passage: different heads,
+    sequence lengths and queries need very different numbers of context
+    tokens; the method that follows that passage is missing from the page, so
+    this rule is a proposal, not the page's).  The k best ids by (score desc,
+    id asc) are the budget; of them, keep the shortest prefix in that order
+    whose share of sum_j exp(scale * s_j) over the k reaches `mass`.  mass <= 0
+    or >= 1 keeps all k (fixed top-k).  Returned in ascending id order.
+    Pinned: mass >= 1 equals topk_order; a hand-worked three-candidate case;
+    equal scores keep ceil(mass * k)."""
+    ids = np.asarray(ids, dtype=np.int64)
+    scores = np.asarray(scores, dtype=np.float64)
+    if k <= 0 or ids.size == 0:
+        return np.zeros(0, dtype=np.int64)
+    order = np.lexsort((ids, -scores))[:k]
+    if mass <= 0.0 or mass >= 1.0:
+        return np.sort(ids[order])
+    s = scores[order]
+    wts = np.exp(scale * (s - s[0]))          # s[0] is the largest score
+    share = np.cumsum(wts) / np.sum(wts)
+    n = int(np.nonzero(share >= mass)[0][0]) + 1 if np.any(share >= mass) else order.size
+    return np.sort(ids[order[:n]])
+
+
 def topk_order(scores: np.ndarray, ids: np.ndarray, k: int) -> np.ndarray:
     """The k best ids by (score desc, id asc), returned in ascending id order.
     Pinned: exact ties planted by duplicated key blocks keep the lower ids."""

@@ -34,7 +34,7 @@ import numpy as np
 from .attention import attend_rows, softmax_attention, visible_dense, visible_swa, visible_triangle
 from .indexer import (block_extremes, block_means, block_scores, block_scores_mean, block_scores_minmax,
                       cluster_scores, dequantize_keys, eligible_blocks, eligible_clusters, project,
-                      quantize_keys_int8, topk_order)
+                      quantize_keys_int8, topk_adaptive, topk_order)
 from .kmeans import lloyd
 
 SWA, RETRIEVAL, TRIANGLE, DENSE = 0, 1, 2, 3
@@ -186,6 +186,16 @@ def layer_prefill(w, q_rows: Callable[[int, int], np.ndarray], K: np.ndarray, V:
             res.kcodes[g] = (codes, s)
             rep_klow[g] = dequantize_keys(codes, s)
 
+    def choose(scores, E):
+        """The selection S_b from the eligible candidates' scores: fixed top-k,
+        or the adaptive budget (topk_mass > 0) with the indexer softmax scale
+        mass_scale (<= 0: 1/sqrt(r), the scaled dot product of the rank-r
+        space)."""
+        if w.topk_mass > 0:
+            ms = w.mass_scale if w.mass_scale > 0 else 1.0 / np.sqrt(w.rank)
+            return topk_adaptive(scores, E, w.topk, w.topk_mass, ms)
+        return topk_order(scores, E, w.topk)
+
     eligible_memo = {}   # (KV head, block) -> eligible clusters (shared by the group's heads)
     group_memo = {}      # (KV head, block) -> (eligible, group scores, selection)
     rep_memo = {}        # block representatives per KV head
@@ -245,10 +255,10 @@ def layer_prefill(w, q_rows: Callable[[int, int], np.ndarray], K: np.ndarray, V:
                     if (g, b) not in group_memo:
                         sg = np.max(np.stack([scores_for(hh, g, b, Qb, rows, qe)[2]
                                               for hh in ret_of_group[g]]), axis=0) if E.size else s
-                        group_memo[(g, b)] = (sg, topk_order(sg, E, w.topk))
+                        group_memo[(g, b)] = (sg, choose(sg, E))
                     s, S = group_memo[(g, b)]
                 else:
-                    S = topk_order(s, E, w.topk)
+                    S = choose(s, E)
                 if sel_override is not None:
                     S = np.asarray(sel_override[h][b], dtype=np.int64)
                 if w.n_clusters > 0:

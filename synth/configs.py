@@ -52,6 +52,11 @@ class Workload:
     # low-rank key storage of the block scores: 0 fp32, 8 int8 codes with one
     # fp32 scale per key (max-pair block scores only)
     index_bits: int = 0
+    # adaptive budget: 0 keeps the fixed top-k; in (0, 1) each query block
+    # keeps the shortest prefix of its top-k (score desc) whose softmax share,
+    # at scale mass_scale (0: 1/sqrt(rank)), reaches topk_mass
+    topk_mass: float = 0.0
+    mass_scale: float = 0.0
     # input recipe: "plain", "planted_lowfreq" (keys carry per-segment topic
     # vectors on the low-frequency dims), "needles" (planted key/query pairs)
     recipe: str = "plain"
@@ -140,13 +145,20 @@ ALLSPARSE_1M = Workload(
 # heads share one top-64 cluster selection per query block.
 ALLSPARSE_1M_GQA = ALLSPARSE_1M.with_(name="allsparse_1m_gqa", group_select=1)
 
+# Adaptive budget (a proposal; the page states only the need): the top-k is a
+# budget, and each query block keeps the shortest prefix of it, by score,
+# whose softmax share at scale 1/sqrt(r) reaches 0.9.
+QWEN3_30B_32K_ADAPTIVE = QWEN3_30B_32K.with_(name="qwen3_30b_a3b_32k_adaptive", topk_mass=0.9)
+ALLSPARSE_1M_ADAPTIVE = ALLSPARSE_1M.with_(name="allsparse_1m_adaptive", topk_mass=0.9)
+
 # The TriangleMix layer split: 12 dense shallow layers, 20 triangle layers.
 TRIANGLE_LAYER_SPLIT = (12, 20)
 
 WORKLOADS = {w.name: w for w in (
     TINY_HYBRID_2K, QWEN3_30B_32K, QWEN3_30B_32K_MEAN, QWEN3_30B_32K_MINMAX, QWEN3_30B_32K_INT8,
     TRIANGLE_8B_128K, DENSE_8B_128K,
-    ORTHROS_8B_128K, ORTHROS_8B_128K_SFT, ALLSPARSE_1M, ALLSPARSE_1M_GQA)}
+    ORTHROS_8B_128K, ORTHROS_8B_128K_SFT, ALLSPARSE_1M, ALLSPARSE_1M_GQA,
+    QWEN3_30B_32K_ADAPTIVE, ALLSPARSE_1M_ADAPTIVE)}
 
 
 def shrink(w: Workload, n_tokens: int, *, n_clusters: Optional[int] = None,
