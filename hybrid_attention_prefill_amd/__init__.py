@@ -38,6 +38,7 @@ class LayerDesc(ctypes.Structure):
         ("kmeans_stride", ctypes.c_int32), ("sink", ctypes.c_int32),
         ("last_q", ctypes.c_int32), ("n_out", ctypes.c_int32),
         ("group_select", ctypes.c_int32), ("block_score", ctypes.c_int32), ("index_bits", ctypes.c_int32),
+        ("topk_mass", ctypes.c_float), ("mass_scale", ctypes.c_float),
     ]
 
 
@@ -130,10 +131,11 @@ def _stream(stream) -> Optional[int]:
 def make_desc(n_tokens, n_q_heads, n_kv_heads, head_dim=128, *, softmax_scale=0.0, window=0, rank=16,
               q_block=64, k_block=64, topk=0, force_block0=0, n_clusters=0, kmeans_iters=0,
               kmeans_stride=0, sink=0, last_q=0, n_out=0, group_select=0, block_score=0,
-              index_bits=0) -> LayerDesc:
+              index_bits=0, topk_mass=0.0, mass_scale=0.0) -> LayerDesc:
     return LayerDesc(n_tokens, n_q_heads, n_kv_heads, head_dim, float(softmax_scale or 0.0), window, rank,
                      q_block, k_block, topk, int(force_block0), n_clusters, kmeans_iters, kmeans_stride,
-                     sink, last_q, n_out, int(group_select), int(block_score), int(index_bits))
+                     sink, last_q, n_out, int(group_select), int(block_score), int(index_bits),
+                     float(topk_mass), float(mass_scale))
 
 
 def _kinds(head_kind: Sequence[int]):
@@ -145,11 +147,13 @@ def ha_workspace_bytes(desc: LayerDesc, head_kind: Sequence[int]) -> int:
     return int(lib().ha_workspace_bytes(ctypes.byref(desc), _kinds(head_kind)))
 
 
+def _aux(aux):
+    return None if aux is None else Aux(*[_ptr(aux.get(f)) for f, _ in Aux._fields_])
+
+
 def ha_prefill(desc, head_kind, Q, K, V, P_idx, xa_scale, xa_offset, O, O_out, aux=None,
                workspace=None, ws_bytes=None, stream=None):
-    a = None
-    if aux is not None:
-        a = Aux(*[_ptr(aux.get(f)) for f, _ in Aux._fields_])
+    a = _aux(aux)
     if ws_bytes is None:
         ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().ha_prefill(ctypes.byref(desc), _kinds(head_kind), _ptr(Q), _ptr(K), _ptr(V), _ptr(P_idx),
@@ -219,7 +223,8 @@ def ha_attn_cross(desc, Q, K, V, xa_scale, xa_offset, O_out, workspace=None, ws_
 
 def hybrid_attn_prefill(Q, K, V, head_kind, window, P_idx=None, topk=0, block=64, *, force_block0=False,
                         n_clusters=0, kmeans_iters=10, kmeans_stride=64, sink=0, last_q=0, n_out=0,
-                        group_select=False, block_score=0, index_bits=0, xa_scale=None, xa_offset=None,
+                        group_select=False, block_score=0, index_bits=0, topk_mass=0.0, mass_scale=0.0,
+                        xa_scale=None, xa_offset=None,
                         softmax_scale=None, out=None, out_cross=None, workspace=None, return_aux=False):
     """One layer's hybrid attention prefill on the current HIP stream.
 
@@ -237,7 +242,7 @@ def hybrid_attn_prefill(Q, K, V, head_kind, window, P_idx=None, topk=0, block=64
                      n_clusters=n_clusters, kmeans_iters=kmeans_iters if n_clusters else 0,
                      kmeans_stride=kmeans_stride if n_clusters else 0, sink=sink, last_q=last_q, n_out=n_out,
                      group_select=int(bool(group_select)), block_score=int(block_score),
-                     index_bits=int(index_bits))
+                     index_bits=int(index_bits), topk_mass=topk_mass, mass_scale=mass_scale)
     dev = Q.device
     O = out if out is not None else torch.empty((N, Hq, D), dtype=torch.float32, device=dev)
     O_out = None

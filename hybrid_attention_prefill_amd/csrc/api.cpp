@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <vector>
 
 #include "common.h"
@@ -40,6 +41,7 @@ int check_desc(const ha_layer_desc* d, const int32_t* kinds, Heads* out) {
   if (d->index_bits != 0 && d->index_bits != 8 && d->index_bits != 32) return HA_ERR_ARG;
   // 8-bit keys are built for the max-pair block scores
   if (d->index_bits == 8 && (d->n_clusters > 0 || d->block_score != 0)) return HA_ERR_UNSUPPORTED;
+  if (!(d->topk_mass >= 0.f) || !std::isfinite(d->topk_mass) || !std::isfinite(d->mass_scale)) return HA_ERR_ARG;
   Heads h;
   h.ret_slot.assign(d->n_q_heads, -1);
   bool need_window = false, any_tri = false;
@@ -111,7 +113,7 @@ size_t cross_ws_bytes(const ha_layer_desc* d) {
 }
 
 struct Layout {
-  size_t qlow, klow, sel, lse, cent, assign, csr_off, csr_mem, km_scratch, kvc, rep, kq, cross, total;
+  size_t qlow, klow, sel, lse, cent, assign, csr_off, csr_mem, km_scratch, kvc, rep, kq, cross, band, total;
 };
 
 // 8-bit indexer keys: int8 codes [Hkv, N, r] then fp32 scales [Hkv, N].
@@ -165,6 +167,8 @@ Layout layout_of(const ha_layer_desc* d, const Heads& h) {
   off += Hret ? kq_bytes(d) : 0;
   L.cross = off;
   off += cross_ws_bytes(d);
+  L.band = off;              // item counters of the persistent banded kernel
+  off += kAlign;
   L.total = off;
   return L;
 }
@@ -271,7 +275,7 @@ AttnParams attn_params(const ha_layer_desc* d, const void* Q, const void* K, con
 }
 
 int run_band(const ha_layer_desc* d, const int32_t* kinds, const void* Q, const void* K, const void* V,
-             float* O, hipStream_t s) {
+             float* O, uint32_t* ctr, hipStream_t s) {
   AttnParams p = attn_params(d, Q, K, V, O);
   static const int band_kinds[3] = {TRIANGLE, DENSE, SWA};
   for (int kind : band_kinds) {
@@ -280,7 +284,7 @@ int run_band(const ha_layer_desc* d, const int32_t* kinds, const void* Q, const 
     if (pt.n == 0) continue;
     order_band_packs(&pt, &p);
     p.kind = kind;
-    const int st = dev_status(launch_attn_band(p, pt, s));
+    const int st = dev_status(launch_attn_band(p, pt, ctr, s));
     if (st != HA_OK) return st;
   }
   return HA_OK;
@@ -319,6 +323,14 @@ int run_project(const ha_layer_desc* d, const Heads& h, const void* Q, const voi
   return HA_OK;
 }
 
+// Adaptive budget of the selection kernels (off unless 0 < topk_mass < 1).
+void fill_mass(const ha_layer_desc* d, SelectParams* sp) {
+  const bool on = d->topk_mass > 0.f && d->topk_mass < 1.f;
+  sp->mass = on ? d->topk_mass : 0.f;
+  const float sc = d->mass_scale > 0.f ? d->mass_scale : 1.0f / sqrtf((float)kRank);
+  sp->mass_scale_log2 = sc * 1.4426950408889634f;
+}
+
 // Selection units: one per retrieval slot, or one per KV group in
 // group-shared mode (slots are numbered in head order, so a group's slots
 // are consecutive).
@@ -349,6 +361,7 @@ int run_select_blocks(const ha_layer_desc* d, const Heads& h, const float* qlow,
   sp.n_ret = (int)h.ret.size();
   for (int t = 0; t < sp.n_ret; ++t) sp.group_of_ret[t] = h.ret[t] / G;
   fill_units(d, h, &sp);
+  fill_mass(d, &sp);
   if (d->index_bits == 8) {
     const size_t rows = (size_t)d->n_kv_heads * d->n_tokens;
     int8_t* codes = static_cast<int8_t*>(kq);
@@ -373,7 +386,7 @@ int run_select_blocks(const ha_layer_desc* d, const Heads& h, const float* qlow,
 // group-shared selection one kernel computes both parts.
 int run_gather(const ha_layer_desc* d, const int32_t* kinds, const Heads& h, const void* Q, const void* K,
                const void* V, const int32_t* sel, const int32_t* csr_off, const int32_t* csr_mem, float* O,
-               float* lse, void* kvc, hipStream_t s) {
+               float* lse, void* kvc, uint32_t* ctr, hipStream_t s) {
   if (h.ret.empty()) return HA_OK;
   AttnParams p = attn_params(d, Q, K, V, O);
   PackTable pt;
@@ -396,7 +409,7 @@ int run_gather(const ha_layer_desc* d, const int32_t* kinds, const Heads& h, con
   p.lse = lse;
   PackTable bt = pt;
   order_band_packs(&bt, &p);
-  st = dev_status(launch_attn_band(p, bt, s));
+  st = dev_status(launch_attn_band(p, bt, ctr, s));
   if (st != HA_OK) return st;
   p.kind = RETRIEVAL;
   SelList sl;
@@ -424,6 +437,7 @@ int run_kmeans(const ha_layer_desc* d, const float* klow, float* cent, int32_t* 
   // 16-byte vector loads read the split centroids: start them on an aligned address
   kp.c_hi = reinterpret_cast<_Float16*>(align_up(reinterpret_cast<uintptr_t>(kp.c_norm + Hkv * M)));
   kp.c_lo = kp.c_hi + Hkv * M * kRank;
+  kp.amax = reinterpret_cast<uint32_t*>(kp.c_lo + Hkv * M * kRank);
   return dev_status(launch_kmeans(kp, d->n_kv_heads, d->kmeans_iters, s));
 }
 
@@ -445,6 +459,7 @@ int run_select_clusters(const ha_layer_desc* d, const Heads& h, const float* qlo
   sp.n_ret = (int)h.ret.size();
   for (int t = 0; t < sp.n_ret; ++t) sp.group_of_ret[t] = h.ret[t] / G;
   fill_units(d, h, &sp);
+  fill_mass(d, &sp);
   const size_t nparts = (size_t)d->n_kv_heads * d->n_clusters * kRank;
   sp.c_hi = static_cast<__bf16*>(scratch);
   sp.c_lo = sp.c_hi + nparts;
@@ -547,11 +562,11 @@ int ha_prefill(const ha_layer_desc* desc, const int32_t* head_kind, const void* 
       if (st != HA_OK) return st;
     }
     st = run_gather(desc, head_kind, h, Q, K, V, sel, off, mem, O, reinterpret_cast<float*>(ws_at(workspace, L.lse)),
-                    ws_at(workspace, L.kvc), s);
+                    ws_at(workspace, L.kvc), reinterpret_cast<uint32_t*>(ws_at(workspace, L.band)), s);
     if (st != HA_OK) return st;
   }
   if (h.any_band) {
-    st = run_band(desc, head_kind, Q, K, V, O, s);
+    st = run_band(desc, head_kind, Q, K, V, O, reinterpret_cast<uint32_t*>(ws_at(workspace, L.band)), s);
     if (st != HA_OK) return st;
   }
   if (desc->n_out > 0) {
@@ -625,12 +640,12 @@ int ha_select_clusters(const ha_layer_desc* desc, const int32_t* head_kind, cons
 
 int ha_attn_band(const ha_layer_desc* desc, const int32_t* head_kind, const void* Q, const void* K, const void* V,
                  float* O, void* workspace, size_t ws_bytes, void* stream) {
-  (void)workspace; (void)ws_bytes;
   Heads h;
   int st = check_desc(desc, head_kind, &h);
   if (st != HA_OK) return st;
   if (!Q || !K || !V || !O) return HA_ERR_ARG;
-  return run_band(desc, head_kind, Q, K, V, O, static_cast<hipStream_t>(stream));
+  if (!ws_ok(workspace, ws_bytes, kAlign)) return HA_ERR_WORKSPACE;
+  return run_band(desc, head_kind, Q, K, V, O, static_cast<uint32_t*>(workspace), static_cast<hipStream_t>(stream));
 }
 
 int ha_attn_gather(const ha_layer_desc* desc, const int32_t* head_kind, const void* Q, const void* K,
@@ -643,9 +658,11 @@ int ha_attn_gather(const ha_layer_desc* desc, const int32_t* head_kind, const vo
   if (!Q || !K || !V || !O || (desc->topk > 0 && !sel)) return HA_ERR_ARG;
   if (desc->n_clusters > 0 && (!csr_off || !csr_mem)) return HA_ERR_ARG;
   const size_t lse_bytes = align_up(h.ret.size() * (size_t)desc->n_tokens * sizeof(float));
-  if (!ws_ok(workspace, ws_bytes, lse_bytes + kvc_bytes(desc))) return HA_ERR_WORKSPACE;
+  const size_t kvc = kvc_bytes(desc);
+  if (!ws_ok(workspace, ws_bytes, lse_bytes + kvc + kAlign)) return HA_ERR_WORKSPACE;
   return run_gather(desc, head_kind, h, Q, K, V, sel, csr_off, csr_mem, O, static_cast<float*>(workspace),
-                    ws_at(workspace, lse_bytes), static_cast<hipStream_t>(stream));
+                    ws_at(workspace, lse_bytes), reinterpret_cast<uint32_t*>(ws_at(workspace, lse_bytes + kvc)),
+                    static_cast<hipStream_t>(stream));
 }
 
 int ha_attn_cross(const ha_layer_desc* desc, const void* Q, const void* K, const void* V, const float* xa_scale,

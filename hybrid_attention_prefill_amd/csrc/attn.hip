@@ -30,6 +30,8 @@
 
 #include <limits.h>
 
+#include <algorithm>
+
 namespace ha {
 namespace {
 
@@ -450,57 +452,170 @@ __device__ __forceinline__ void run_tiles(const AttnParams& p, uint16_t* smem, i
   }
 }
 
-__global__ __launch_bounds__(NT, 1) void attn_band_kernel(AttnParams p, PackTable packs) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM_ELEMS];
-  const int wave = threadIdx.x >> 6;
-  const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  // pack class c (workgroup-uniform): packs of 4 >> c heads, 64 << c query
-  // rows per workgroup; wave w takes head slot w % (4 >> c) and the 32 rows
-  // of row group w / (4 >> c)
-  int c = 0, pk = 0, qt = 0, nq = 1;
-  {
-    int rem = lid, base = 0;
-    for (; c < 3; ++c) {
-      nq = (p.N + (BK << c) - 1) / (BK << c);
-      const int nwg = p.band_np[c] * nq;
-      if (rem < nwg) break;
-      rem -= nwg;
-      base += p.band_np[c];
-    }
-    if (c == 3) return;   // past the last class (the grid is sized exactly)
-    pk = base + rem / nq;
-    qt = rem % nq;
+// A band work item: one pack of heads x one tile of query rows (64 rows of
+// 4 heads, 128 of 2 or 256 of 1), with its closed-form key-tile schedule:
+// tiles idx < st are the sink tiles idx * 64, the rest the band tiles
+// bl + idx - st (no tile without a visible key for some row of the item).
+struct BandItem {
+  int valid;
+  int pk;         // pack
+  int sh;         // log2 of the heads per pack
+  int qt0;        // first query row
+  int g;          // KV head
+  int bl, st, T;  // tile schedule
+};
+
+// Item lid in the launch's order: pack classes in turn (4-, 2-, 1-head
+// packs), pack by pack, and inside a pack the row tiles from the last (the
+// longest causal rows) to the first for dense and triangle heads.
+__device__ __forceinline__ BandItem band_item(const AttnParams& p, const PackTable& packs, int lid) {
+  BandItem it{};
+  if (lid < 0) return it;
+  int c = 0, rem = lid, base = 0, nq = 1;
+  for (; c < 3; ++c) {
+    nq = (p.N + (BK << c) - 1) / (BK << c);
+    const int nwg = p.band_np[c] * nq;
+    if (rem < nwg) break;
+    rem -= nwg;
+    base += p.band_np[c];
   }
-  if (p.kind != SWA) qt = nq - 1 - qt;     // long causal rows first
-  const int sh = 2 - c;                    // log2 of the heads per pack
-  const int hs = wave & ((1 << sh) - 1);   // head slot in the pack
-  const int rows = BK << c;                // query rows of the workgroup
-  const uint32_t pw = packs.heads[pk];
-  const int h = (pw >> (8 * hs)) & 0xFF;
-  const int g = (int)(pw & 0xFF) / p.G;
-  const int qt0 = qt * rows;               // first row of the workgroup
-  const int q0 = qt0 + QW * (wave >> sh);  // first row of this wave
-  const bool active = h != 0xFF && q0 < p.N;
-  const int hi_t = min(p.N - 1, qt0 + rows - 1) >> 6;
+  if (c == 3) return it;
+  it.valid = 1;
+  it.pk = base + rem / nq;
+  int qt = rem % nq;
+  if (p.kind != SWA) qt = nq - 1 - qt;
+  it.sh = 2 - c;
+  const int rows = BK << c;
+  it.qt0 = qt * rows;
+  it.g = (int)(packs.heads[it.pk] & 0xFF) / p.G;
+  const int hi_t = min(p.N - 1, it.qt0 + rows - 1) >> 6;
+  if (p.kind == SWA) {
+    it.bl = max(0, it.qt0 - p.window + 1) >> 6;
+  } else if (p.kind == TRIANGLE && it.qt0 + rows - 1 < p.dense_from) {
+    it.bl = max(0, it.qt0 - p.window + 1) >> 6;
+    it.st = min((p.sink + 63) >> 6, it.bl);
+  }
+  it.T = it.st + (hi_t - it.bl + 1);
+  return it;
+}
+
+__device__ __forceinline__ int item_k0(const BandItem& it, int idx) {
+  return (idx < it.st ? idx : it.bl + idx - it.st) * BK;
+}
+
+// Persistent banded / dense / triangle kernel.  Every workgroup (one per CU)
+// takes items of its XCD's share of the launch order (XCD x = workgroup id
+// mod nx serves a contiguous range of items, so the items resident on one XCD
+// are neighbouring row tiles of one pack, whose band tiles overlap in its
+// L2): first three fixed items (its rank, + the XCD's workgroup count, + twice
+// that), then one item at a time from the XCD's counter, so long items (the
+// dense last rows of a triangle layer come first in the order) spread over
+// workgroups and the rest balance around them.  The K/V tile pipeline runs
+// across item boundaries: the next item's first tiles are staged while the
+// current item's last tiles compute, so a new item starts without waiting
+// for its first tile.  Three items are known at any time (the one computing
+// and the next two): the pipeline looks at most two tiles ahead.
+__global__ __launch_bounds__(NT, 1) void attn_band_kernel(AttnParams p, PackTable packs, uint32_t* ctr,
+                                                          int n_items) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM_ELEMS];
+  __shared__ int s_next;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = tid >> 6;
+  const int nx = min(8, (int)gridDim.x);
+  const int x = blockIdx.x % nx, j = blockIdx.x / nx;
+  const int nW = ((int)gridDim.x - x + nx - 1) / nx;      // workgroups of this XCD share
+  const int per = n_items / nx, rem = n_items % nx;
+  const int lo = x * per + min(x, rem), hi = lo + per + (x < rem ? 1 : 0);
+  auto item_id = [&](int k) { return k < hi ? k : -1; };
+
+  BandItem I0 = band_item(p, packs, item_id(lo + j));
+  if (!I0.valid) return;
+  BandItem I1 = band_item(p, packs, item_id(lo + j + nW));
+  BandItem I2 = band_item(p, packs, item_id(lo + j + 2 * nW));
 
   MaskSpec ms;
-  int bl = 0, st = 0;
-  if (p.kind == DENSE) {
-    ms = {0, INT_MAX, 0, INT_MAX};
-  } else if (p.kind == SWA) {
-    ms = {0, p.window, 0, INT_MAX};
-    bl = max(0, qt0 - p.window + 1) >> 6;
-  } else {  // TRIANGLE
-    ms = {0, p.window, p.sink, p.dense_from};
-    if (qt0 + rows - 1 < p.dense_from) {
-      bl = max(0, qt0 - p.window + 1) >> 6;
-      st = min((p.sink + 63) >> 6, bl);
+  if (p.kind == DENSE) ms = {0, INT_MAX, 0, INT_MAX};
+  else if (p.kind == SWA) ms = {0, p.window, 0, INT_MAX};
+  else ms = {0, p.window, p.sink, p.dense_from};
+
+  const int rs = p.Hkv * D;   // elements between consecutive keys
+  const bool v_wave = __builtin_amdgcn_readfirstlane(tid >> 6) < 4;
+  TileRegs r;
+  auto src_for = [&](int g) { return tile_src(p.K, p.V, g, rs, tid, v_wave); };
+
+  // loader cursor: the position whose tile the registers hold: tile lj of
+  // item L, which is lq items after the computing one (a copy, so that no
+  // item is ever selected by a run-time index, which would put the queue in
+  // scratch memory); valid while has_l
+  BandItem L = I0;
+  int lq = 0, lj = 0;
+  bool has_l;
+  auto advance = [&]() -> bool {
+    if (lj + 1 < L.T) {
+      ++lj;
+      return true;
     }
+    if (lq == 0 && I1.valid) {
+      L = I1;
+      lq = 1;
+      lj = 0;
+      return true;
+    }
+    if (lq == 1 && I2.valid) {
+      L = I2;
+      lq = 2;
+      lj = 0;
+      return true;
+    }
+    return false;
+  };
+  // prologue: the first tile into buffer 0, the second into registers
+  tile_load(r, src_for(I0.g), item_k0(I0, 0), p.N, rs);
+  tile_store(r, smem, tid, v_wave);
+  has_l = advance();
+  if (has_l) tile_load(r, src_for(L.g), item_k0(L, lj), p.N, rs);
+  __syncthreads();
+
+  int buf = 0;
+  while (true) {
+    // per-wave view of the item
+    const int hs = wave & ((1 << I0.sh) - 1);
+    const uint32_t pw = packs.heads[I0.pk];
+    const int h = (pw >> (8 * hs)) & 0xFF;
+    const int q0 = I0.qt0 + QW * (wave >> I0.sh);
+    const bool active = h != 0xFF && q0 < p.N;
+    const int slot = (packs.slots[I0.pk] >> (8 * hs)) & 0xFF;
+    bf16x8 qf[8];
+    WaveAcc acc;
+    acc_init(acc);
+    if (active) load_q(qf, p.Q, p.N, p.Hq, h, q0, lane);
+    // the item's query fragments are complete before its tile loop, so the
+    // loop's waits on them cannot also drain the tile loads in flight
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    for (int t = 0; t < I0.T; ++t) {
+      const bool last = t + 1 == I0.T;
+      if (last && tid == 0) s_next = item_id(lo + 3 * nW + (int)atomicAdd(&ctr[x], 1u));
+      if (has_l) {
+        // stage the loaded tile into the other buffer, load the next one
+        tile_store(r, smem + (buf ^ 1) * BUF_ELEMS, tid, v_wave);
+        has_l = advance();
+        if (has_l) tile_load(r, src_for(L.g), item_k0(L, lj), p.N, rs);
+      }
+      const int cur = item_k0(I0, t);
+      if (active && !tile_empty(ms, q0, cur))
+        tile_compute<false>(smem + buf * BUF_ELEMS, qf, nullptr, acc, lane, q0, cur, ms, p.c);
+      __syncthreads();
+      buf ^= 1;
+    }
+    if (active) store_o(acc, p.O, p.lse, slot, p.N, p.Hq, h, q0, lane, p.c);
+    // next item: the queue moves up by one and takes the fetched item
+    I0 = I1;
+    I1 = I2;
+    I2 = band_item(p, packs, __builtin_amdgcn_readfirstlane(s_next));
+    if (has_l) --lq;
+    if (!I0.valid) break;
+    __syncthreads();   // every wave has read s_next before it is written again
   }
-  const int T = st + (hi_t - bl + 1);
-  const int slot = (packs.slots[pk] >> (8 * hs)) & 0xFF;
-  run_tiles<false>(p, smem, T, g, h, slot, active, q0, ms,
-                   [&](int idx) { return (idx < st ? idx : bl + idx - st) * BK; });
 }
 
 // Orthros cross-attention for many output positions (Orthros page: in
@@ -560,12 +675,24 @@ __global__ __launch_bounds__(D) void cross_merge_kernel(AttnParams p) {
 
 }  // namespace
 
-hipError_t launch_attn_band(const AttnParams& p, const PackTable& packs, hipStream_t s) {
+// Clears the per-XCD item counters of a persistent launch.
+__global__ void clear_counters_kernel(uint32_t* ctr) {
+  if (threadIdx.x < kBandCounters) ctr[threadIdx.x] = 0u;
+}
+
+hipError_t launch_attn_band(const AttnParams& p, const PackTable& packs, uint32_t* ctr, hipStream_t s) {
   if (p.band_np[0] + p.band_np[1] + p.band_np[2] != packs.n) return hipErrorInvalidValue;
-  int nwg = 0;
-  for (int c = 0; c < 3; ++c) nwg += p.band_np[c] * ((p.N + (BK << c) - 1) / (BK << c));
-  if (nwg == 0) return hipSuccess;
-  hipLaunchKernelGGL(attn_band_kernel, dim3(nwg), dim3(NT), 0, s, p, packs);
+  int n_items = 0;
+  for (int c = 0; c < 3; ++c) n_items += p.band_np[c] * ((p.N + (BK << c) - 1) / (BK << c));
+  if (n_items == 0) return hipSuccess;
+  int dev = 0, n_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(clear_counters_kernel, dim3(1), dim3(64), 0, s, ctr);
+  // one workgroup per CU (the kernel's registers and LDS allow one)
+  const int grid = std::max(1, std::min(n_items, n_cu));
+  hipLaunchKernelGGL(attn_band_kernel, dim3(grid), dim3(NT), 0, s, p, packs, ctr, n_items);
   return hipGetLastError();
 }
 

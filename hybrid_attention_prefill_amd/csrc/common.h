@@ -67,7 +67,11 @@ struct SelList {
 };
 
 // Host launchers (each returns a hipError_t from the launch).
-hipError_t launch_attn_band(const AttnParams& p, const PackTable& packs, hipStream_t s);
+// The banded kernel is persistent: its workgroups take work items from
+// per-XCD counters (kBandCounters words of device memory, cleared by the
+// launcher on the stream before the kernel).
+constexpr int kBandCounters = 8;
+hipError_t launch_attn_band(const AttnParams& p, const PackTable& packs, uint32_t* ctr, hipStream_t s);
 hipError_t launch_attn_selected(const AttnParams& p, const SelList& sl, hipStream_t s);
 // Group-shared selection: every retrieval head of a KV group has the same key
 // set (window + the selection row of the group's first retrieval head), so
@@ -102,6 +106,8 @@ struct SelectParams {
   const int8_t* kcodes;  // 8-bit indexer keys [Hkv, N, r] (nullptr: fp32 klow)
   const float* kscale;   // [Hkv, N] their scales
   int N, n_qb, window, topk, force_block0, M;
+  float mass;            // adaptive budget: share of the top-k's softmax mass to keep (0: fixed top-k)
+  float mass_scale_log2; // softmax scale of the indexer scores, times log2(e)
   int n_ret;
   int32_t group_of_ret[kMaxHeads];
   // A selection unit is a run of retrieval slots that share one top-k: one
@@ -126,6 +132,7 @@ struct KmeansParams {
   _Float16* c_hi;      // scratch [Hkv, M, r]: centroids split in two fp16 parts
   _Float16* c_lo;
   float* c_norm;       // scratch [Hkv, M]
+  uint32_t* amax;      // scratch [Hkv]: largest |klow| component per KV head (fp32 bits)
   int N, M, stride, n_chunks;
 };
 size_t kmeans_scratch_bytes(int N, int M, int Hkv);

@@ -103,6 +103,11 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// The float an order key was made from.
+__device__ __forceinline__ float key_value(uint32_t u) {
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+
 constexpr int kHistCopies = 8;            // histogram replicas (cuts same-bin atomic conflicts)
 constexpr int kHistStride = 257;          // words between replicas (different banks)
 constexpr int kHistWords = kHistCopies * kHistStride;
@@ -115,14 +120,10 @@ constexpr int kHistWords = kHistCopies * kHistStride;
 // the digits found so far (8 lane-strided replicas, so lanes with equal
 // digits mostly hit different words), then one wave finds the digit where
 // the count from the top reaches k.  hist needs kHistWords ints.
-__device__ inline void topk_select(const uint32_t* keys, int n, int k, int topk, int id_base, int32_t* out,
-                                   int* hist, int* tmp4, int* bcast, const uint16_t* idmap = nullptr) {
+// The radix passes of topk_select alone: the k-th largest of keys[0..n)
+// (1 <= k <= n); *need_out = how many keys equal to it are among the k.
+__device__ inline uint32_t radix_kth(const uint32_t* keys, int n, int k, int* hist, int* bcast, int* need_out) {
   const int tid = threadIdx.x, lane = tid & 63;
-  if (k > n) k = n;
-  if (k <= 0) {
-    for (int x = tid; x < topk; x += kNT) out[x] = -1;
-    return;
-  }
   uint32_t prefix = 0, pmask = 0;
   int need = k;
   int* myhist = hist + (lane & (kHistCopies - 1)) * kHistStride;
@@ -176,6 +177,21 @@ __device__ inline void topk_select(const uint32_t* keys, int n, int k, int topk,
     need = bcast[1];
     __syncthreads();
   }
+  *need_out = need;
+  return prefix;
+}
+
+__device__ inline void topk_select(const uint32_t* keys, int n, int k, int topk, int id_base, int32_t* out,
+                                   int* hist, int* tmp4, int* bcast, const uint16_t* idmap = nullptr,
+                                   uint32_t* out_keys = nullptr) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (k > n) k = n;
+  if (k <= 0) {
+    for (int x = tid; x < topk; x += kNT) out[x] = -1;
+    return;
+  }
+  int need;
+  const uint32_t prefix = radix_kth(keys, n, k, hist, bcast, &need);
   // prefix is the k-th largest key; take every key above it and the first
   // `need` keys equal to it in index order.  Wave w scans a contiguous quarter
   // of the index range in rounds of 64 consecutive keys (lane = offset);
@@ -209,12 +225,79 @@ __device__ inline void topk_select(const uint32_t* keys, int n, int k, int topk,
     const int tie_rank = tie_run + (int)__popcll(tb & ((1ull << lane) - 1ull));
     const bool take = x < wb && (u > prefix || (is_tie && tie_rank < need));
     const uint64_t kb = __ballot(take);
-    if (take) out[pos_run + (int)__popcll(kb & ((1ull << lane) - 1ull))] = idmap ? (int)idmap[x] : id_base + x;
+    if (take) {
+      const int pos = pos_run + (int)__popcll(kb & ((1ull << lane) - 1ull));
+      out[pos] = idmap ? (int)idmap[x] : id_base + x;
+      if (out_keys) out_keys[pos] = u;
+    }
     tie_run += (int)__popcll(tb);
     pos_run += (int)__popcll(kb);
   }
   __syncthreads();
   for (int x = k + tid; x < topk; x += kNT) out[x] = -1;
+}
+
+// Adaptive budget (a proposal for the RTPurboV2 article's point that heads,
+// lengths and queries need different numbers of tokens): row[0..k) holds the
+// top-k ids in ascending order and rkeys[0..k) their order keys (k <= kNT).
+// Keeps the shortest prefix, in (score desc, id asc) order, whose share of
+// sum exp(scale * s) over the k reaches `mass`, and rewrites row[0..topk)
+// ascending with -1 padding.  scale_log2 = scale * log2(e).  wrank needs kNT
+// floats, tmp 8 ints, bcast 2 ints; called by all kNT threads.
+__device__ inline void adaptive_cut(int32_t* row, const uint32_t* rkeys, int k, int topk, float scale_log2,
+                                    float mass, float* wrank, int* tmp, int* bcast) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  int rank = 0, id = -1;
+  uint32_t key = 0u;
+  if (tid < k) {
+    key = rkeys[tid];
+    id = row[tid];
+    for (int j = 0; j < k; ++j) {
+      const uint32_t kj = rkeys[j];
+      rank += (kj > key) | ((kj == key) & (j < tid));   // ids ascend with j
+    }
+    if (rank == 0) bcast[0] = (int)key;
+  }
+  __syncthreads();
+  const float s0 = key_value((uint32_t)bcast[0]);
+  if (tid < k) wrank[rank] = exp2f((key_value(key) - s0) * scale_log2);
+  __syncthreads();
+  // inclusive prefix sums in rank order: one wave, four ranks per lane
+  if (tid < 64) {
+    float v[4];
+    float run = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * lane + e;
+      run += r < k ? wrank[r] : 0.f;
+      v[e] = run;
+    }
+    float inc = run;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float t = __shfl_up(inc, o);
+      if (lane >= o) inc += t;
+    }
+    const float base = inc - run;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (4 * lane + e < k) wrank[4 * lane + e] = base + v[e];
+  }
+  __syncthreads();
+  const float thr = mass * wrank[k - 1];
+  if (tid < k) {
+    const bool hit = wrank[tid] >= thr && (tid == 0 || wrank[tid - 1] < thr);
+    if (hit) bcast[1] = tid + 1;
+  }
+  __syncthreads();
+  const int n = bcast[1];
+  const bool keep = tid < k && rank < n;
+  int kept;
+  const int pos = block_excl_scan((int)keep, tmp, &kept);   // (synchronizes)
+  __syncthreads();
+  if (keep) row[pos] = id;
+  for (int x = kept + tid; x < topk; x += kNT) row[x] = -1;
+  __syncthreads();
 }
 
 }  // namespace dev

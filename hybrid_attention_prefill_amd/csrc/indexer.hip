@@ -138,6 +138,8 @@ __global__ __launch_bounds__(NT) void select_blocks_kernel(SelectParams p) {
   __shared__ int hist[dev::kHistWords];
   __shared__ int tmp4[8];
   __shared__ int bcast[2];
+  __shared__ uint32_t sel_keys[dev::kNT];   // adaptive budget: keys of the top-k
+  __shared__ float wrank[dev::kNT];
   const int b = blockIdx.x;
   const int t0 = (int)(p.unit[blockIdx.y] & 0xFFFFu), ns = (int)(p.unit[blockIdx.y] >> 16);
   const int g = p.group_of_ret[t0];
@@ -152,7 +154,8 @@ __global__ __launch_bounds__(NT) void select_blocks_kernel(SelectParams p) {
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 31, lh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (p.topk == 0) return;
-  if (nE <= p.topk) {
+  const bool adaptive = p.mass > 0.f;
+  if (nE <= p.topk && !adaptive) {
     for (int s = 0; s < ns; ++s)
       for (int x = tid; x < p.topk; x += NT) out[s * row_stride + x] = x < nE ? c_lo + x : -1;
     return;
@@ -289,15 +292,19 @@ __global__ __launch_bounds__(NT) void select_blocks_kernel(SelectParams p) {
     }
   }
   __syncthreads();
-  if (ns == 1) {
+  if (ns == 1 && !adaptive) {
     dev::topk_select(keys, nE, p.topk, p.topk, c_lo, out, hist, tmp4, bcast);
     return;
   }
   // shared row: select into LDS (the histogram is free once the last radix
-  // pass is done), then write it to every slot of the unit
+  // pass is done), cut it to the adaptive budget, then write it to every
+  // slot of the unit
   int32_t* shared_row = reinterpret_cast<int32_t*>(hist);
-  dev::topk_select(keys, nE, p.topk, p.topk, c_lo, shared_row, hist, tmp4, bcast);
+  dev::topk_select(keys, nE, p.topk, p.topk, c_lo, shared_row, hist, tmp4, bcast, nullptr,
+                   adaptive ? sel_keys : nullptr);
   __syncthreads();
+  if (adaptive && min(p.topk, nE) > 0)
+    dev::adaptive_cut(shared_row, sel_keys, min(p.topk, nE), p.topk, p.mass_scale_log2, p.mass, wrank, tmp4, bcast);
   for (int x = tid; x < ns * p.topk; x += NT) {
     const int s = x / p.topk, e = x - s * p.topk;
     out[s * row_stride + e] = shared_row[e];

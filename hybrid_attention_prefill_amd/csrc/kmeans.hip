@@ -20,6 +20,7 @@
 
 #include <limits.h>
 
+#include <algorithm>
 #include <type_traits>
 
 namespace ha {
@@ -33,23 +34,56 @@ constexpr int kCTile = 512;       // centroids per LDS tile in the assign step
 __global__ __launch_bounds__(NT) void km_init_kernel(KmeansParams p) {
   const int g = blockIdx.y;
   const int x = blockIdx.x * NT + threadIdx.x;   // (m, r) flat
+  if (blockIdx.x == 0 && threadIdx.x == 0) p.amax[g] = 0u;
   if (x >= p.M * R) return;
   const int m = x / R, r = x % R;
   p.cent[((size_t)g * p.M + m) * R + r] = p.klow[((size_t)g * p.N + (size_t)m * p.stride) * R + r];
 }
 
-// Per iteration: centroids split into two fp16 parts and their squared
-// norms, for the MFMA distance pass.
+// Largest |component| of each KV head's low-rank keys, as fp32 bits (for a
+// non-negative float the bit pattern orders as the value): grid-stride
+// float4 reads, a wave maximum, one atomic per wave.
+constexpr int kAmaxBlocks = 512;
+__global__ __launch_bounds__(NT) void km_amax_kernel(KmeansParams p) {
+  const int g = blockIdx.y;
+  const float4* src = reinterpret_cast<const float4*>(p.klow + (size_t)g * p.N * R);
+  const size_t n4 = (size_t)p.N * R / 4;
+  uint32_t m = 0u;
+  for (size_t x = (size_t)blockIdx.x * NT + threadIdx.x; x < n4; x += (size_t)gridDim.x * NT) {
+    const float4 v = src[x];
+    m = max(m, max(max(__float_as_uint(fabsf(v.x)), __float_as_uint(fabsf(v.y))),
+                   max(__float_as_uint(fabsf(v.z)), __float_as_uint(fabsf(v.w)))));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+  if ((threadIdx.x & 63) == 0) atomicMax(&p.amax[g], m);
+}
+
+// Power of two that brings the KV head's largest key component into
+// [2^9, 2^10): keys and centroids are multiplied by it before the fp16
+// split, so the split neither overflows (fp16 max 65504) nor falls into the
+// fp16 subnormals, whatever the keys' range.  Multiplying by a power of two
+// is exact and scales every distance by the same factor, so the argmin is
+// unchanged.  The exponent is clamped to fp32's normal range.
+__device__ __forceinline__ float key_scale(uint32_t amax_bits) {
+  const int e_max = (int)((amax_bits >> 23) & 0xFFu) - 127;
+  const int e = min(127, max(-126, 9 - e_max));
+  return __uint_as_float((uint32_t)(e + 127) << 23);
+}
+
+// Per iteration: centroids (times the KV head's key scale) split into two
+// fp16 parts and their squared norms, for the MFMA distance pass.
 __global__ __launch_bounds__(NT) void km_prep_kernel(KmeansParams p) {
   const int g = blockIdx.y;
   const int m = blockIdx.x * NT + threadIdx.x;
   if (m >= p.M) return;
+  const float sc = key_scale(p.amax[g]);
   const size_t o = ((size_t)g * p.M + m) * R;
   const float* c = p.cent + o;
   float nrm = 0.f;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const float v = c[r];
+    const float v = c[r] * sc;
     nrm = fmaf(v, v, nrm);
     dev::split2_f16(v, p.c_hi[o + r], p.c_lo[o + r]);
   }
@@ -71,7 +105,8 @@ __global__ __launch_bounds__(NT) void km_prep_kernel(KmeansParams p) {
 // tiles are scanned in increasing order and replace the best only when
 // strictly smaller, so the lowest index wins on equal distances).  The two
 // lane halves are merged with the same rule at the end.  Keys and centroids
-// must stay well inside the fp16 range (|component| < 16384).
+// enter the split multiplied by the KV head's power-of-two key scale
+// (key_scale), so every component lies below 2^10 in magnitude.
 constexpr int kCChunk = 256;      // centroids per LDS chunk
 constexpr int kCStr = 24;         // 16-bit row stride of a staged part (48 B: conflict-free 16-B reads)
 constexpr int KT = 4;             // 32-key blocks per wave
@@ -84,6 +119,7 @@ __global__ __launch_bounds__(NT) void km_assign_kernel(KmeansParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, lr = lane & 31, lh = lane >> 5;
   const int j0 = (blockIdx.x * 4 + wave) * (32 * KT);
+  const float ksc = -2.f * key_scale(p.amax[g]);
   dev::f16x8 kh[KT], kl[KT];
 #pragma unroll
   for (int kt = 0; kt < KT; ++kt) {
@@ -92,7 +128,7 @@ __global__ __launch_bounds__(NT) void km_assign_kernel(KmeansParams p) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       _Float16 h, l;
-      dev::split2_f16(-2.f * kp[e], h, l);
+      dev::split2_f16(ksc * kp[e], h, l);
       kh[kt][e] = h;
       kl[kt][e] = l;
     }
@@ -377,6 +413,9 @@ __global__ __launch_bounds__(NT) void block_prep_kernel(SelectParams p) {
 // max(q, 0) . a + min(q, 0) . b, so part 0 pairs max(q, 0) with the block
 // maxima and part 1 pairs min(q, 0) with the minima.
 constexpr int kSelBlocks = 1;
+// Padding after the selection tables: the last tile's lanes past the end
+// read up to 31 rows of 64 B (split parts) and 31 first members beyond M.
+constexpr size_t kTablePad = 4096;
 constexpr int kGroups = 128;      // scoring lanes (4 waves x 32)
 constexpr int kCapW = 192;        // candidate slots per wave
 
@@ -393,6 +432,7 @@ __global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
   __shared__ uint32_t tau_s;
   __shared__ int ovf;
   __shared__ uint32_t sink_word;                  // store target of padding lanes
+  __shared__ uint32_t sel_keys[NT];               // adaptive budget: keys of the top-k
   const int t0 = (int)(p.unit[blockIdx.y] & 0xFFFFu), ns = (int)(p.unit[blockIdx.y] >> 16);
   const int tid = threadIdx.x;
   const int lane = tid & 63, lr = lane & 31, lh = lane >> 5;
@@ -447,8 +487,10 @@ __global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
   // member of its cluster (eligibility: a member <= lim).
   // Buffer loads: the lane's offset inside a tile is fixed and the tile's
   // offset is wave-uniform (scalar), so a load needs no vector address
-  // arithmetic.  Lanes of the last tile past cluster M-1 fall outside the
-  // resource's range and read zeros; their keys go to the dummy word.
+  // arithmetic.  Lanes of the last tile past cluster M-1 may read past the
+  // end of a table (the scalar offset is not part of the range check): the
+  // scratch is padded by kTablePad bytes so those reads stay inside it, and
+  // whatever they return is discarded (their keys go to the dummy word).
   const __amdgpu_buffer_rsrc_t rs_hi = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<__bf16*>(chi), 0, p.M * NPART * R * 2, dev::kBufWord3);
   const __amdgpu_buffer_rsrc_t rs_lo = __builtin_amdgcn_make_buffer_rsrc(
@@ -564,19 +606,26 @@ __global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
   const int k = min(p.topk, nE);
   const size_t row_stride = (size_t)p.n_qb * p.topk;   // between slots' sel rows
   int32_t* out = p.sel + ((size_t)t0 * p.n_qb + b0) * p.topk;
-  // a unit of several slots selects into LDS (the histogram is free once the
-  // last radix pass is done) and copies the row to every slot
-  int32_t* dst_row = ns == 1 ? out : reinterpret_cast<int32_t*>(hist);
+  // a unit of several slots, or the adaptive budget, selects into LDS (the
+  // histogram is free once the last radix pass is done), cuts the row to the
+  // budget and copies it to every slot
+  const bool adaptive = p.mass > 0.f;
+  int32_t* dst_row = (ns == 1 && !adaptive) ? out : reinterpret_cast<int32_t*>(hist);
+  uint32_t* rkeys = adaptive ? sel_keys : nullptr;
   auto copy_row = [&]() {
-    if (ns == 1) return;
+    if (dst_row == out) return;
     __syncthreads();
+    // ckeys is free once the select is done: it holds the budget's weights
+    if (adaptive && k > 0)
+      dev::adaptive_cut(dst_row, sel_keys, k, p.topk, p.mass_scale_log2, p.mass, reinterpret_cast<float*>(ckeys),
+                        tmp4, bcast);
     for (int x = tid; x < ns * p.topk; x += NT) {
       const int s = x / p.topk, e = x - s * p.topk;
       out[s * row_stride + e] = dst_row[e];
     }
   };
   if (k > kGroups) {
-    dev::topk_select(keys[0], p.M, k, p.topk, 0, dst_row, hist, tmp4, bcast);
+    dev::topk_select(keys[0], p.M, k, p.topk, 0, dst_row, hist, tmp4, bcast, nullptr, rkeys);
     copy_row();
     return;
   }
@@ -617,9 +666,9 @@ __global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
   }
   __syncthreads();
   if (ovf == 0) {
-    dev::topk_select(ckeys, 4 * kCapW, k, p.topk, 0, dst_row, hist, tmp4, bcast, cidx);
+    dev::topk_select(ckeys, 4 * kCapW, k, p.topk, 0, dst_row, hist, tmp4, bcast, cidx, rkeys);
   } else {
-    dev::topk_select(keys[0], p.M, k, p.topk, 0, dst_row, hist, tmp4, bcast);
+    dev::topk_select(keys[0], p.M, k, p.topk, 0, dst_row, hist, tmp4, bcast, nullptr, rkeys);
   }
   copy_row();
 }
@@ -629,12 +678,14 @@ __global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
 size_t kmeans_scratch_bytes(int N, int M, int Hkv) {
   const size_t n_chunks = (size_t)(N + kChunk - 1) / kChunk;
   return (size_t)Hkv * n_chunks * M * sizeof(int32_t) + (size_t)Hkv * M * sizeof(int32_t) +
-         (size_t)Hkv * M * (2 * R * sizeof(_Float16) + sizeof(float)) + 256;
+         (size_t)Hkv * M * (2 * R * sizeof(_Float16) + sizeof(float)) + (size_t)Hkv * sizeof(uint32_t) + 256;
 }
 
 hipError_t launch_kmeans(KmeansParams p, int Hkv, int iters, hipStream_t s) {
   p.n_chunks = (p.N + kChunk - 1) / kChunk;
   hipLaunchKernelGGL(km_init_kernel, dim3((p.M * R + NT - 1) / NT, Hkv), dim3(NT), 0, s, p);
+  const int amax_blocks = (int)std::min<size_t>(kAmaxBlocks, ((size_t)p.N * R / 4 + NT - 1) / NT);
+  hipLaunchKernelGGL(km_amax_kernel, dim3(amax_blocks, Hkv), dim3(NT), 0, s, p);
   hipError_t e = hipGetLastError();
   for (int it = 0; it < iters && e == hipSuccess; ++it) {
     hipLaunchKernelGGL(km_prep_kernel, dim3((p.M + NT - 1) / NT, Hkv), dim3(NT), 0, s, p);
@@ -658,7 +709,7 @@ hipError_t launch_select_clusters(const SelectParams& p, int Hkv, hipStream_t s)
 }
 
 size_t select_clusters_scratch_bytes(int M, int Hkv) {
-  return (size_t)Hkv * M * (2 * R * sizeof(__bf16) + sizeof(int32_t));
+  return (size_t)Hkv * M * (2 * R * sizeof(__bf16) + sizeof(int32_t)) + kTablePad;
 }
 
 hipError_t launch_select_block_reps(const SelectParams& p, int Hkv, int mode, hipStream_t s) {
@@ -676,7 +727,7 @@ hipError_t launch_select_block_reps(const SelectParams& p, int Hkv, int mode, hi
 
 size_t select_block_reps_scratch_bytes(int n_kb, int Hkv, int mode) {
   const size_t npart = mode == 2 ? 2 : 1;
-  return (size_t)Hkv * n_kb * (2 * R * npart * sizeof(__bf16) + sizeof(int32_t));
+  return (size_t)Hkv * n_kb * (2 * R * npart * sizeof(__bf16) + sizeof(int32_t)) + kTablePad;
 }
 
 }  // namespace ha

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define HA_VERSION 4
+#define HA_VERSION 5
 
 typedef enum {
   HA_SWA = 0,        /* causal sliding window: keys i-w < j <= i */
@@ -119,6 +119,18 @@ typedef struct {
                           * long-context attention, mixed-precision index
                           * section: an 8-bit indexer).  8 is built for block
                           * mode with block_score = 0 only. */
+  float topk_mass;       /* adaptive budget ("RTPurboV2" article, fixed-top-k
+                          * passage: heads, sequence lengths and queries need
+                          * very different numbers of context tokens; the page's
+                          * own method is missing, so this rule is a proposal):
+                          * 0 (or >= 1) keeps the fixed top-k; in (0, 1) the topk
+                          * best candidates of a query block are the budget and
+                          * only the shortest prefix of them, by (score desc, id
+                          * asc), whose share of sum exp(mass_scale * score)
+                          * over the budget reaches topk_mass is kept (rows of
+                          * sel then hold fewer ids, -1 padded) */
+  float mass_scale;      /* scale of the indexer scores in that softmax; <= 0
+                          * selects 1/sqrt(rank) */
 } ha_layer_desc;
 
 /* Optional copies of the indexer's intermediate results (caller-owned device
@@ -205,7 +217,12 @@ int ha_quantize_keys(const ha_layer_desc* desc, const float* klow, int8_t* codes
  * running with iters = t reproduces the state after t iterations.
  *   klow [Hkv, N, r]; centroids [Hkv, M, r]; assign [Hkv, N];
  *   csr_off [Hkv, M+1]; csr_mem [Hkv, N] (members of cluster m at
- *   csr_mem[off[m] .. off[m+1]), ascending key position). */
+ *   csr_mem[off[m] .. off[m+1]), ascending key position).
+ * Input range: any finite klow.  The distance pass runs on fp16 matrix
+ * products of two-part splits; each KV head's keys and centroids enter it
+ * multiplied by one power of two (largest |component| brought into
+ * [2^9, 2^10)), which is exact and leaves the argmin unchanged.  Centroid
+ * sums are fp32, so max |klow| * N must stay below the fp32 range. */
 int ha_kmeans(const ha_layer_desc* desc, const float* klow, float* centroids,
               int32_t* assign, int32_t* csr_off, int32_t* csr_mem,
               void* workspace, size_t ws_bytes, void* stream);
@@ -231,7 +248,9 @@ int ha_select_clusters(const ha_layer_desc* desc, const int32_t* head_kind,
  * TriangleMix introduction in the 36kr interview (sink keys + local band,
  * and the last query rows attend to every earlier key).  Key sets as in
  * ha_head_kind; exact softmax, bf16 products, fp32 statistics and output.
- *   workspace  unused (may be NULL). */
+ *   workspace  >= 256 bytes, 256-byte aligned (ha_workspace_bytes() covers it):
+ *              the work counters of the persistent kernel, cleared on the
+ *              stream by the call itself. */
 int ha_attn_band(const ha_layer_desc* desc, const int32_t* head_kind,
                  const void* Q, const void* K, const void* V, float* O,
                  void* workspace, size_t ws_bytes, void* stream);
@@ -245,10 +264,10 @@ int ha_attn_band(const ha_layer_desc* desc, const int32_t* head_kind,
  *   csr_off, csr_mem: NULL in block mode; in cluster mode a valid CSR (each
  *              cluster's members ascending, positions in [0, N)).
  *   workspace  >= ha_workspace_bytes(desc, head_kind) bytes, 256-byte aligned:
- *              the window part's log2-sum-exp per retrieval row and, in
- *              cluster mode, K and V copied into CSR order (2 * Hkv * N * D
- *              bf16), so that a selected cluster's visible members are read
- *              as one contiguous range of rows.
+ *              the window part's log2-sum-exp per retrieval row, in cluster
+ *              mode K and V copied into CSR order (2 * Hkv * N * D bf16), so
+ *              that a selected cluster's visible members are read as one
+ *              contiguous range of rows, and the window pass's work counters.
  * With group_select = 1 every retrieval head of a KV group reads the sel row
  * of the group's first retrieval head (the rows ha_select_* writes are equal). */
 int ha_attn_gather(const ha_layer_desc* desc, const int32_t* head_kind,

@@ -85,6 +85,7 @@ class Workload:
             kmeans_iters=self.kmeans_iters, kmeans_stride=self.kmeans_stride,
             sink=self.sink, last_q=self.last_q, n_out=self.n_out,
             group_select=self.group_select, block_score=self.block_score, index_bits=self.index_bits,
+            topk_mass=self.topk_mass, mass_scale=self.mass_scale,
         )
 
 

@@ -23,7 +23,7 @@ def test_header_and_binding_agree_and_library_exports_all():
     L = ha.lib()
     for name in decl:
         assert hasattr(L, name), name
-    assert L.ha_version() == 4
+    assert L.ha_version() == 5
 
 
 def test_status_strings():

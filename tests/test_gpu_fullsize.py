@@ -52,15 +52,31 @@ def _run(name, heads=None, blocks=None, out_rows=None, **changes):
                 continue
             override[h] = {}
             for b, (E, s) in ref.scored[h].items():
-                n_diff += _gpu.check_selection(sel[t, b], E, s, w.topk, f"head {h} block {b}")
+                n_diff += _gpu.check_sel(w, sel[t, b], E, s, f"head {h} block {b}")
                 override[h][b] = np.array([x for x in sel[t, b] if x >= 0], dtype=np.int64)
         print(f"selection differences inside the tie band: {n_diff}")
+        nq = _gpu.check_lowrank_rows(aux, ref, w, heads=heads)
+        print(f"low-rank queries ({nq} rows x {len(w.ret_heads)} heads max) and keys ({w.n_tokens} rows) "
+              "within 1e-5 of the row norm")
         ref = layer_prefill(w, q_rows, K, V, P, xs, xo, blocks=blocks, heads=heads, sel_override=override,
                             out_rows=out_rows, klow32_override=k32)
     Og = O.cpu().numpy()[ref.rows]
     hs = list(range(w.n_q_heads)) if heads is None else list(heads)
     mx, mean = _gpu.assert_close_out(Og[:, hs], ref.O[:, hs], name)
     print(f"{name}: {len(blocks)} blocks x {len(hs)} heads, max abs {mx:.3e}, mean abs {mean:.3e}")
+    # discrimination: the tolerances reject an all-zero output
+    assert _gpu.fails_tolerance(np.zeros_like(ref.O[:, hs]), ref.O[:, hs]), f"{name}: O = 0 would pass"
+    if w.ret_heads and w.window and w.topk:
+        # ... and, for retrieval heads, the window-only (SWA) output on the rows
+        # whose selected keys lie outside the window
+        far = [b for b in blocks if b * w.q_block - 1 - w.window >= w.k_block]
+        rh = [h for h in w.ret_heads if heads is None or h in heads]
+        if far and rh:
+            ws = w.with_(head_kind=tuple(0 if k == 1 else k for k in w.head_kind), n_clusters=0, n_out=0)
+            swa = layer_prefill(ws, q_rows, K, V, None, blocks=far, heads=rh)
+            pos = np.searchsorted(ref.rows, swa.rows)
+            assert _gpu.fails_tolerance(Og[pos][:, rh], swa.O[:, rh]), f"{name}: SWA-only output would pass"
+            print(f"{name}: window-only output rejected on {len(far)} blocks x {len(rh)} retrieval heads")
     if w.n_out:
         Og_out = O_out.cpu().numpy()[ref.out_rows]
         mx, mean = _gpu.assert_close_out(Og_out[:, hs], ref.O_out[:, hs], name + " cross")
@@ -104,6 +120,43 @@ def test_block_representative_selection_agreement_32k():
         label = "8-bit keys" if m == 10 else f"block_score {m}"
         print(f"{label}: keeps {kept / max(tot, 1):.3f} of the max-pair selection ({tot} selected blocks)")
         assert tot > 0
+
+
+def test_qwen3_30b_layer_32k_adaptive_budget():
+    _run("qwen3_30b_a3b_32k_adaptive")
+
+
+def test_allsparse_layer_1m_adaptive_budget_sampled():
+    """The 1M layer with the adaptive budget: the GPU's own k-means, then the
+    selections of 16 sampled query blocks (every head) against the oracle's
+    budget rule, and their outputs."""
+    w = synth.WORKLOADS["allsparse_1m_adaptive"]
+    print(f"\n[case] full-size {w.name}", flush=True)
+    li = synth.make_layer_inputs(w)
+    O, _, aux = _gpu.run_gpu(w, li)
+    C = aux["centroids"].cpu().numpy()
+    asg = aux["assign"].cpu().numpy()
+    sel = aux["sel"].cpu().numpy()
+    n = w.n_qb
+    rng = np.random.default_rng(16)
+    blocks = sorted({int(rng.integers(s * n // 16, (s + 1) * n // 16)) for s in range(16)})
+    K, V = si.bf16_to_f64(li.K), si.bf16_to_f64(li.V)
+    P = li.P.astype(np.float64)
+    q_rows = lambda a, b: si.bf16_to_f64(li.Q[a:b])
+    km = {g: (C[g], asg[g]) for g in range(w.n_kv_heads)}
+    ref = layer_prefill(w, q_rows, K, V, P, blocks=blocks, kmeans_override=km)
+    override, kept, full = {}, 0, 0
+    for t, h in enumerate(w.ret_heads):
+        override[h] = {}
+        for b, (E, s) in ref.scored[h].items():
+            _gpu.check_sel(w, sel[t, b], E, s, f"head {h} block {b}")
+            override[h][b] = np.array([x for x in sel[t, b] if x >= 0], dtype=np.int64)
+            kept += override[h][b].size
+            full += min(w.topk, E.size)
+    print(f"adaptive budget keeps {kept} of {full} clusters ({kept / max(full, 1):.3f})", flush=True)
+    ref = layer_prefill(w, q_rows, K, V, P, blocks=blocks, kmeans_override=km, sel_override=override)
+    mx, mean = _gpu.assert_close_out(O.cpu().numpy()[ref.rows], ref.O, w.name)
+    print(f"{w.name}: {len(blocks)} blocks x 16 heads, max abs {mx:.3e}, mean abs {mean:.3e}")
 
 
 def test_trianglemix_layer_128k():
@@ -189,12 +242,28 @@ def test_allsparse_layer_1m():
     for t, h in enumerate(w.ret_heads):
         override[h] = {}
         for b, (E, s) in ref.scored[h].items():
-            n_diff += _gpu.check_selection(sel[t, b], E, s, w.topk, f"head {h} block {b}")
+            n_diff += _gpu.check_sel(w, sel[t, b], E, s, f"head {h} block {b}")
             override[h][b] = np.array([x for x in sel[t, b] if x >= 0], dtype=np.int64)
     print(f"selection near-tie differences: {n_diff}", flush=True)
+    # staged parity, stage 1: low-rank queries of the sampled blocks, keys at
+    # 65536 sampled positions per KV head
+    krows = np.sort(np.random.default_rng(78).choice(w.n_tokens, 65536, replace=False))
+    _gpu.check_lowrank_rows(aux, ref, w, klow_rows=krows)
     ref = layer_prefill(w, q_rows, K, V, P, blocks=blocks, kmeans_override=km, sel_override=override)
-    mx, mean = _gpu.assert_close_out(O.cpu().numpy()[ref.rows], ref.O, w.name)
+    Og = O.cpu().numpy()[ref.rows]
+    mx, mean = _gpu.assert_close_out(Og, ref.O, w.name)
     print(f"allsparse_1m: {len(blocks)} blocks x 16 heads, max abs {mx:.3e}, mean abs {mean:.3e}")
+    # discrimination: O = 0 fails, and so does the window-only output on the
+    # needle rows (each needle query's own head)
+    assert _gpu.fails_tolerance(np.zeros_like(ref.O), ref.O)
+    nb = sorted({int(r) // 64 for r in nd.q_row[:4]})
+    swa = layer_prefill(w.with_(head_kind=(0,) * 16, n_clusters=0), q_rows, K, V, None, blocks=nb)
+    for n in range(4):
+        i, h = int(nd.q_row[n]), int(nd.q_head[n])
+        gi = int(np.searchsorted(ref.rows, i))
+        si_ = int(np.searchsorted(swa.rows, i))
+        assert _gpu.fails_tolerance(Og[gi, h][None], swa.O[si_, h][None]), f"needle {n}: SWA-only would pass"
+    print("allsparse_1m: O = 0 and the window-only output on 4 needle rows are rejected")
 
 
 def test_allsparse_gqa_layer_1m():
@@ -228,7 +297,7 @@ def test_allsparse_gqa_layer_1m():
     for t, h in enumerate(w.ret_heads):
         override[h] = {}
         for b, (E, s) in ref.scored[h].items():
-            n_diff += _gpu.check_selection(sel[t, b], E, s, w.topk, f"head {h} block {b}")
+            n_diff += _gpu.check_sel(w, sel[t, b], E, s, f"head {h} block {b}")
             override[h][b] = np.array([x for x in sel[t, b] if x >= 0], dtype=np.int64)
     print(f"selection near-tie differences: {n_diff}", flush=True)
     ref = layer_prefill(w, q_rows, K, V, P, blocks=blocks, kmeans_override=km, sel_override=override)

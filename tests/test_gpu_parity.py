@@ -27,8 +27,7 @@ def _compare(w, blocks=None, check_sel=True):
         sel = aux["sel"].cpu().numpy()
         _gpu.check_group_rows(sel, w)
         klow = aux["klow"].cpu().numpy()
-        for g, kl in ref.klow.items():
-            _gpu.assert_lowrank(klow[g], kl, f"klow[{g}]")
+        _gpu.check_lowrank_rows(aux, ref, w)
         k32 = None
         if w.index_bits == 8:
             # 8-bit keys: the oracle quantizes the GPU's validated fp32 keys, so
@@ -39,7 +38,7 @@ def _compare(w, blocks=None, check_sel=True):
         for t, h in enumerate(w.ret_heads):
             override[h] = {}
             for b, (E, s) in ref.scored[h].items():
-                _gpu.check_selection(sel[t, b], E, s, w.topk, f"head {h} block {b}")
+                _gpu.check_sel(w, sel[t, b], E, s, f"head {h} block {b}")
                 override[h][b] = np.array([x for x in sel[t, b] if x >= 0], dtype=np.int64)
         # grade attention given the validated GPU selection
         ref = layer_prefill(w, q, K, V, P, xs, xo, blocks=blocks, sel_override=override, klow32_override=k32)
@@ -265,3 +264,18 @@ def test_cluster_selection_exact_ties_keep_lowest_ids(M):
             E = [m for m in range(M) if m <= lim]
             expect = E[:k] + [-1] * (k - min(k, len(E)))
             assert list(sel[t, b]) == expect, (t, b, list(sel[t, b]), expect)
+
+
+@pytest.mark.parametrize("N,window,topk,mass,scale,f0,gs,score", [
+    (1000, 100, 8, 0.5, 0.0, 0, 0, 0), (1337, 64, 12, 0.9, 0.0, 1, 0, 0), (1000, 100, 8, 0.7, 2.0, 0, 1, 0),
+    (700, 1, 30, 0.3, 0.5, 0, 0, 0), (640, 50, 100, 0.8, 0.0, 0, 0, 0), (1000, 100, 8, 0.6, 0.0, 0, 0, 1),
+    (300, 5000, 4, 0.5, 0.0, 0, 0, 0)])
+def test_adaptive_budget_block_mode(N, window, topk, mass, scale, f0, gs, score):
+    # adaptive budget: each query block keeps the shortest prefix of its top-k
+    # whose softmax share reaches the mass (max-pair scores, group-shared
+    # selection, mean representatives; budgets larger than the candidate set)
+    kinds = [HEAD_RETRIEVAL, HEAD_SWA, HEAD_RETRIEVAL, HEAD_RETRIEVAL, HEAD_SWA, HEAD_RETRIEVAL, HEAD_RETRIEVAL,
+             HEAD_RETRIEVAL]
+    _compare(_layer(kinds, N, window=window, topk=topk, force_block0=f0, group_select=gs, block_score=score,
+                    topk_mass=mass, mass_scale=scale))
+
