@@ -40,27 +40,41 @@ PEAK_HBM_GBS = 8000.0
 DEFAULT_SUITE = ["qwen3_30b_a3b_32k", "trianglemix_llama8b_128k", "dense_llama8b_128k",
                  "orthros_8b_128k", "allsparse_1m"]
 COPY_CAL_BYTES = 1 << 30
+PEAK_FP32_TFLOPS = 157.3
+PEAK_SPLIT3_TFLOPS = PEAK_BF16_TFLOPS / 3   # fp32-accurate products as three 16-bit MFMA passes
 # HBM bytes per launch measured with rocprofv3 --pmc (FETCH_SIZE, WRITE_SIZE,
 # KiB per dispatch, scaled by the same counters on a plain 1 GiB copy); valid
-# only while the kernel source is the one the counters were taken on.
+# only while the kernel's sources and compile flags are the ones the counters
+# were taken on (digest of the listed sources plus the hipcc flags).
 TRAFFIC = {
     ("dense_llama8b_128k", "attn_band"): {
-        "bytes": 20688568621, "source": "hybrid_attention_prefill_amd/csrc/attn.hip",
-        "sha256_prefix": "385622c8e0ec6f6e"},
+        "bytes": 20688568621, "sources": ("attn.hip", "common.h", "device_util.h"),
+        "digest": "unmeasured"},
 }
 
 
-def traffic_for(workload, stage):
+def kernel_digest(sources):
+    """sha256 over the kernel's source files and the flags build.py compiles
+    them with (the first file decides the per-file flags)."""
     import hashlib
+    from hybrid_attention_prefill_amd import build as hb
+    h = hashlib.sha256()
+    for f in sources:
+        with open(os.path.join(hb.CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    h.update(" ".join(hb.COMMON + hb.FILE_FLAGS.get(sources[0], [])).replace(hb.ROOT, "<root>").encode())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(workload, stage):
     t = TRAFFIC.get((workload, stage))
     if t is None:
         return None
     try:
-        with open(os.path.join(ROOT, t["source"]), "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
+        ok = kernel_digest(t["sources"]) == t["digest"]
     except OSError:
         return None
-    return t["bytes"] if sha.startswith(t["sha256_prefix"]) else None
+    return t["bytes"] if ok else None
 
 
 # ---------------------------------------------------------------------------
@@ -101,13 +115,9 @@ def pairs_retrieval_blocks(N, w, sel_rows, f0, Bk=64, Bq=64):
     return total
 
 
-def pairs_retrieval_clusters(N, w, sel_rows, csr_off, csr_mem, Bq=64):
-    """Pairs of one retrieval head in cluster mode: window + members j <= i-w
-    of the selected clusters, from the CSR (members ascending per cluster).
-    For rows [qs, qe] of a block and a cluster with C(x) = #members <= x and
-    S(x) = sum of members <= x:
-      pairs = n*C(qs-w) + (qe-w+1)*(C(qe-w) - C(qs-w)) - (S(qe-w) - S(qs-w))."""
-    total = pairs_swa(N, w)
+def _cluster_counts(N, w, sel_rows, csr_off, csr_mem, Bq=64):
+    """Per (query block, selected cluster): C(x) = #members <= x and S(x) =
+    sum of members <= x at x = qs - w and x = qe - w (members ascending)."""
     n_qb, k = sel_rows.shape
     M = csr_off.size - 1
     clus = np.repeat(np.arange(M, dtype=np.int64), np.diff(csr_off))
@@ -119,7 +129,6 @@ def pairs_retrieval_clusters(N, w, sel_rows, csr_off, csr_mem, Bq=64):
     b, m = b[ok], m[ok]
     qs = b * Bq
     qe = np.minimum(N, qs + Bq) - 1
-    n = qe - qs + 1
 
     def CS(x):
         xx = np.maximum(x, -1)
@@ -130,14 +139,61 @@ def pairs_retrieval_clusters(N, w, sel_rows, csr_off, csr_mem, Bq=64):
 
     c1, s1 = CS(qs - w)
     c2, s2 = CS(qe - w)
-    total += int((n * c1 + (qe - w + 1) * (c2 - c1) - (s2 - s1)).sum())
-    return total
+    return qs, qe, c1, s1, c2, s2
+
+
+def pairs_retrieval_clusters(N, w, sel_rows, csr_off, csr_mem, Bq=64):
+    """Pairs of one retrieval head in cluster mode: window + members j <= i-w
+    of the selected clusters, from the CSR (members ascending per cluster).
+    For rows [qs, qe] of a block and a cluster with C(x) = #members <= x and
+    S(x) = sum of members <= x:
+      pairs = n*C(qs-w) + (qe-w+1)*(C(qe-w) - C(qs-w)) - (S(qe-w) - S(qs-w))."""
+    qs, qe, c1, s1, c2, s2 = _cluster_counts(N, w, sel_rows, csr_off, csr_mem, Bq)
+    n = qe - qs + 1
+    return pairs_swa(N, w) + int((n * c1 + (qe - w + 1) * (c2 - c1) - (s2 - s1)).sum())
+
+
+def gathered_keys_clusters(N, w, sel_rows, csr_off, csr_mem, Bq=64):
+    """Keys a retrieval head's query blocks gather outside the window: for each
+    block and selected cluster, its members j <= qe - w."""
+    return int(_cluster_counts(N, w, sel_rows, csr_off, csr_mem, Bq)[4].sum())
+
+
+def gathered_keys_blocks(N, w, sel_rows, f0, Bk=64, Bq=64):
+    """Keys a retrieval head's query blocks gather outside the window: the
+    selected (and forced) blocks' keys j <= qe - w."""
+    n_qb = sel_rows.shape[0]
+    qe = np.minimum(N, (np.arange(n_qb) + 1) * Bq) - 1
+    c = sel_rows.astype(np.int64)
+    cnt = np.where(c >= 0, np.clip(qe[:, None] - w - c * Bk + 1, 0, Bk), 0).sum()
+    if f0:
+        cnt += np.clip(qe - w + 1, 0, Bk).sum()
+    return int(cnt)
+
+
+def eligible_block_pairs(w):
+    """Eligible (query block, key block) pairs of one retrieval head."""
+    qe = np.minimum(w.n_tokens, (np.arange(w.n_qb) + 1) * w.q_block) - 1
+    hi = np.where(qe - w.window >= 0, (qe - w.window) // w.k_block, w.force_block0 - 1)
+    return int(np.clip(hi - w.force_block0 + 1, 0, None).sum())
+
+
+def band_pairs(w, kinds=None):
+    kinds = w.head_kind if kinds is None else kinds
+    N = w.n_tokens
+    return sum(pairs_swa(N, w.window) if k == 0 else pairs_dense(N) if k == 3 else
+               pairs_triangle(N, w.sink, w.window, w.last_q) if k == 2 else 0 for k in kinds)
 
 
 def layer_work(w, sel=None, csr=None):
-    """(actual attention pairs, dense-equivalent pairs) summed over heads."""
+    """(actual attention pairs, dense-equivalent pairs, retrieval pairs,
+    gathered keys) summed over heads; gathered keys count, per retrieval head
+    and query block, the keys read outside the window (once per KV group and
+    query block with group-shared selection)."""
     N = w.n_tokens
-    act = 0
+    act = ret_pairs = gathered = 0
+    G = w.n_q_heads // w.n_kv_heads
+    seen_groups = set()
     for h, k in enumerate(w.head_kind):
         if k == 0:
             act += pairs_swa(N, w.window)
@@ -147,14 +203,88 @@ def layer_work(w, sel=None, csr=None):
             act += pairs_triangle(N, w.sink, w.window, w.last_q)
         else:
             t = w.ret_heads.index(h)
+            g = h // G
             if w.n_clusters:
-                g = h // (w.n_q_heads // w.n_kv_heads)
-                act += pairs_retrieval_clusters(N, w.window, sel[t], csr[0][g], csr[1][g])
+                pr = pairs_retrieval_clusters(N, w.window, sel[t], csr[0][g], csr[1][g])
+                gk = gathered_keys_clusters(N, w.window, sel[t], csr[0][g], csr[1][g])
             else:
-                act += pairs_retrieval_blocks(N, w.window, sel[t], w.force_block0)
+                pr = pairs_retrieval_blocks(N, w.window, sel[t], w.force_block0)
+                gk = gathered_keys_blocks(N, w.window, sel[t], w.force_block0)
+            act += pr
+            ret_pairs += pr
+            if not w.group_select or g not in seen_groups:
+                gathered += gk
+                seen_groups.add(g)
     # cross-attention rows p = N - n_out .. N - 1 see keys 0..p
     act += w.n_q_heads * (w.n_out * (N - w.n_out) + w.n_out * (w.n_out + 1) // 2)
-    return act, w.n_q_heads * pairs_dense(N)
+    return act, w.n_q_heads * pairs_dense(N), ret_pairs, gathered
+
+
+def _roof(bound, work, sec, peak, unit, what):
+    if sec <= 0:
+        return None
+    rate = work / sec / (1e12 if unit == "TFLOP/s" else 1e9)
+    return {"bound": bound, "work": work, "work_unit": "FLOP" if unit == "TFLOP/s" else "B",
+            "achieved": round(rate, 2), "peak": peak, "unit": unit, "frac": round(rate / peak, 4), "what": what}
+
+
+def stage_rooflines(w, stage_ms, work, window_ms=None):
+    """Roofline of every stage (one C-ABI call each) from its algorithmic work:
+    FLOPs for the matrix-core and fp32 contractions, bytes for the HBM-bound
+    stages.  The gather stage is mixed (its window on the matrix cores, the
+    selected keys from HBM); with window_ms (the same window pass timed on its
+    own) its selected part is reported as derived: gather - window."""
+    N, Hkv = w.n_tokens, w.n_kv_heads
+    Hret = len(w.ret_heads)
+    act, _, ret_pairs, gathered = work
+    out = {}
+    for name, ms in stage_ms.items():
+        sec = ms * 1e-3
+        if name == "index_project":
+            out[name] = _roof("hbm", (Hret + Hkv) * N * (256 + 64), sec, PEAK_HBM_GBS, "GB/s",
+                              "256 B read + 64 B written per projected (row, head): retrieval queries, all keys")
+        elif name == "select_blocks":
+            out[name] = _roof("mfma", 32 * 4096 * Hret * eligible_block_pairs(w), sec, PEAK_SPLIT3_TFLOPS,
+                              "TFLOP/s", "2 r FLOP per (query, key) pair of every eligible 64 x 64 tile; an "
+                              "fp32-accurate contraction run as three bf16 MFMA passes over hi/lo splits, so the "
+                              "peak is 2.5 PFLOP/s / 3")
+        elif name == "kmeans":
+            out[name] = _roof("mfma", 32 * w.kmeans_iters * Hkv * N * w.n_clusters, sec, PEAK_SPLIT3_TFLOPS,
+                              "TFLOP/s", "2 r FLOP per (key, centroid) pair per Lloyd iteration; an fp32-accurate "
+                              "contraction run as three fp16 MFMA passes (peak 2.5 PFLOP/s / 3); the update is "
+                              "HBM / integer work")
+        elif name == "select_clusters":
+            out[name] = _roof("mfma", 32 * Hret * N * w.n_clusters, sec, PEAK_BF16_TFLOPS, "TFLOP/s",
+                              "2 r FLOP per (query row, centroid) pair, one bf16 MFMA pass (peak 2.5 PFLOP/s); "
+                              "the few candidates near the k-th score are re-scored in fp32")
+        elif name == "attn_band":
+            out[name] = _roof("mfma", 512 * band_pairs(w), sec, PEAK_BF16_TFLOPS, "TFLOP/s",
+                              "4 D FLOP per (query, key) pair of the band heads' key sets")
+        elif name == "attn_cross":
+            if w.n_out < 64:
+                out[name] = _roof("hbm", N * Hkv * 2 * 256, sec, PEAK_HBM_GBS, "GB/s",
+                                  "K and V read once (256 B each per key and KV head)")
+            else:
+                pairs = w.n_q_heads * (w.n_out * (N - w.n_out) + w.n_out * (w.n_out + 1) // 2)
+                out[name] = _roof("mfma", 512 * pairs, sec, PEAK_BF16_TFLOPS, "TFLOP/s",
+                                  "4 D FLOP per (output row, key) pair")
+        elif name == "attn_gather":
+            gb = gathered * 512 + (2 * 512 * Hkv * N if w.n_clusters else 0)
+            e = {"mfma": _roof("mfma", 512 * ret_pairs, sec, PEAK_BF16_TFLOPS, "TFLOP/s",
+                               "4 D FLOP per pair of the retrieval heads' key sets (window + selected)"),
+                 "hbm": _roof("hbm", gb, sec, PEAK_HBM_GBS, "GB/s",
+                              "512 B of K + V per gathered key per (head, query block)"
+                              + (" + 1 KB per key copied into cluster order" if w.n_clusters else ""))}
+            if window_ms is not None and 0 < window_ms < ms:
+                wp = sum(pairs_swa(N, w.window) for _ in w.ret_heads)
+                e["window_part"] = _roof("mfma", 512 * wp, window_ms * 1e-3, PEAK_BF16_TFLOPS, "TFLOP/s",
+                                         "the window pass timed alone (same kernel, retrieval heads as SWA)")
+                e["window_part"]["ms"] = round(window_ms, 4)
+                e["selected_part_derived"] = _roof("hbm", gb, (ms - window_ms) * 1e-3, PEAK_HBM_GBS, "GB/s",
+                                                   "gathered bytes / (gather ms - window ms)")
+                e["selected_part_derived"]["ms"] = round(ms - window_ms, 4)
+            out[name] = e
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -172,7 +302,7 @@ class Layer:
                                  n_clusters=w.n_clusters, kmeans_iters=w.kmeans_iters,
                                  kmeans_stride=w.kmeans_stride, sink=w.sink, last_q=w.last_q, n_out=w.n_out,
                                  group_select=w.group_select, block_score=w.block_score,
-                                 index_bits=w.index_bits)
+                                 index_bits=w.index_bits, topk_mass=w.topk_mass, mass_scale=w.mass_scale)
         self.kinds = list(w.head_kind)
         self.O = torch.empty((N, Hq, D), dtype=torch.float32, device=dev)
         self.O_out = torch.empty((w.n_out, Hq, D), dtype=torch.float32, device=dev) if w.n_out else None
@@ -244,25 +374,70 @@ def dev_inputs_for(w, cache, torch, log):
     return base + (P, xs, xo)
 
 
-def cpu_baseline(names, log, budget_s=20.0):
-    """The fp64 oracle, as it stands, on one query block per layer of the suite
-    (the last block of each, so every row sees its full key set); rate =
-    oracle attention FLOPs / oracle seconds."""
+def _oracle_block_pairs(w, b, res, assign=None):
+    """Exact (query, key) pairs the oracle evaluated for query block b, all
+    heads (key-set sizes of its rows), plus the cross-attention row if any."""
+    N = w.n_tokens
+    rows = np.arange(b * w.q_block, min(N, (b + 1) * w.q_block), dtype=np.int64)
+    win = np.minimum(w.window, rows + 1)
+    G = w.n_q_heads // w.n_kv_heads
+    act = 0
+    for h, k in enumerate(w.head_kind):
+        if k == 0:
+            act += int(win.sum())
+        elif k == 3:
+            act += int((rows + 1).sum())
+        elif k == 2:
+            extra = np.clip(np.minimum(w.sink, rows - w.window + 1), 0, None)
+            act += int(np.where(rows >= N - w.last_q, rows + 1, win + extra).sum())
+        else:
+            S = np.asarray(res.sel[h][b], dtype=np.int64)
+            if w.n_clusters:
+                a = assign[h // G]
+                mem = np.nonzero(np.isin(a[:max(0, int(rows[-1]) - w.window + 1)], S))[0]
+                sel_cnt = np.searchsorted(mem, rows - w.window, side="right")
+            else:
+                blocks = list(S) + ([0] if w.force_block0 else [])
+                sel_cnt = sum(np.clip(np.minimum(c * w.k_block + w.k_block - 1, rows - w.window) - c * w.k_block + 1,
+                                      0, None) for c in blocks) if blocks else 0
+            act += int(win.sum() + np.sum(sel_cnt))
+    if w.n_out:
+        act += w.n_q_heads * N     # the last output row attends to every key
+    return act
+
+
+def cpu_baseline(names, log, gpu_kmeans=None, layer_flops=None):
+    """The fp64 oracle as it stands, on a bounded sample of every layer of the
+    suite: one whole query block with all heads (the last block; for the 1M
+    layer the block of its first needle query, with the GPU's k-means
+    centroids and assignment injected, since the oracle's own Lloyd over 1M
+    keys is far outside the budget), plus the Orthros layer's last output
+    row.  Reported per layer: oracle seconds, seconds per query row, and the
+    full layer's oracle time extrapolated from the sample's FLOP rate; the
+    TriangleMix 32-layer stack (12 dense + 20 triangle) extrapolated the same
+    way.  value = oracle FLOPs / oracle seconds over all samples."""
     import synth
     from synth import inputs as si
     from oracle.prefill import layer_prefill
     try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        cores = 1
-    flops = 0.0
-    secs = 0.0
-    done = []
+        blas = 1
+    flops = secs = 0.0
+    per_layer = {}
     for name in names:
         w = synth.WORKLOADS[name]
+        km = None
         if w.n_clusters:
-            continue   # k-means over 1M keys does not fit the sampling budget
+            if not gpu_kmeans or name not in gpu_kmeans:
+                continue
+            km = gpu_kmeans[name]
+        t0 = time.time()
         K = si.bf16_to_f64(si.gen_k(w))
         V = si.bf16_to_f64(si.gen_v(w))
         P = si.gen_proj(w).astype(np.float64) if w.ret_heads else None
@@ -270,33 +445,40 @@ def cpu_baseline(names, log, budget_s=20.0):
         if w.n_out:
             s, o = si.gen_scale_offset(w)
             xs, xo = s.astype(np.float64), o.astype(np.float64)
+        t_in = time.time() - t0
         b = w.n_qb - 1
+        nd = si.needles(w)
+        if w.n_clusters and nd is not None:
+            b = int(nd.q_row[0]) // w.q_block
         t = time.time()
         res = layer_prefill(w, lambda a, c: si.bf16_to_f64(si.gen_q(w, a, c)), K, V, P, xs, xo, blocks=[b],
-                            out_rows=[w.n_out - 1] if w.n_out else None)
+                            out_rows=[w.n_out - 1] if w.n_out else None, kmeans_override=km)
         dt = time.time() - t
-        # attention pairs the oracle evaluated for that block (+ the cross row)
-        act = 0
-        rows = res.rows
-        for h, k in enumerate(w.head_kind):
-            if k == 0:
-                act += int(np.minimum(w.window, rows + 1).sum())
-            elif k == 3:
-                act += int((rows + 1).sum())
-            elif k == 2:
-                act += int((rows + 1).sum()) if rows[0] >= w.n_tokens - w.last_q else \
-                    int(np.minimum(w.window, rows + 1).sum())
-            else:
-                act += int(np.minimum(w.window, rows + 1).sum()) + 64 * 64 * len(res.sel[h][b])
-        act += w.n_q_heads * w.n_tokens if w.n_out else 0   # the last output row: all N keys
-        flops += 4.0 * w.head_dim * act
+        fl = 4.0 * w.head_dim * _oracle_block_pairs(w, b, res, None if km is None else
+                                                    {g: km[g][1] for g in km})
+        del K, V
+        flops += fl
         secs += dt
-        done.append(f"{name}: block {b} all heads" + (", last output row" if w.n_out else ""))
-        log(f"cpu oracle {name}: {dt:.1f}s")
-        if secs > budget_s:
-            break
-    return {"value": flops / secs / 1e12 if secs > 0 else None, "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle", "sample": "; ".join(done) + f"; {secs:.1f}s of fp64 numpy"}
+        rate = fl / dt
+        e = {"sample": f"query block {b} ({res.rows.size} rows) x {w.n_q_heads} heads"
+                       + (", last output row" if w.n_out else "")
+                       + (", GPU k-means injected" if km is not None else ""),
+             "oracle_s": round(dt, 3), "s_per_row": round(dt / res.rows.size, 5),
+             "oracle_gflops": round(rate / 1e9, 3), "input_gen_s": round(t_in, 2)}
+        if layer_flops and name in layer_flops:
+            e["extrapolated_layer_s"] = round(layer_flops[name] / rate, 1)
+            e["extrapolation"] = "full layer's actual FLOPs / the sample's oracle FLOP rate"
+        per_layer[name] = e
+        log(f"cpu oracle {name}: block {b}, {dt:.1f}s")
+    out = {"value": flops / secs / 1e12 if secs > 0 else None, "unit": "TFLOP/s", "cores": int(cores),
+           "blas_threads": int(blas), "kind": "oracle",
+           "sample": "one query block x all heads per layer (see layers); " + f"{secs:.1f}s of fp64 numpy",
+           "layers": per_layer}
+    tri, den = per_layer.get("trianglemix_llama8b_128k", {}), per_layer.get("dense_llama8b_128k", {})
+    if "extrapolated_layer_s" in tri and "extrapolated_layer_s" in den:
+        out["trianglemix_stack_32_extrapolated_s"] = round(
+            12 * den["extrapolated_layer_s"] + 20 * tri["extrapolated_layer_s"], 1)
+    return out
 
 
 def main():
@@ -306,6 +488,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workloads", type=str, default=",".join(DEFAULT_SUITE))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the untimed extras (window-pass timing, TriangleMix 32-layer stack)")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one plain device copy of 1 GiB (reference for HBM byte counters)")
@@ -368,47 +552,72 @@ def main():
     stage_ms /= args.steps
     log(f"timed {args.steps} steps: {ms_step:.2f} ms/step")
 
+    def timed(fns, reps):
+        """Average ms of one pass over fns (HIP events on the current stream)."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for fn in fns:
+            fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            for fn in fns:
+                fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    # untimed extras: the retrieval heads' window pass alone (the same banded
+    # kernel the gather stage launches first, run with those heads as SWA),
+    # and the TriangleMix 32-layer stack
+    window_ms = {}
+    stack = None
+    if not args.no_extras:
+        for L in layers:
+            w = L.w
+            if w.ret_heads and not w.group_select:
+                kinds = [0 if k == 1 else 1 for k in L.kinds]
+                window_ms[w.name] = timed([lambda L=L, kinds=kinds: ha.ha_attn_band(
+                    L.desc, kinds, L.Q, L.K, L.V, L.O, L.ws)], max(2, args.steps // 2))
+        by = {L.w.name: L for L in layers}
+        if "trianglemix_llama8b_128k" in by and "dense_llama8b_128k" in by:
+            Lt, Ld = by["trianglemix_llama8b_128k"], by["dense_llama8b_128k"]
+            dense_fn = [fn for name, fn in Ld.stages()]
+            tri_fn = [fn for name, fn in Lt.stages()]
+            stack = timed(dense_fn * 12 + tri_fn * 20, 1)
+            log(f"TriangleMix 32-layer stack: {stack:.1f} ms")
+
     per_layer = {}
+    layer_fl = {}
     tot_act = tot_dense = 0.0
     for L in layers:
         w = L.w
         sel = L.sel.cpu().numpy() if w.ret_heads else None
         csr = (L.csr_off.cpu().numpy(), L.csr_mem.cpu().numpy()) if w.n_clusters else None
-        act, dense = layer_work(w, sel, csr)
+        work = layer_work(w, sel, csr)
+        act, dense = work[0], work[1]
         ms = float(sum(stage_ms[t] for t, (LL, _, _) in enumerate(plan) if LL is L))
         stg = {name: round(float(stage_ms[t]), 4) for t, (LL, name, _) in enumerate(plan) if LL is L}
-        fl_act = None if act is None else 4.0 * w.head_dim * act
+        fl_act = 4.0 * w.head_dim * act
         fl_dense = 4.0 * w.head_dim * dense
+        layer_fl[w.name] = fl_act
         per_layer[w.name] = {
             "ms": round(ms, 4), "stages_ms": stg,
-            "actual_tflops": None if fl_act is None else round(fl_act / ms / 1e9, 2),
+            "actual_tflops": round(fl_act / ms / 1e9, 2),
             "dense_equiv_tflops": round(fl_dense / ms / 1e9, 2),
-            "mfma_frac_actual": None if fl_act is None else round(fl_act / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+            "mfma_frac_actual": round(fl_act / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
             "attn_pairs": act,
+            "stage_roofline": stage_rooflines(w, stg, work, window_ms.get(w.name)),
         }
-        if fl_act is not None:
-            tot_act += fl_act
+        tot_act += fl_act
         tot_dense += fl_dense
 
     # dominant kernel: the longest single-kernel stage
-    best = max(range(len(plan)), key=lambda t: stage_ms[t])
+    best = max(range(len(plan)), key=lambda t: stage_ms[t] if plan[t][1] in ("attn_band", "attn_cross") else 0)
     L, sname, _ = plan[best]
     w = L.w
-    roof = None
-    if sname in ("attn_band", "attn_gather"):
-        if sname == "attn_band":
-            act = sum(pairs_swa(w.n_tokens, w.window) if k == 0 else pairs_dense(w.n_tokens) if k == 3 else
-                      pairs_triangle(w.n_tokens, w.sink, w.window, w.last_q) if k == 2 else 0
-                      for k in w.head_kind)
-        else:
-            act = per_layer[w.name]["attn_pairs"] - sum(
-                pairs_swa(w.n_tokens, w.window) for k in w.head_kind if k == 0)
-        achieved = 4.0 * w.head_dim * act / (stage_ms[best] * 1e-3) / 1e12
-        tr = traffic_for(w.name, sname)
-        roof = {"kernel": f"{sname} ({w.name})", "bound": "mfma", "achieved": round(achieved, 2),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": tr, "avg_ms": round(float(stage_ms[best]), 4),
-                "work": "4*D FLOPs per (query, key) pair of the realised key sets"}
+    r = per_layer[w.name]["stage_roofline"][sname]
+    roof = dict(r, kernel=f"{sname} ({w.name})", traffic=traffic_for(w.name, sname),
+                avg_ms=round(float(stage_ms[best]), 4))
 
     value = tot_act / (ms_step * 1e-3) / 1e12 if tot_act else None
     out = {
@@ -422,8 +631,21 @@ def main():
         "dense_equiv_tflops": round(tot_dense / (ms_step * 1e-3) / 1e12, 2),
         "roofline": roof,
     }
+    if stack is not None:
+        fl = 12 * layer_fl["dense_llama8b_128k"] + 20 * layer_fl["trianglemix_llama8b_128k"]
+        out["trianglemix_stack_32"] = {
+            "layers": "12 dense + 20 TriangleMix layers, one C-ABI call each on the same tensors (untimed extra)",
+            "ms": round(stack, 2),
+            "ms_sum_of_layers": round(12 * per_layer["dense_llama8b_128k"]["ms"]
+                                      + 20 * per_layer["trianglemix_llama8b_128k"]["ms"], 2),
+            "actual_tflops": round(fl / (stack * 1e-3) / 1e12, 2)}
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(names, log)
+        gk = {}
+        for L in layers:
+            if L.w.n_clusters:
+                gk[L.w.name] = {g: (L.cent[g].cpu().numpy(), L.assign[g].cpu().numpy())
+                                for g in range(L.w.n_kv_heads)}
+        out["cpu_baseline"] = cpu_baseline(names, log, gk, layer_fl)
     print(json.dumps(out), flush=True)
 
 
