@@ -20,9 +20,10 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libha.so")
 
 HA_SWA, HA_RETRIEVAL, HA_TRIANGLE, HA_DENSE = 0, 1, 2, 3
-HA_OK, HA_ERR_ARG, HA_ERR_UNSUPPORTED, HA_ERR_WORKSPACE, HA_ERR_DEVICE = range(5)
+HA_OK, HA_ERR_ARG, HA_ERR_UNSUPPORTED, HA_ERR_WORKSPACE, HA_ERR_DEVICE, HA_ERR_SCRATCH = range(6)
+HA_STATIC_SCRATCH_BYTES = 64 << 20
 
-EXPORTS = ("ha_status_string", "ha_version", "ha_workspace_bytes", "ha_prefill",
+EXPORTS = ("ha_status_string", "ha_version", "ha_workspace_bytes", "ha_prefill", "ha_prefill_static",
            "ha_index_project", "ha_select_blocks", "ha_quantize_keys", "ha_kmeans", "ha_select_clusters",
            "ha_attn_band", "ha_attn_gather", "ha_attn_cross")
 
@@ -75,6 +76,8 @@ def lib():
         L.ha_prefill.restype = ctypes.c_int
         L.ha_prefill.argtypes = [dp, i32p, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(Aux), vp,
                                  ctypes.c_size_t, vp]
+        L.ha_prefill_static.restype = ctypes.c_int
+        L.ha_prefill_static.argtypes = [dp, i32p, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(Aux), vp]
         L.ha_index_project.restype = ctypes.c_int
         L.ha_index_project.argtypes = [dp, i32p, vp, vp, vp, vp, vp, vp]
         L.ha_select_blocks.restype = ctypes.c_int
@@ -160,6 +163,14 @@ def ha_prefill(desc, head_kind, Q, K, V, P_idx, xa_scale, xa_offset, O, O_out, a
                             _ptr(xa_scale), _ptr(xa_offset), _ptr(O), _ptr(O_out),
                             ctypes.byref(a) if a is not None else None, _ptr(workspace), int(ws_bytes),
                             _stream(stream)))
+
+
+def ha_prefill_static(desc, head_kind, Q, K, V, P_idx, xa_scale, xa_offset, O, O_out, aux=None, stream=None):
+    """ha_prefill without a workspace: the library's static device scratch."""
+    a = _aux(aux)
+    _check(lib().ha_prefill_static(ctypes.byref(desc), _kinds(head_kind), _ptr(Q), _ptr(K), _ptr(V), _ptr(P_idx),
+                                   _ptr(xa_scale), _ptr(xa_offset), _ptr(O), _ptr(O_out),
+                                   ctypes.byref(a) if a is not None else None, _stream(stream)))
 
 
 def ha_index_project(desc, head_kind, Q, K, P_idx, qlow, klow, stream=None):

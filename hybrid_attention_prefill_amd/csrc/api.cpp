@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <vector>
 
 #include "common.h"
@@ -493,6 +494,28 @@ int run_cross(const ha_layer_desc* d, const void* Q, const void* K, const void* 
 
 inline char* ws_at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
+// Scratch of ha_prefill_static.  In host code `scratch` is only a handle for
+// the symbol lookup; its device address (one copy per GPU) comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+__device__ __attribute__((aligned(256))) unsigned char scratch[HA_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int static_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return HA_ERR_DEVICE;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return HA_ERR_DEVICE;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return HA_OK;
+}
+
 bool ws_ok(void* ws, size_t ws_bytes, size_t need) {
   if (need == 0) return true;
   if (!ws || ws_bytes < need) return false;
@@ -513,6 +536,7 @@ const char* ha_status_string(int status) {
     case HA_ERR_UNSUPPORTED: return "HA_ERR_UNSUPPORTED: configuration not supported by this library";
     case HA_ERR_WORKSPACE: return "HA_ERR_WORKSPACE: workspace missing, misaligned or too small";
     case HA_ERR_DEVICE: return "HA_ERR_DEVICE: HIP launch failed";
+    case HA_ERR_SCRATCH: return "HA_ERR_SCRATCH: the layer needs more scratch than the static array holds";
     default: return "unknown ha_status";
   }
 }
@@ -574,6 +598,23 @@ int ha_prefill(const ha_layer_desc* desc, const int32_t* head_kind, const void* 
     if (st != HA_OK) return st;
   }
   return HA_OK;
+}
+
+int ha_prefill_static(const ha_layer_desc* desc, const int32_t* head_kind, const void* Q, const void* K,
+                      const void* V, const float* P_idx, const float* xa_scale, const float* xa_offset, float* O,
+                      float* O_out, ha_aux* aux, void* stream) {
+  Heads h;
+  int st = check_desc(desc, head_kind, &h);
+  if (st != HA_OK) return st;
+  if (!Q || !K || !V || !O) return HA_ERR_ARG;
+  if (!h.ret.empty() && !P_idx) return HA_ERR_ARG;
+  if (desc->n_out > 0 && (!xa_scale || !xa_offset || !O_out)) return HA_ERR_ARG;
+  if (layout_of(desc, h).total > HA_STATIC_SCRATCH_BYTES) return HA_ERR_SCRATCH;
+  void* ws = nullptr;
+  st = static_scratch(&ws);
+  if (st != HA_OK) return st;
+  return ha_prefill(desc, head_kind, Q, K, V, P_idx, xa_scale, xa_offset, O, O_out, aux, ws,
+                    HA_STATIC_SCRATCH_BYTES, stream);
 }
 
 int ha_index_project(const ha_layer_desc* desc, const int32_t* head_kind, const void* Q, const void* K,

@@ -38,7 +38,8 @@
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
  *     and is asynchronous: outputs are valid once the stream has completed.
  *     No entry point synchronises.
- *   - The library holds no global mutable state; concurrent calls are safe
+ *   - The library holds no global mutable state apart from the scratch of
+ *     ha_prefill_static; concurrent calls of the other entry points are safe
  *     as long as they do not share output or workspace buffers.
  *   - Layouts are token-major and contiguous:
  *       Q  bf16 [N, Hq, D]       K, V  bf16 [N, Hkv, D]
@@ -57,7 +58,10 @@
 extern "C" {
 #endif
 
-#define HA_VERSION 5
+#define HA_VERSION 6
+
+/* Size of the device scratch array ha_prefill_static uses on each GPU. */
+#define HA_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
 
 typedef enum {
   HA_SWA = 0,        /* causal sliding window: keys i-w < j <= i */
@@ -74,7 +78,9 @@ typedef enum {
                             * or clusters, force_block0 with clusters, index_bits 8
                             * outside block mode with block_score 0 */
   HA_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than ha_workspace_bytes() */
-  HA_ERR_DEVICE = 4        /* a HIP launch or query failed */
+  HA_ERR_DEVICE = 4,       /* a HIP launch or query failed */
+  HA_ERR_SCRATCH = 5       /* ha_prefill_static: the layer needs more scratch than
+                            * HA_STATIC_SCRATCH_BYTES */
 } ha_status;
 
 typedef struct {
@@ -181,6 +187,25 @@ int ha_prefill(const ha_layer_desc* desc, const int32_t* head_kind,
                const float* xa_scale, const float* xa_offset,
                float* O, float* O_out, ha_aux* aux,
                void* workspace, size_t ws_bytes, void* stream);
+
+/* Whole-layer prefill that allocates nothing, for callers that cannot call
+ * hipMalloc or bring a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Arguments and results as
+ * ha_prefill, without the workspace: the kernels use a device array of
+ * HA_STATIC_SCRATCH_BYTES bytes that the library holds on every GPU it runs
+ * on until the process ends (its address is looked up once per device, on
+ * the first call made with that device current).
+ *   Returns HA_ERR_SCRATCH, before any HIP call, when
+ *   ha_workspace_bytes(desc, head_kind) > HA_STATIC_SCRATCH_BYTES (the 1M
+ *   cluster-mode layer, for one, needs about 2.4 GB).
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind: calls that overlap on one GPU (several streams or threads) race,
+ * so the caller serialises them.  No entry point ever calls hipMalloc,
+ * hipFree or an allocating library routine. */
+int ha_prefill_static(const ha_layer_desc* desc, const int32_t* head_kind,
+                      const void* Q, const void* K, const void* V, const float* P_idx,
+                      const float* xa_scale, const float* xa_offset,
+                      float* O, float* O_out, ha_aux* aux, void* stream);
 
 /* Stage: low-rank projection (RTPurboV2, low-rank projector passage).
  *   qlow[t] = Q[:, h_t, :] P[g(h_t)] for the t-th retrieval head h_t, [Hret, N, r]

@@ -23,11 +23,11 @@ def test_header_and_binding_agree_and_library_exports_all():
     L = ha.lib()
     for name in decl:
         assert hasattr(L, name), name
-    assert L.ha_version() == 5
+    assert L.ha_version() == 6
 
 
 def test_status_strings():
-    for c in range(5):
+    for c in range(6):
         assert ha.status_string(c).startswith("HA_")
     assert "unknown" in ha.status_string(99)
 
@@ -152,3 +152,28 @@ def test_binding_raises_on_error():
     with pytest.raises(ha.HAError) as ei:
         ha.ha_attn_band(_desc(head_dim=64), [0] * 8, FAKE, FAKE, FAKE, FAKE, stream=0)
     assert ei.value.code == ha.HA_ERR_UNSUPPORTED
+
+
+def test_static_entry_point_rejects_layers_beyond_its_scratch():
+    # the 1M cluster-mode layer needs ~2.4 GB of scratch: rejected on the host,
+    # before any HIP call (no GPU needed)
+    import synth
+    w = synth.WORKLOADS["allsparse_1m"]
+    d = ha.make_desc(w.n_tokens, w.n_q_heads, w.n_kv_heads, 128, window=w.window, topk=w.topk,
+                     n_clusters=w.n_clusters, kmeans_iters=w.kmeans_iters, kmeans_stride=w.kmeans_stride)
+    assert ha.ha_workspace_bytes(d, w.head_kind) > ha.HA_STATIC_SCRATCH_BYTES
+    rc = ha.lib().ha_prefill_static(ctypes.byref(d), ha._kinds(w.head_kind), FAKE, FAKE, FAKE, FAKE, None, None,
+                                    FAKE, None, None, None)
+    assert rc == ha.HA_ERR_SCRATCH
+    # argument errors come first
+    rc = ha.lib().ha_prefill_static(ctypes.byref(d), ha._kinds(w.head_kind), FAKE, FAKE, FAKE, None, None, None,
+                                    FAKE, None, None, None)
+    assert rc == ha.HA_ERR_ARG
+    # the default workloads that fit: every one but the 1M layers
+    for name, wl in synth.WORKLOADS.items():
+        dd = ha.make_desc(wl.n_tokens, wl.n_q_heads, wl.n_kv_heads, 128, **{
+            k: v for k, v in wl.desc_dict().items()
+            if k not in ("n_tokens", "n_q_heads", "n_kv_heads", "head_dim")})
+        fits = ha.ha_workspace_bytes(dd, wl.head_kind) <= ha.HA_STATIC_SCRATCH_BYTES
+        assert fits == (wl.n_tokens < (1 << 20)), name
+
