@@ -103,6 +103,7 @@ struct SelectParams {
   __bf16* c_hi;        // scratch: [Hkv, M, parts * r] split centroids / block representatives
   __bf16* c_lo;
   int32_t* first_mem;  // [Hkv, M] smallest member position (INT_MAX if empty or not a candidate)
+  uint32_t* cnorm;     // [Hkv] largest candidate-vector norm (fp32 bits), for the scoring error bound
   const int8_t* kcodes;  // 8-bit indexer keys [Hkv, N, r] (nullptr: fp32 klow)
   const float* kscale;   // [Hkv, N] their scales
   int N, n_qb, window, topk, force_block0, M;

@@ -338,20 +338,43 @@ __global__ __launch_bounds__(NT) void km_update_kernel(KmeansParams p) {
 // first CSR member is the smallest position); score = max over the query
 // block's rows of qlow_i . C_m; the topk best by (score desc, cluster asc).
 
-// Per layer, once: centroids split into bf16 hi/lo parts and the first
-// (smallest) member position of every cluster (INT_MAX when empty).
+// Largest candidate-vector norm of a KV head (fp32 bits; a non-negative
+// float orders as its bits): per wave the max of the lanes' squared norms,
+// one atomic per wave (a NaN norm counts as +inf).  The counters start at
+// zero (sel_clear_kernel).
+__device__ __forceinline__ void cnorm_max(uint32_t* cnorm, float n2) {
+  if (n2 != n2) n2 = __builtin_inff();   // a NaN component makes the bound infinite
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) n2 = fmaxf(n2, __shfl_xor(n2, o));
+  if ((threadIdx.x & 63) == 0) atomicMax(cnorm, __float_as_uint(sqrtf(n2)));
+}
+
+__global__ void sel_clear_kernel(uint32_t* w, int n) {
+  if ((int)threadIdx.x < n) w[threadIdx.x] = 0u;
+}
+
+// Per layer, once: centroids split into bf16 hi/lo parts, the first
+// (smallest) member position of every cluster (INT_MAX when empty) and the
+// largest centroid norm.
 __global__ __launch_bounds__(NT) void cluster_prep_kernel(SelectParams p) {
   const int g = blockIdx.y;
   const int m = blockIdx.x * NT + threadIdx.x;
-  if (m >= p.M) return;
-  const float* c = p.cent + ((size_t)g * p.M + m) * R;
-  __bf16* hi = p.c_hi + ((size_t)g * p.M + m) * R;
-  __bf16* lo = p.c_lo + ((size_t)g * p.M + m) * R;
+  float n2 = 0.f;
+  if (m < p.M) {
+    const float* c = p.cent + ((size_t)g * p.M + m) * R;
+    __bf16* hi = p.c_hi + ((size_t)g * p.M + m) * R;
+    __bf16* lo = p.c_lo + ((size_t)g * p.M + m) * R;
 #pragma unroll
-  for (int r = 0; r < R; ++r) dev::split2(c[r], hi[r], lo[r]);
-  const int32_t* off = p.csr_off + (size_t)g * (p.M + 1);
-  const int lo_i = off[m], hi_i = off[m + 1];
-  p.first_mem[(size_t)g * p.M + m] = hi_i > lo_i ? p.csr_mem[(size_t)g * p.N + lo_i] : INT_MAX;
+    for (int r = 0; r < R; ++r) {
+      const float v = c[r];
+      n2 = fmaf(v, v, n2);
+      dev::split2(v, hi[r], lo[r]);
+    }
+    const int32_t* off = p.csr_off + (size_t)g * (p.M + 1);
+    const int lo_i = off[m], hi_i = off[m + 1];
+    p.first_mem[(size_t)g * p.M + m] = hi_i > lo_i ? p.csr_mem[(size_t)g * p.N + lo_i] : INT_MAX;
+  }
+  cnorm_max(p.cnorm + g, n2);
 }
 
 // Per layer, once, for block mode with a representative score: each key
@@ -364,75 +387,111 @@ __global__ __launch_bounds__(NT) void block_prep_kernel(SelectParams p) {
   const int g = blockIdx.y;
   const int t = blockIdx.x * NT + threadIdx.x;
   const int c = t / R, d = t % R;
-  if (c >= p.M) return;
-  const int j0 = c * kBlock, j1 = min(p.N, j0 + kBlock);
-  const float* kl = p.klow + (size_t)g * p.N * R + d;
-  __bf16* hi = p.c_hi + ((size_t)g * p.M + c) * R * NPART;
-  __bf16* lo = p.c_lo + ((size_t)g * p.M + c) * R * NPART;
-  if (NPART == 1) {
-    float s = 0.f;
-    for (int j = j0; j < j1; ++j) s += kl[(size_t)j * R];
-    dev::split2(s / (float)(j1 - j0), hi[d], lo[d]);
-  } else {
-    float a = -__builtin_inff(), b = __builtin_inff();
-    for (int j = j0; j < j1; ++j) {
-      const float v = kl[(size_t)j * R];
-      a = fmaxf(a, v);
-      b = fminf(b, v);
+  float n2 = 0.f;
+  if (c < p.M) {
+    const int j0 = c * kBlock, j1 = min(p.N, j0 + kBlock);
+    const float* kl = p.klow + (size_t)g * p.N * R + d;
+    __bf16* hi = p.c_hi + ((size_t)g * p.M + c) * R * NPART;
+    __bf16* lo = p.c_lo + ((size_t)g * p.M + c) * R * NPART;
+    if (NPART == 1) {
+      float s = 0.f;
+      for (int j = j0; j < j1; ++j) s += kl[(size_t)j * R];
+      const float v = s / (float)(j1 - j0);
+      n2 = v * v;
+      dev::split2(v, hi[d], lo[d]);
+    } else {
+      float a = -__builtin_inff(), b = __builtin_inff();
+      for (int j = j0; j < j1; ++j) {
+        const float v = kl[(size_t)j * R];
+        a = fmaxf(a, v);
+        b = fminf(b, v);
+      }
+      n2 = fmaf(a, a, b * b);
+      dev::split2(a, hi[d], lo[d]);
+      dev::split2(b, hi[R + d], lo[R + d]);
     }
-    dev::split2(a, hi[d], lo[d]);
-    dev::split2(b, hi[R + d], lo[R + d]);
+    if (d == 0) p.first_mem[(size_t)g * p.M + c] = (p.force_block0 && c == 0) ? INT_MAX : j0;
   }
-  if (d == 0) p.first_mem[(size_t)g * p.M + c] = (p.force_block0 && c == 0) ? INT_MAX : j0;
+  // the R threads of a block are consecutive lanes: their sum is the block's
+  // squared norm (NPART 2: of the 2R-vector of maxima and minima)
+#pragma unroll
+  for (int o = 1; o < R; o <<= 1) n2 += __shfl_xor(n2, o);
+  cnorm_max(p.cnorm + g, n2);
 }
 
 // One workgroup per (retrieval head, query block).  S[i][m] = qlow_i . C_m on
-// MFMA (32 rows x 32 centroids per instruction, k = r = 16), split operands;
-// a lane ends with 16 rows of one centroid, so the row max is a lane-local
-// reduction plus one exchange with lane ^ 32.  Wave w takes centroid tiles
-// w, w+4, ...  The scores stay in LDS for the exact top-k.
+// MFMA (32 rows x 32 centroids per instruction, k = r = 16); a lane ends with
+// 16 rows of one centroid, so the row max is a lane-local reduction plus one
+// exchange with lane ^ 32.  Wave w takes centroid tiles w, w+4, ...  Only
+// clusters with a member at or before the block's last row minus the window
+// are eligible.
 //
-// Exact prefilter for the top-k: each of the 128 scoring lanes keeps the
-// largest key it wrote.  If tau is the k-th largest of these lane maxima, at
-// least k keys are >= tau, so the k-th largest key is >= tau and every key
-// of the answer (ties at the k-th value included) is >= tau.  One pass
-// collects the keys >= tau in index order (each wave a contiguous quarter of
-// the clusters, into its own region of kCapW slots, the rest of the region
-// zero-filled), and the radix select runs on those 4 * kCapW slots.  A wave
-// that finds more than kCapW candidates sends the block to the full select.
+// Exact scores (the selection's definition): split operands, three bf16
+// passes ql.ch + qh.cl + qh.ch, fp32-accurate; the order key of the row max
+// ranks the clusters (larger first, lower index first among equal keys).
+// They are computed only where they decide something:
+//   1. approximate pass: one product qh.ch per (row, cluster) gives an
+//      approximate row max a_m for every cluster (-inf when ineligible) in
+//      LDS; each of the 128 scoring lanes keeps the largest it wrote.
+//   2. error bound: qh.ch differs from the three-pass score by qh.cl + ql.ch
+//      plus accumulation rounding, at most
+//        eps = 1.03 * 2^-7 * max_i |q_i| * max_m |C_m|   (+ a denormal floor)
+//      (|cl| <= 2^-8 |C|, |ql| <= 2^-8 |q| per component; Cauchy-Schwarz
+//      over the r components; the 3% covers the norms' own rounding and the
+//      fp32 accumulation of up to 48 products).  The row max moves by at most
+//      eps as well.
+//   3. prefilter: tau = the topk-th largest lane maximum.  At least topk
+//      eligible clusters have a >= tau, hence exact score >= tau - eps, so
+//      the k-th exact score is >= tau - eps and every cluster of the exact
+//      top-k (ties included) has a >= tau - 2 eps.  Those candidates are
+//      collected in index order (each wave a contiguous quarter of the
+//      clusters, into its own region of kCapW slots).  Fewer than topk valid
+//      lane maxima: every eligible cluster is a candidate.
+//   4. the candidates are re-scored with the three passes (the same
+//      operands and the same product order as a full exact pass, so the
+//      keys are bit-identical to it), packed with their index as
+//      (key << 32 | 0xFFFF - m), and a candidate is chosen when fewer than k
+//      packed keys exceed its own; the chosen ones keep index order.
+// More than kCapW candidates in a wave or 2 * NT in all, a bound that is not
+// finite, or a budget above 128 (k > kGroups) sends the block through the
+// exact pass over every cluster and a radix select over all of them.
 //
 // A unit of several slots (group-shared selection) repeats the scoring for
-// each slot and keeps the max key per cluster (the order key is monotone);
-// a lane owns the same clusters for every slot, so the lane maxima and the
-// prefilter hold for the max scores as they do for one slot.
+// each slot and keeps the max per cluster (the order key is monotone); a
+// lane owns the same clusters for every slot, so the lane maxima and the
+// prefilter hold for the max scores as they do for one slot, and the bound
+// uses the largest row norm over the slots.
 //
 // The same kernel scores key-block representatives (block mode with a
 // representative score): candidate m = key block m, "first member" = its
 // first key.  NPART = 2 scores the per-dimension extremes bound as a 32-dim
 // dot product: sum_d max(q_d a_d, q_d b_d) with a >= b equals
 // max(q, 0) . a + min(q, 0) . b, so part 0 pairs max(q, 0) with the block
-// maxima and part 1 pairs min(q, 0) with the minima.
+// maxima and part 1 pairs min(q, 0) with the minima; |(max(q,0), min(q,0))|
+// = |q| and the candidate norm is |(a, b)|.
 constexpr int kSelBlocks = 1;
 // Padding after the selection tables: the last tile's lanes past the end
 // read up to 31 rows of 64 B (split parts) and 31 first members beyond M.
 constexpr size_t kTablePad = 4096;
 constexpr int kGroups = 128;      // scoring lanes (4 waves x 32)
 constexpr int kCapW = 192;        // candidate slots per wave
+constexpr float kEpsRel = 1.03f * 0x1p-7f;
 
 template <int NPART>
-__global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
+__global__ __launch_bounds__(NT, 2) void select_clusters_kernel(SelectParams p) {
   static_assert(kSelBlocks == 1, "the prefilter handles one query block per workgroup");
-  __shared__ uint32_t keys[kSelBlocks][kMaxSelCand];
+  // scores (approximate pass: fp32 values; exact pass: order keys); after
+  // the candidates are collected, scratch for their packed keys and the
+  // budget's weights
+  __shared__ __attribute__((aligned(16))) uint32_t keys[kMaxSelCand + 32];   // + 32: approximate-pass sink
   __shared__ int hist[dev::kHistWords];
   __shared__ int tmp4[8];
   __shared__ int bcast[2];
-  __shared__ uint32_t ckeys[4 * kCapW];
   __shared__ uint16_t cidx[4 * kCapW];
   __shared__ uint32_t gmax[kGroups];
   __shared__ uint32_t tau_s;
-  __shared__ int ovf;
-  __shared__ uint32_t sink_word;                  // store target of padding lanes
-  __shared__ uint32_t sel_keys[NT];               // adaptive budget: keys of the top-k
+  __shared__ int cnt_s[4], nel_s[4];
+  __shared__ uint32_t sink_word;                  // store target of padding lanes (exact pass)
   const int t0 = (int)(p.unit[blockIdx.y] & 0xFFFFu), ns = (int)(p.unit[blockIdx.y] >> 16);
   const int tid = threadIdx.x;
   const int lane = tid & 63, lr = lane & 31, lh = lane >> 5;
@@ -441,6 +500,8 @@ __global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
   const int b0 = blockIdx.x * kSelBlocks;
   const int nb = min(kSelBlocks, p.n_qb - b0);
   if (p.topk == 0) return;
+  // the approximate pass pays off when the prefilter applies (k <= kGroups)
+  const bool approx = p.topk <= kGroups;
 
   int nrow[kSelBlocks], lim[kSelBlocks];
 #pragma unroll
@@ -451,8 +512,10 @@ __global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
   }
   // split query rows of slot t (parts as above); rows past the end of a
   // ragged last block repeat the block's first row, so the row max needs no
-  // mask
+  // mask.  qn2 tracks the largest squared row norm seen (the lane's rows).
   dev::bf16x8 qh[NPART][2], ql[NPART][2];
+  float qn2 = 0.f;
+  bool qbad = false;                // a row norm that is not finite
   auto load_q = [&](int t) {
     const int qs0 = b0 * kBlock;
 #pragma unroll
@@ -460,9 +523,11 @@ __global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
       const int i = rt * 32 + lr;
       const int row = nb > 0 ? qs0 + (i < nrow[0] ? i : 0) : 0;
       const float* qp = p.qlow + ((size_t)t * p.N + row) * R + lh * 8;
+      float ss = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float v = qp[e];
+        ss = fmaf(v, v, ss);
 #pragma unroll
         for (int part = 0; part < NPART; ++part) {
           const float vp = NPART == 1 ? v : (part == 0 ? fmaxf(v, 0.f) : fminf(v, 0.f));
@@ -472,205 +537,332 @@ __global__ __launch_bounds__(NT) void select_clusters_kernel(SelectParams p) {
           ql[part][rt][e] = ll;
         }
       }
+      const float rn2 = dev::pair32_sum(ss);
+      qbad |= !(rn2 <= __FLT_MAX__);
+      qn2 = fmaxf(qn2, rn2);
     }
   };
   const __bf16* chi = p.c_hi + (size_t)g * p.M * R * NPART;
   const __bf16* clo = p.c_lo + (size_t)g * p.M * R * NPART;
   const int32_t* fm = p.first_mem + (size_t)g * p.M;
-  int n_el[kSelBlocks] = {};
-  uint32_t gmx = 0;                 // largest key this lane wrote
+  int n_el = 0;                     // exact pass: eligible clusters counted by this lane
+  uint32_t gmx = 0;                 // exact pass: largest key this lane wrote
+  float gmxf = -__builtin_inff();   // approximate pass: largest value this lane wrote
   const int n_tiles = (p.M + 31) / 32;
-  // A wave's tiles are x = wave + 4 i.  Operands are loaded kPre tiles ahead
-  // (register ring, static slots: the loop is unrolled by kPre).
-  constexpr int kPre = 4;
-  // A ring slot holds a tile's split centroids and, per lane, the first
-  // member of its cluster (eligibility: a member <= lim).
   // Buffer loads: the lane's offset inside a tile is fixed and the tile's
   // offset is wave-uniform (scalar), so a load needs no vector address
   // arithmetic.  Lanes of the last tile past cluster M-1 may read past the
   // end of a table (the scalar offset is not part of the range check): the
   // scratch is padded by kTablePad bytes so those reads stay inside it, and
-  // whatever they return is discarded (their keys go to the dummy word).
+  // whatever they return is discarded.
   const __amdgpu_buffer_rsrc_t rs_hi = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<__bf16*>(chi), 0, p.M * NPART * R * 2, dev::kBufWord3);
   const __amdgpu_buffer_rsrc_t rs_lo = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<__bf16*>(clo), 0, p.M * NPART * R * 2, dev::kBufWord3);
   const __amdgpu_buffer_rsrc_t rs_fm = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int32_t*>(fm), 0, p.M * 4, dev::kBufWord3);
-  auto ld = [&](int x, dev::bf16x8 (&bh)[NPART], dev::bf16x8 (&bl)[NPART], int& f) {
-#pragma unroll
-    for (int part = 0; part < NPART; ++part) {
-      const int vo = (lr * NPART + part) * R * 2 + lh * 16;
-      const int so = x * 32 * NPART * R * 2;
-      bh[part] = __builtin_bit_cast(dev::bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs_hi, vo, so, 0));
-      bl[part] = __builtin_bit_cast(dev::bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs_lo, vo, so, 0));
-    }
-    f = (int)__builtin_amdgcn_raw_buffer_load_b32(rs_fm, lr * 4, x * 32 * 4, 0);
-  };
-  dev::bf16x8 rbh[kPre][NPART], rbl[kPre][NPART];
-  int rfm[kPre];
   const int lim0 = lim[0];
-  for (int s = 0; s < ns; ++s) {
-    load_q(t0 + s);
-    // slot order, as in the loop body, so the first group waits only for its own slot
+  float* keysf = reinterpret_cast<float*>(keys);
+
+  // Scoring pass over every cluster tile: approximate (one product, hi
+  // parts only) or exact (three products).
+  auto scan = [&](auto exact_c) {
+    constexpr bool kExact = decltype(exact_c)::value;
+    // operands are loaded kPre tiles ahead (register ring, static slots: the
+    // loop is unrolled by kPre); a slot holds a tile's split centroids and,
+    // per lane, the first member of its cluster (eligibility: a member <= lim)
+    constexpr int kPre = (kExact || NPART == 2) ? 4 : 8;
+    constexpr int kProd = kExact ? 3 : 1;
+    auto ld = [&](int x, dev::bf16x8 (&bh)[NPART], dev::bf16x8 (&bl)[NPART], int& f) {
 #pragma unroll
-    for (int u = 0; u < kPre; ++u) {
-      ld(min(n_tiles - 1, wave + 4 * u), rbh[u], rbl[u], rfm[u]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // The keys of tile x are finished one tile later, after the products of
-    // the next tile are issued, so the matrix-result reads never wait on the
-    // products just issued.  Key of a cluster: order key of the row max, 0 if
-    // ineligible (no member <= lim); padding lanes store to a dummy word.
-    dev::f32x16 pacc[2] = {dev::f32x16{}, dev::f32x16{}};
-    int pm = INT_MAX;                 // the first finish stores 0 to the dummy word
-    bool pel = false;
-    // The loop is instantiated once for the first slot of a unit (plain
-    // store) and once for later slots (max with the stored key), so its body
-    // is one basic block and the previous tile's vector work can be placed
-    // between the current tile's matrix products.
-    auto run = [&](auto later_slot) {
-      constexpr bool kLater = decltype(later_slot)::value;
-      auto finish = [&]() {
-        float mx = -__builtin_inff();
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, pacc[rt][e]);
-        mx = dev::pair32_max(mx);
-        const bool mok = pm < p.M;
-        const bool el = mok & pel;
-        const uint32_t key = el ? dev::order_key(mx) : 0u;
-        uint32_t* dst = mok ? &keys[0][pm] : &sink_word;
-        if constexpr (kLater) {
-          *dst = max(*dst, key);
-        } else {
-          *dst = key;
-          n_el[0] += (int)(el & (lh == 0));
-        }
-        gmx = max(gmx, key);
-      };
-      // Groups of kPre tiles run whole (tiles past the end compute on the
-      // last tile and store nothing: their centroid index is >= M), so the
-      // body has no branches around loads.
-      for (int x0 = wave; x0 < n_tiles; x0 += 4 * kPre) {
-#pragma unroll
-        for (int u = 0; u < kPre; ++u) {
-          const int x = x0 + 4 * u;
-          // the two row tiles' chains alternate, so no product waits on the
-          // one just issued
-          dev::f32x16 acc[2] = {dev::f32x16{}, dev::f32x16{}};
-#pragma unroll
-          for (int part = 0; part < NPART; ++part) {
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) acc[rt] = dev::mfma32(ql[part][rt], rbh[u][part], acc[rt]);
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) acc[rt] = dev::mfma32(qh[part][rt], rbl[u][part], acc[rt]);
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) acc[rt] = dev::mfma32(qh[part][rt], rbh[u][part], acc[rt]);
-          }
-          // eligibility of the slot's cluster, taken before the slot's refill
-          // is issued (the empty asm orders the two), so the refill lands in
-          // the slot's own registers: no ring rotation copies, which would
-          // wait for the newest loads
-          const bool fel = (lim0 >= 0) & (rfm[u] <= lim0);
-          { const int fi = fel; asm volatile("" ::"v"(fi) : "memory"); }
-          ld(min(x + 4 * kPre, n_tiles - 1), rbh[u], rbl[u], rfm[u]);
-          finish();
-          pacc[0] = acc[0];
-          pacc[1] = acc[1];
-          pm = x * 32 + lr;
-          pel = fel;
-          // products of this tile, the previous tile's vector work between
-          // them, then the slot's refill
-#pragma unroll
-          for (int i = 0; i < 6 * NPART; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-          }
-          __builtin_amdgcn_sched_group_barrier(0x020, 2 * NPART + 1, 0);
-        }
+      for (int part = 0; part < NPART; ++part) {
+        const int vo = (lr * NPART + part) * R * 2 + lh * 16;
+        const int so = x * 32 * NPART * R * 2;
+        bh[part] = __builtin_bit_cast(dev::bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs_hi, vo, so, 0));
+        if constexpr (kExact)
+          bl[part] = __builtin_bit_cast(dev::bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs_lo, vo, so, 0));
       }
-      finish();
+      f = (int)__builtin_amdgcn_raw_buffer_load_b32(rs_fm, lr * 4, x * 32 * 4, 0);
     };
-    if (s == 0) run(std::integral_constant<bool, false>{});
-    else run(std::integral_constant<bool, true>{});
-  }
-  if (lh == 0) gmax[wave * 32 + lr] = gmx;
-  if (tid == 0) {
-    tau_s = 1u;
-    ovf = 0;
-  }
-  int nE;
-  dev::block_excl_scan(n_el[0], tmp4, &nE);     // (synchronizes)
-  const int k = min(p.topk, nE);
+    dev::bf16x8 rbh[kPre][NPART], rbl[kPre][NPART];
+    int rfm[kPre];
+    gmx = 0;
+    gmxf = -__builtin_inff();
+    n_el = 0;
+    for (int s = 0; s < ns; ++s) {
+      load_q(t0 + s);
+      // slot order, as in the loop body, so the first group waits only for its own slot
+#pragma unroll
+      for (int u = 0; u < kPre; ++u) {
+        ld(min(n_tiles - 1, wave + 4 * u), rbh[u], rbl[u], rfm[u]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // The scores of tile x are finished one tile later, after the products
+      // of the next tile are issued, so the matrix-result reads never wait on
+      // the products just issued.
+      dev::f32x16 pacc[2] = {dev::f32x16{}, dev::f32x16{}};
+      bool pel = false;
+      // the first finish stores 0 (exact) or -inf (approximate) to a sink;
+      // so do tiles past the end, which would otherwise add a second copy of
+      // the last tile's values to the lane maxima
+      int pm = kExact ? INT_MAX : kMaxSelCand + lr;
+      // The loop is instantiated once for the first slot of a unit (plain
+      // store) and once for later slots (max with the stored value), so its
+      // body is one basic block and the previous tile's vector work can be
+      // placed between the current tile's matrix products.
+      auto run = [&](auto later_slot) {
+        constexpr bool kLater = decltype(later_slot)::value;
+        auto finish = [&]() {
+          float mx = -__builtin_inff();
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, pacc[rt][e]);
+          mx = dev::pair32_max(mx);
+          if constexpr (kExact) {
+            const bool mok = pm < p.M;
+            const bool el = mok & pel;
+            const uint32_t key = el ? dev::order_key(mx) : 0u;
+            uint32_t* dst = mok ? &keys[pm] : &sink_word;
+            if constexpr (kLater) {
+              *dst = max(*dst, key);
+            } else {
+              *dst = key;
+              n_el += (int)(el & (lh == 0));
+            }
+            gmx = max(gmx, key);
+          } else {
+            const float v = pel ? mx : -__builtin_inff();
+            if constexpr (kLater) keysf[pm] = fmaxf(keysf[pm], v);
+            else keysf[pm] = v;
+            gmxf = fmaxf(gmxf, v);
+          }
+        };
+        // Groups of kPre tiles run whole (tiles past the end compute on the
+        // last tile), so the body has no branches around loads.
+        for (int x0 = wave; x0 < n_tiles; x0 += 4 * kPre) {
+#pragma unroll
+          for (int u = 0; u < kPre; ++u) {
+            const int x = x0 + 4 * u;
+            // the two row tiles' chains alternate, so no product waits on the
+            // one just issued
+            dev::f32x16 acc[2] = {dev::f32x16{}, dev::f32x16{}};
+#pragma unroll
+            for (int part = 0; part < NPART; ++part) {
+              if constexpr (kExact) {
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) acc[rt] = dev::mfma32(ql[part][rt], rbh[u][part], acc[rt]);
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) acc[rt] = dev::mfma32(qh[part][rt], rbl[u][part], acc[rt]);
+              }
+#pragma unroll
+              for (int rt = 0; rt < 2; ++rt) acc[rt] = dev::mfma32(qh[part][rt], rbh[u][part], acc[rt]);
+            }
+            // eligibility of the slot's cluster, taken before the slot's refill
+            // is issued (the empty asm orders the two), so the refill lands in
+            // the slot's own registers: no ring rotation copies, which would
+            // wait for the newest loads
+            // (approximate pass: lanes past cluster M-1 and tiles past the
+            // end are ineligible)
+            const bool real = x < n_tiles;
+            const bool fel = (lim0 >= 0) & (rfm[u] <= lim0) & (kExact || (real & (lr < p.M - x * 32)));
+            { const int fi = fel; asm volatile("" ::"v"(fi) : "memory"); }
+            ld(min(x + 4 * kPre, n_tiles - 1), rbh[u], rbl[u], rfm[u]);
+            finish();
+            pacc[0] = acc[0];
+            pacc[1] = acc[1];
+            pm = (kExact || real ? x * 32 : kMaxSelCand) + lr;
+            pel = fel;
+            // products of this tile, the previous tile's vector work between
+            // them, then the slot's refill
+#pragma unroll
+            for (int i = 0; i < 2 * kProd * NPART; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x002, kExact ? 5 : 10, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x020, (kExact ? 2 : 1) * NPART + 1, 0);
+          }
+        }
+        finish();
+      };
+      // a wave without tiles stores nothing
+      if (wave < n_tiles) {
+        if (s == 0) run(std::integral_constant<bool, false>{});
+        else run(std::integral_constant<bool, true>{});
+      }
+    }
+  };
+
   const size_t row_stride = (size_t)p.n_qb * p.topk;   // between slots' sel rows
   int32_t* out = p.sel + ((size_t)t0 * p.n_qb + b0) * p.topk;
   // a unit of several slots, or the adaptive budget, selects into LDS (the
   // histogram is free once the last radix pass is done), cuts the row to the
-  // budget and copies it to every slot
+  // budget and copies it to every slot; the chosen keys go behind the row
   const bool adaptive = p.mass > 0.f;
   int32_t* dst_row = (ns == 1 && !adaptive) ? out : reinterpret_cast<int32_t*>(hist);
-  uint32_t* rkeys = adaptive ? sel_keys : nullptr;
-  auto copy_row = [&]() {
+  uint32_t* rkeys = adaptive ? reinterpret_cast<uint32_t*>(hist) + 1024 : nullptr;
+  auto copy_row = [&](int k) {
     if (dst_row == out) return;
     __syncthreads();
-    // ckeys is free once the select is done: it holds the budget's weights
+    // the scores are dead once the select is done: they hold the budget's weights
     if (adaptive && k > 0)
-      dev::adaptive_cut(dst_row, sel_keys, k, p.topk, p.mass_scale_log2, p.mass, reinterpret_cast<float*>(ckeys),
-                        tmp4, bcast);
+      dev::adaptive_cut(dst_row, rkeys, k, p.topk, p.mass_scale_log2, p.mass, keysf, tmp4, bcast);
     for (int x = tid; x < ns * p.topk; x += NT) {
       const int s = x / p.topk, e = x - s * p.topk;
       out[s * row_stride + e] = dst_row[e];
     }
   };
-  if (k > kGroups) {
-    dev::topk_select(keys[0], p.M, k, p.topk, 0, dst_row, hist, tmp4, bcast, nullptr, rkeys);
-    copy_row();
+  // exact keys of every cluster, then the radix select over all of them
+  auto select_all_exact = [&]() {
+    scan(std::integral_constant<bool, true>{});
+    int nE;
+    dev::block_excl_scan(n_el, tmp4, &nE);     // (synchronizes)
+    const int k = min(p.topk, nE);
+    dev::topk_select(keys, p.M, k, p.topk, 0, dst_row, hist, tmp4, bcast, nullptr, rkeys);
+    copy_row(k);
+  };
+  if (!approx) {
+    select_all_exact();
     return;
   }
-  // tau = k-th largest lane maximum (the one with #{>} < k <= #{>=});
-  // eligible keys are >= 1, so tau >= 1 also drops the ineligible ones
-  if (k > 0 && tid < kGroups) {
-    const uint32_t gv = gmax[tid];
-    int gt = 0, ge = 0;
-    for (int j = 0; j < kGroups; ++j) {
-      const uint32_t v = gmax[j];
-      gt += v > gv;
-      ge += v >= gv;
+  scan(std::integral_constant<bool, false>{});
+  if (lh == 0) gmax[wave * 32 + lr] = dev::order_key(gmxf);
+  // largest row norm over the unit's slots (every wave holds all rows)
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) qn2 = fmaxf(qn2, __shfl_xor(qn2, o));
+  __syncthreads();
+  // tau = the topk-th largest lane maximum: the largest T with at least topk
+  // maxima >= T, found bit by bit from the top with wave ballots
+  if (wave == 0) {
+    const uint32_t a = gmax[lane], b = gmax[64 + lane];
+    uint32_t pre = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t c = pre | (1u << bit);
+      const int n = (int)__popcll(__ballot(a >= c)) + (int)__popcll(__ballot(b >= c));
+      if (n >= p.topk) pre = c;
     }
-    if (gt < k && k <= ge && gv > 1u) tau_s = gv;
+    if (lane == 0) tau_s = pre;
   }
   __syncthreads();
-  const uint32_t tau = tau_s;
-  {
-    const int per = ((p.M + 4 * 64 - 1) / (4 * 64)) * 64;
-    const int wa = min(p.M, wave * per), wb = min(p.M, wa + per);
-    uint32_t* ck = ckeys + wave * kCapW;
-    uint16_t* ci = cidx + wave * kCapW;
-    int cnt = 0;
-    for (int x0 = wa; x0 < wb; x0 += 64) {
-      const int x = x0 + lane;
-      const uint32_t u = x < wb ? keys[0][x] : 0u;
-      const bool take = u >= tau;
-      const uint64_t b = __ballot(take);
-      const int pos = cnt + (int)__popcll(b & ((1ull << lane) - 1ull));
-      if (take && pos < kCapW) {
-        ck[pos] = u;
-        ci[pos] = (uint16_t)x;
+  // candidate threshold; -FLT_MAX (every eligible cluster) when fewer than
+  // topk lane maxima are finite
+  const float tv = dev::key_value(tau_s);
+  const float qn = sqrtf(qn2), cn = __uint_as_float(p.cnorm[g]);
+  const float eps = kEpsRel * qn * cn + 0x1p-120f * (8.f * (qn + cn) + 1.f);
+  const bool bound_ok = eps < 1e36f && !(tv > 1e36f) && !(tv != tv) && !__any(qbad);
+  const float thr = tv >= -1e36f ? fmaxf(tv - 2.f * eps, -__FLT_MAX__) : -__FLT_MAX__;
+  // collect: all of the wave's values first (latency), then in index order
+  const int per = ((p.M + 4 * 64 - 1) / (4 * 64)) * 64;
+  const int wa = min(p.M, wave * per), wb = min(p.M, wa + per);
+  uint16_t* ci = cidx + wave * kCapW;
+  int cnt = 0, nel = 0;
+  constexpr int kColl = 16;
+  for (int x0 = wa; x0 < wb; x0 += 64 * kColl) {
+    float v[kColl];
+#pragma unroll
+    for (int i = 0; i < kColl; ++i) {
+      const int x = x0 + 64 * i + lane;
+      v[i] = x < wb ? keysf[x] : -__builtin_inff();
+    }
+#pragma unroll
+    for (int i = 0; i < kColl; ++i) {
+      nel += (int)__popcll(__ballot(v[i] >= -__FLT_MAX__));
+      const bool take = v[i] >= thr;
+      const uint64_t bt = __ballot(take);
+      const int pos = cnt + (int)__popcll(bt & ((1ull << lane) - 1ull));
+      if (take && pos < kCapW) ci[pos] = (uint16_t)(x0 + 64 * i + lane);
+      cnt += (int)__popcll(bt);
+    }
+  }
+  if (lane == 0) {
+    cnt_s[wave] = cnt;
+    nel_s[wave] = nel;
+  }
+  __syncthreads();
+  int n = 0, base = 0, nE = 0;
+  bool ovf = !bound_ok;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int c = cnt_s[w];
+    base += w < wave ? c : 0;
+    n += c;
+    nE += nel_s[w];
+    ovf |= c > kCapW;
+  }
+  ovf |= n > 2 * NT;
+  if (ovf) {
+    __syncthreads();    // the scores are rewritten
+    select_all_exact();
+    return;
+  }
+  const int k = min(p.topk, nE);
+  // exact keys of the wave's candidates, 32 at a time: lane (lr, lh) loads
+  // candidate lr's parts for dimensions lh*8 .. lh*8+7, as in the scan;
+  // packed keys go to pk[base + pos] (index order across the waves)
+  uint64_t* pk = reinterpret_cast<uint64_t*>(keys);
+  const int n_ct = (cnt + 31) / 32;
+  for (int s = 0; s < ns; ++s) {
+    if (ns > 1) load_q(t0 + s);
+    for (int x = 0; x < n_ct; ++x) {
+      const int pos = x * 32 + lr;
+      const bool valid = pos < cnt;
+      const int m = valid ? (int)ci[pos] : 0;
+      dev::f32x16 acc[2] = {dev::f32x16{}, dev::f32x16{}};
+#pragma unroll
+      for (int part = 0; part < NPART; ++part) {
+        const int vo = (m * NPART + part) * R * 2 + lh * 16;
+        const dev::bf16x8 bh = __builtin_bit_cast(dev::bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs_hi, vo, 0, 0));
+        const dev::bf16x8 bl = __builtin_bit_cast(dev::bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs_lo, vo, 0, 0));
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) acc[rt] = dev::mfma32(ql[part][rt], bh, acc[rt]);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) acc[rt] = dev::mfma32(qh[part][rt], bl, acc[rt]);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) acc[rt] = dev::mfma32(qh[part][rt], bh, acc[rt]);
       }
-      cnt += (int)__popcll(b);
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[rt][e]);
+      mx = dev::pair32_max(mx);
+      const uint64_t kk = ((uint64_t)dev::order_key(mx) << 32) | (uint32_t)(0xFFFF - m);
+      if (valid && lh == 0) pk[base + pos] = s == 0 ? kk : max(pk[base + pos], kk);
     }
-    for (int pos = cnt + lane; pos < kCapW; pos += 64) ck[pos] = 0u;
-    if (cnt > kCapW && lane == 0) ovf = 1;
   }
+  if (tid == 0) pk[n] = 0ull;         // pads the pairwise reads below; ranks below every key
   __syncthreads();
-  if (ovf == 0) {
-    dev::topk_select(ckeys, 4 * kCapW, k, p.topk, 0, dst_row, hist, tmp4, bcast, cidx, rkeys);
+  // rank = number of packed keys above one's own (all distinct); chosen when
+  // rank < k, so exactly k are chosen.  Candidate t and t + NT per thread.
+  const uint64_t ka = tid < n ? pk[tid] : 0ull, kb = tid + NT < n ? pk[tid + NT] : 0ull;
+  int ra = 0, rb = 0;
+  if (n > NT) {
+    for (int j = 0; j < n; j += 2) {
+      const uint64_t u0 = pk[j], u1 = pk[j + 1];
+      ra += (int)(u0 > ka) + (int)(u1 > ka);
+      rb += (int)(u0 > kb) + (int)(u1 > kb);
+    }
   } else {
-    dev::topk_select(keys[0], p.M, k, p.topk, 0, dst_row, hist, tmp4, bcast, nullptr, rkeys);
+    for (int j = 0; j < n; j += 2) {
+      const uint64_t u0 = pk[j], u1 = pk[j + 1];
+      ra += (int)(u0 > ka) + (int)(u1 > ka);
+    }
   }
-  copy_row();
+  const bool ca = tid < n && ra < k, cb = tid + NT < n && rb < k;
+  int na;
+  const int pa = dev::block_excl_scan((int)ca, tmp4, &na);   // (synchronizes)
+  int nbb;
+  const int pb = na + dev::block_excl_scan((int)cb, tmp4, &nbb);
+  if (ca) {
+    dst_row[pa] = 0xFFFF - (int)(uint32_t)(ka & 0xFFFFu);
+    if (rkeys) rkeys[pa] = (uint32_t)(ka >> 32);
+  }
+  if (cb) {
+    dst_row[pb] = 0xFFFF - (int)(uint32_t)(kb & 0xFFFFu);
+    if (rkeys) rkeys[pb] = (uint32_t)(kb >> 32);
+  }
+  for (int x = k + tid; x < p.topk; x += NT) dst_row[x] = -1;
+  copy_row(k);
 }
 
 }  // namespace
@@ -702,6 +894,7 @@ hipError_t launch_kmeans(KmeansParams p, int Hkv, int iters, hipStream_t s) {
 
 hipError_t launch_select_clusters(const SelectParams& p, int Hkv, hipStream_t s) {
   if (p.n_ret == 0 || p.n_qb == 0) return hipSuccess;
+  hipLaunchKernelGGL(sel_clear_kernel, dim3(1), dim3(kMaxHeads), 0, s, p.cnorm, Hkv);
   hipLaunchKernelGGL(cluster_prep_kernel, dim3((p.M + NT - 1) / NT, Hkv), dim3(NT), 0, s, p);
   hipLaunchKernelGGL(select_clusters_kernel<1>, dim3((p.n_qb + kSelBlocks - 1) / kSelBlocks, p.n_units), dim3(NT),
                      0, s, p);
@@ -709,12 +902,13 @@ hipError_t launch_select_clusters(const SelectParams& p, int Hkv, hipStream_t s)
 }
 
 size_t select_clusters_scratch_bytes(int M, int Hkv) {
-  return (size_t)Hkv * M * (2 * R * sizeof(__bf16) + sizeof(int32_t)) + kTablePad;
+  return (size_t)Hkv * M * (2 * R * sizeof(__bf16) + sizeof(int32_t)) + (size_t)Hkv * sizeof(uint32_t) + kTablePad;
 }
 
 hipError_t launch_select_block_reps(const SelectParams& p, int Hkv, int mode, hipStream_t s) {
   if (p.n_units == 0 || p.n_qb == 0) return hipSuccess;
   const dim3 prep((p.M * R + NT - 1) / NT, Hkv), grid((p.n_qb + kSelBlocks - 1) / kSelBlocks, p.n_units);
+  hipLaunchKernelGGL(sel_clear_kernel, dim3(1), dim3(kMaxHeads), 0, s, p.cnorm, Hkv);
   if (mode == 2) {
     hipLaunchKernelGGL(block_prep_kernel<2>, prep, dim3(NT), 0, s, p);
     hipLaunchKernelGGL(select_clusters_kernel<2>, grid, dim3(NT), 0, s, p);
@@ -727,7 +921,8 @@ hipError_t launch_select_block_reps(const SelectParams& p, int Hkv, int mode, hi
 
 size_t select_block_reps_scratch_bytes(int n_kb, int Hkv, int mode) {
   const size_t npart = mode == 2 ? 2 : 1;
-  return (size_t)Hkv * n_kb * (2 * R * npart * sizeof(__bf16) + sizeof(int32_t)) + kTablePad;
+  return (size_t)Hkv * n_kb * (2 * R * npart * sizeof(__bf16) + sizeof(int32_t)) + (size_t)Hkv * sizeof(uint32_t) +
+         kTablePad;
 }
 
 }  // namespace ha
