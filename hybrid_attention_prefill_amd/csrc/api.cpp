@@ -378,7 +378,8 @@ int run_select_blocks(const ha_layer_desc* d, const Heads& h, const float* qlow,
   sp.M = sp.n_qb;
   sp.c_hi = static_cast<__bf16*>(rep);
   sp.c_lo = sp.c_hi + nparts;
-  sp.first_mem = reinterpret_cast<int32_t*>(sp.c_lo + nparts);
+  sp.c_f16 = reinterpret_cast<_Float16*>(sp.c_lo + nparts);
+  sp.first_mem = reinterpret_cast<int32_t*>(sp.c_f16 + nparts);
   sp.cnorm = reinterpret_cast<uint32_t*>(sp.first_mem + (size_t)d->n_kv_heads * sp.M);
   return dev_status(launch_select_block_reps(sp, d->n_kv_heads, d->block_score, s));
 }
@@ -465,7 +466,8 @@ int run_select_clusters(const ha_layer_desc* d, const Heads& h, const float* qlo
   const size_t nparts = (size_t)d->n_kv_heads * d->n_clusters * kRank;
   sp.c_hi = static_cast<__bf16*>(scratch);
   sp.c_lo = sp.c_hi + nparts;
-  sp.first_mem = reinterpret_cast<int32_t*>(sp.c_lo + nparts);
+  sp.c_f16 = reinterpret_cast<_Float16*>(sp.c_lo + nparts);
+  sp.first_mem = reinterpret_cast<int32_t*>(sp.c_f16 + nparts);
   sp.cnorm = reinterpret_cast<uint32_t*>(sp.first_mem + (size_t)d->n_kv_heads * d->n_clusters);
   return dev_status(launch_select_clusters(sp, d->n_kv_heads, s));
 }

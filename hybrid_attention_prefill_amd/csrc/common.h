@@ -102,6 +102,7 @@ struct SelectParams {
   int32_t* sel;        // [Hret, n_qb, topk]
   __bf16* c_hi;        // scratch: [Hkv, M, parts * r] split centroids / block representatives
   __bf16* c_lo;
+  _Float16* c_f16;     // scratch: (hi + lo) times the KV head's power-of-two scale, in fp16
   int32_t* first_mem;  // [Hkv, M] smallest member position (INT_MAX if empty or not a candidate)
   uint32_t* cnorm;     // [Hkv] largest candidate-vector norm (fp32 bits), for the scoring error bound
   const int8_t* kcodes;  // 8-bit indexer keys [Hkv, N, r] (nullptr: fp32 klow)

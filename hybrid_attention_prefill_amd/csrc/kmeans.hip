@@ -419,6 +419,28 @@ __global__ __launch_bounds__(NT) void block_prep_kernel(SelectParams p) {
   cnorm_max(p.cnorm + g, n2);
 }
 
+// Power of two that brings a norm into [2^8, 2^9): the approximate pass
+// scores fp16 copies of the queries and the candidate table, scaled by it
+// (scaling by a power of two is exact and scales every score alike); norms
+// outside [2^-60, 2^60] are not scaled and take the exact pass instead.
+__device__ __forceinline__ float norm_scale(float nrm) {
+  const int e = (int)((__float_as_uint(nrm) >> 23) & 0xFFu) - 127;
+  return __uint_as_float((uint32_t)(min(127, max(-126, 8 - e)) + 127) << 23);
+}
+__device__ __forceinline__ bool norm_in_range(float nrm) { return nrm >= 0x1p-60f && nrm <= 0x1p60f; }
+
+// Per layer, once, after the prep kernels: the candidate table (hi + lo, the
+// value the exact products see) times the KV head's norm_scale, in fp16.
+template <int NPART>
+__global__ __launch_bounds__(NT) void table_f16_kernel(SelectParams p) {
+  const int g = blockIdx.y;
+  const size_t x = (size_t)blockIdx.x * NT + threadIdx.x, n = (size_t)p.M * R * NPART;
+  if (x >= n) return;
+  const float sc = norm_scale(__uint_as_float(p.cnorm[g]));
+  const size_t o = (size_t)g * n + x;
+  p.c_f16[o] = (_Float16)(((float)p.c_hi[o] + (float)p.c_lo[o]) * sc);
+}
+
 // One workgroup per (retrieval head, query block).  S[i][m] = qlow_i . C_m on
 // MFMA (32 rows x 32 centroids per instruction, k = r = 16); a lane ends with
 // 16 rows of one centroid, so the row max is a lane-local reduction plus one
@@ -430,16 +452,20 @@ __global__ __launch_bounds__(NT) void block_prep_kernel(SelectParams p) {
 // passes ql.ch + qh.cl + qh.ch, fp32-accurate; the order key of the row max
 // ranks the clusters (larger first, lower index first among equal keys).
 // They are computed only where they decide something:
-//   1. approximate pass: one product qh.ch per (row, cluster) gives an
-//      approximate row max a_m for every cluster (-inf when ineligible) in
-//      LDS; each of the 128 scoring lanes keeps the largest it wrote.
-//   2. error bound: qh.ch differs from the three-pass score by qh.cl + ql.ch
-//      plus accumulation rounding, at most
-//        eps = 1.03 * 2^-7 * max_i |q_i| * max_m |C_m|   (+ a denormal floor)
-//      (|cl| <= 2^-8 |C|, |ql| <= 2^-8 |q| per component; Cauchy-Schwarz
-//      over the r components; the 3% covers the norms' own rounding and the
-//      fp32 accumulation of up to 48 products).  The row max moves by at most
-//      eps as well.
+//   1. approximate pass: one fp16 product per (row, cluster), on copies of
+//      the query rows and of the table scaled by powers of two (norm_scale of
+//      the largest row norm over the unit's slots, and of the largest table
+//      norm), gives a scaled approximate row max a_m for every cluster (-inf
+//      when ineligible) in LDS; each of the 128 scoring lanes keeps the
+//      largest it wrote.
+//   2. error bound, in the scaled units: with Q = max_i |q_i| and
+//      C = max_m |C_m| after scaling (both in [2^8, 2^9)),
+//        eps = 1.1 * 2^-10 * Q * C + 2^-10 (Q + C) + 2^-20 + a denormal floor
+//      bounds |a_m - three-pass score| (fp16 rounding of both operands,
+//      2^-11 relative each, against the three-pass products' own 2^-15
+//      from the dropped lo*lo terms, Cauchy-Schwarz over the components,
+//      fp32 accumulation of up to 48 products; the absolute terms cover fp16
+//      subnormals).  The row max moves by at most eps as well.
 //   3. prefilter: tau = the topk-th largest lane maximum.  At least topk
 //      eligible clusters have a >= tau, hence exact score >= tau - eps, so
 //      the k-th exact score is >= tau - eps and every cluster of the exact
@@ -475,7 +501,7 @@ constexpr int kSelBlocks = 1;
 constexpr size_t kTablePad = 4096;
 constexpr int kGroups = 128;      // scoring lanes (4 waves x 32)
 constexpr int kCapW = 192;        // candidate slots per wave
-constexpr float kEpsRel = 1.03f * 0x1p-7f;
+constexpr float kEpsRel = 1.1f * 0x1p-10f;
 
 template <int NPART>
 __global__ __launch_bounds__(NT, 2) void select_clusters_kernel(SelectParams p) {
@@ -500,8 +526,6 @@ __global__ __launch_bounds__(NT, 2) void select_clusters_kernel(SelectParams p) 
   const int b0 = blockIdx.x * kSelBlocks;
   const int nb = min(kSelBlocks, p.n_qb - b0);
   if (p.topk == 0) return;
-  // the approximate pass pays off when the prefilter applies (k <= kGroups)
-  const bool approx = p.topk <= kGroups;
 
   int nrow[kSelBlocks], lim[kSelBlocks];
 #pragma unroll
@@ -510,37 +534,64 @@ __global__ __launch_bounds__(NT, 2) void select_clusters_kernel(SelectParams p) 
     nrow[bi] = bi < nb ? min(kBlock, p.N - qs0) : 0;
     lim[bi] = bi < nb ? qs0 + nrow[bi] - 1 - p.window : -1;
   }
-  // split query rows of slot t (parts as above); rows past the end of a
-  // ragged last block repeat the block's first row, so the row max needs no
-  // mask.  qn2 tracks the largest squared row norm seen (the lane's rows).
-  dev::bf16x8 qh[NPART][2], ql[NPART][2];
-  float qn2 = 0.f;
-  bool qbad = false;                // a row norm that is not finite
-  auto load_q = [&](int t) {
+  // query rows of slot t: lane (lr, lh) holds dimensions lh*8 .. lh*8+7 of
+  // rows lr and 32 + lr; rows past the end of a ragged last block repeat the
+  // block's first row, so the row max needs no mask
+  auto load_rows = [&](int t, float (&v)[2][8]) {
     const int qs0 = b0 * kBlock;
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
       const int i = rt * 32 + lr;
       const int row = nb > 0 ? qs0 + (i < nrow[0] ? i : 0) : 0;
       const float* qp = p.qlow + ((size_t)t * p.N + row) * R + lh * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[rt][e] = qp[e];
+    }
+  };
+  // largest squared row norm over the unit's slots (every lane ends with
+  // the block's value; all waves compute the same), and whether some row
+  // norm is not finite
+  float qn2 = 0.f;
+  bool qbad = false;
+  for (int s = 0; s < ns; ++s) {
+    float v[2][8];
+    load_rows(t0 + s, v);
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
       float ss = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float v = qp[e];
-        ss = fmaf(v, v, ss);
-#pragma unroll
-        for (int part = 0; part < NPART; ++part) {
-          const float vp = NPART == 1 ? v : (part == 0 ? fmaxf(v, 0.f) : fminf(v, 0.f));
-          __bf16 hh, ll;
-          dev::split2(vp, hh, ll);
-          qh[part][rt][e] = hh;
-          ql[part][rt][e] = ll;
-        }
-      }
+      for (int e = 0; e < 8; ++e) ss = fmaf(v[rt][e], v[rt][e], ss);
       const float rn2 = dev::pair32_sum(ss);
       qbad |= !(rn2 <= __FLT_MAX__);
       qn2 = fmaxf(qn2, rn2);
     }
+  }
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) qn2 = fmaxf(qn2, __shfl_xor(qn2, o));
+  const float qn = sqrtf(qn2), cn = __uint_as_float(p.cnorm[g]);
+  const bool approx = p.topk <= kGroups && !__any(qbad) && norm_in_range(qn) && norm_in_range(cn);
+  const float sq = norm_scale(qn);
+  // the split rows (parts as above) and, for the approximate pass, their
+  // scaled fp16 copies
+  dev::bf16x8 qh[NPART][2], ql[NPART][2];
+  dev::f16x8 qf[NPART][2];
+  auto load_q = [&](int t) {
+    float v[2][8];
+    load_rows(t, v);
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int part = 0; part < NPART; ++part) {
+          const float x = v[rt][e];
+          const float vp = NPART == 1 ? x : (part == 0 ? fmaxf(x, 0.f) : fminf(x, 0.f));
+          __bf16 hh, ll;
+          dev::split2(vp, hh, ll);
+          qh[part][rt][e] = hh;
+          ql[part][rt][e] = ll;
+          qf[part][rt][e] = (_Float16)(vp * sq);
+        }
   };
   const __bf16* chi = p.c_hi + (size_t)g * p.M * R * NPART;
   const __bf16* clo = p.c_lo + (size_t)g * p.M * R * NPART;
@@ -559,6 +610,8 @@ __global__ __launch_bounds__(NT, 2) void select_clusters_kernel(SelectParams p) 
       const_cast<__bf16*>(chi), 0, p.M * NPART * R * 2, dev::kBufWord3);
   const __amdgpu_buffer_rsrc_t rs_lo = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<__bf16*>(clo), 0, p.M * NPART * R * 2, dev::kBufWord3);
+  const __amdgpu_buffer_rsrc_t rs_f16 = __builtin_amdgcn_make_buffer_rsrc(
+      p.c_f16 + (size_t)g * p.M * R * NPART, 0, p.M * NPART * R * 2, dev::kBufWord3);
   const __amdgpu_buffer_rsrc_t rs_fm = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int32_t*>(fm), 0, p.M * 4, dev::kBufWord3);
   const int lim0 = lim[0];
@@ -578,9 +631,13 @@ __global__ __launch_bounds__(NT, 2) void select_clusters_kernel(SelectParams p) 
       for (int part = 0; part < NPART; ++part) {
         const int vo = (lr * NPART + part) * R * 2 + lh * 16;
         const int so = x * 32 * NPART * R * 2;
-        bh[part] = __builtin_bit_cast(dev::bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs_hi, vo, so, 0));
-        if constexpr (kExact)
+        if constexpr (kExact) {
+          bh[part] = __builtin_bit_cast(dev::bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs_hi, vo, so, 0));
           bl[part] = __builtin_bit_cast(dev::bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs_lo, vo, so, 0));
+        } else {
+          // the fp16 copy, carried in the hi slot's registers
+          bh[part] = __builtin_bit_cast(dev::bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs_f16, vo, so, 0));
+        }
       }
       f = (int)__builtin_amdgcn_raw_buffer_load_b32(rs_fm, lr * 4, x * 32 * 4, 0);
     };
@@ -655,8 +712,14 @@ __global__ __launch_bounds__(NT, 2) void select_clusters_kernel(SelectParams p) 
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt) acc[rt] = dev::mfma32(qh[part][rt], rbl[u][part], acc[rt]);
               }
+              if constexpr (kExact) {
 #pragma unroll
-              for (int rt = 0; rt < 2; ++rt) acc[rt] = dev::mfma32(qh[part][rt], rbh[u][part], acc[rt]);
+                for (int rt = 0; rt < 2; ++rt) acc[rt] = dev::mfma32(qh[part][rt], rbh[u][part], acc[rt]);
+              } else {
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
+                  acc[rt] = dev::mfma32_f16(qf[part][rt], __builtin_bit_cast(dev::f16x8, rbh[u][part]), acc[rt]);
+              }
             }
             // eligibility of the slot's cluster, taken before the slot's refill
             // is issued (the empty asm orders the two), so the refill lands in
@@ -727,9 +790,6 @@ __global__ __launch_bounds__(NT, 2) void select_clusters_kernel(SelectParams p) 
   }
   scan(std::integral_constant<bool, false>{});
   if (lh == 0) gmax[wave * 32 + lr] = dev::order_key(gmxf);
-  // largest row norm over the unit's slots (every wave holds all rows)
-#pragma unroll
-  for (int o = 16; o >= 1; o >>= 1) qn2 = fmaxf(qn2, __shfl_xor(qn2, o));
   __syncthreads();
   // tau = the topk-th largest lane maximum: the largest T with at least topk
   // maxima >= T, found bit by bit from the top with wave ballots
@@ -747,9 +807,10 @@ __global__ __launch_bounds__(NT, 2) void select_clusters_kernel(SelectParams p) 
   // candidate threshold; -FLT_MAX (every eligible cluster) when fewer than
   // topk lane maxima are finite
   const float tv = dev::key_value(tau_s);
-  const float qn = sqrtf(qn2), cn = __uint_as_float(p.cnorm[g]);
-  const float eps = kEpsRel * qn * cn + 0x1p-120f * (8.f * (qn + cn) + 1.f);
-  const bool bound_ok = eps < 1e36f && !(tv > 1e36f) && !(tv != tv) && !__any(qbad);
+  const float sc = norm_scale(cn), qs = qn * sq, cs = cn * sc;
+  const float eps = kEpsRel * qs * cs + 0x1p-10f * (qs + cs) + 0x1p-20f +
+                    0x1p-120f * sq * sc * (8.f * (qn + cn) + 1.f);
+  const bool bound_ok = eps < 1e36f && !(tv > 1e36f) && !(tv != tv);
   const float thr = tv >= -1e36f ? fmaxf(tv - 2.f * eps, -__FLT_MAX__) : -__FLT_MAX__;
   // collect: all of the wave's values first (latency), then in index order
   const int per = ((p.M + 4 * 64 - 1) / (4 * 64)) * 64;
@@ -799,53 +860,72 @@ __global__ __launch_bounds__(NT, 2) void select_clusters_kernel(SelectParams p) 
   // exact keys of the wave's candidates, 32 at a time: lane (lr, lh) loads
   // candidate lr's parts for dimensions lh*8 .. lh*8+7, as in the scan;
   // packed keys go to pk[base + pos] (index order across the waves)
+  // (every tile's operands are loaded before the first product: the rows
+  // are gathered from L2, and their latency would otherwise add up per tile)
   uint64_t* pk = reinterpret_cast<uint64_t*>(keys);
+  constexpr int kMaxCT = kCapW / 32;
   const int n_ct = (cnt + 31) / 32;
-  for (int s = 0; s < ns; ++s) {
-    if (ns > 1) load_q(t0 + s);
-    for (int x = 0; x < n_ct; ++x) {
-      const int pos = x * 32 + lr;
-      const bool valid = pos < cnt;
-      const int m = valid ? (int)ci[pos] : 0;
-      dev::f32x16 acc[2] = {dev::f32x16{}, dev::f32x16{}};
+  dev::bf16x8 cbh[kMaxCT][NPART], cbl[kMaxCT][NPART];
+  int cm[kMaxCT];
+#pragma unroll
+  for (int x = 0; x < kMaxCT; ++x) {
+    const int pos = x * 32 + lr;
+    cm[x] = pos < cnt ? (int)ci[pos] : 0;
+    if (x < n_ct) {
 #pragma unroll
       for (int part = 0; part < NPART; ++part) {
-        const int vo = (m * NPART + part) * R * 2 + lh * 16;
-        const dev::bf16x8 bh = __builtin_bit_cast(dev::bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs_hi, vo, 0, 0));
-        const dev::bf16x8 bl = __builtin_bit_cast(dev::bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs_lo, vo, 0, 0));
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) acc[rt] = dev::mfma32(ql[part][rt], bh, acc[rt]);
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) acc[rt] = dev::mfma32(qh[part][rt], bl, acc[rt]);
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) acc[rt] = dev::mfma32(qh[part][rt], bh, acc[rt]);
+        const int vo = (cm[x] * NPART + part) * R * 2 + lh * 16;
+        cbh[x][part] = __builtin_bit_cast(dev::bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs_hi, vo, 0, 0));
+        cbl[x][part] = __builtin_bit_cast(dev::bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs_lo, vo, 0, 0));
       }
-      float mx = -__builtin_inff();
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[rt][e]);
-      mx = dev::pair32_max(mx);
-      const uint64_t kk = ((uint64_t)dev::order_key(mx) << 32) | (uint32_t)(0xFFFF - m);
-      if (valid && lh == 0) pk[base + pos] = s == 0 ? kk : max(pk[base + pos], kk);
     }
   }
-  if (tid == 0) pk[n] = 0ull;         // pads the pairwise reads below; ranks below every key
+  for (int s = 0; s < ns; ++s) {
+    if (ns > 1) load_q(t0 + s);
+#pragma unroll
+    for (int x = 0; x < kMaxCT; ++x) {
+      if (x < n_ct) {
+        const int pos = x * 32 + lr;
+        dev::f32x16 acc[2] = {dev::f32x16{}, dev::f32x16{}};
+#pragma unroll
+        for (int part = 0; part < NPART; ++part) {
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt) acc[rt] = dev::mfma32(ql[part][rt], cbh[x][part], acc[rt]);
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt) acc[rt] = dev::mfma32(qh[part][rt], cbl[x][part], acc[rt]);
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt) acc[rt] = dev::mfma32(qh[part][rt], cbh[x][part], acc[rt]);
+        }
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[rt][e]);
+        mx = dev::pair32_max(mx);
+        const uint64_t kk = ((uint64_t)dev::order_key(mx) << 32) | (uint32_t)(0xFFFF - cm[x]);
+        if (pos < cnt && lh == 0) pk[base + pos] = s == 0 ? kk : max(pk[base + pos], kk);
+      }
+    }
+  }
+  // pads the reads below to whole groups of kRankU; ranks below every key
+  constexpr int kRankU = 16;
+  if (tid < kRankU) pk[n + tid] = 0ull;
   __syncthreads();
   // rank = number of packed keys above one's own (all distinct); chosen when
-  // rank < k, so exactly k are chosen.  Candidate t and t + NT per thread.
+  // rank < k, so exactly k are chosen.  Candidate t and t + NT per thread;
+  // kRankU broadcast reads in flight per step.
   const uint64_t ka = tid < n ? pk[tid] : 0ull, kb = tid + NT < n ? pk[tid + NT] : 0ull;
   int ra = 0, rb = 0;
-  if (n > NT) {
-    for (int j = 0; j < n; j += 2) {
-      const uint64_t u0 = pk[j], u1 = pk[j + 1];
-      ra += (int)(u0 > ka) + (int)(u1 > ka);
-      rb += (int)(u0 > kb) + (int)(u1 > kb);
-    }
-  } else {
-    for (int j = 0; j < n; j += 2) {
-      const uint64_t u0 = pk[j], u1 = pk[j + 1];
-      ra += (int)(u0 > ka) + (int)(u1 > ka);
+  const bool two = n > NT;
+  for (int j = 0; j < n; j += kRankU) {
+    uint64_t u[kRankU];
+#pragma unroll
+    for (int e = 0; e < kRankU; ++e) u[e] = pk[j + e];
+#pragma unroll
+    for (int e = 0; e < kRankU; ++e) ra += (int)(u[e] > ka);
+    if (two) {
+#pragma unroll
+      for (int e = 0; e < kRankU; ++e) rb += (int)(u[e] > kb);
     }
   }
   const bool ca = tid < n && ra < k, cb = tid + NT < n && rb < k;
@@ -896,13 +976,14 @@ hipError_t launch_select_clusters(const SelectParams& p, int Hkv, hipStream_t s)
   if (p.n_ret == 0 || p.n_qb == 0) return hipSuccess;
   hipLaunchKernelGGL(sel_clear_kernel, dim3(1), dim3(kMaxHeads), 0, s, p.cnorm, Hkv);
   hipLaunchKernelGGL(cluster_prep_kernel, dim3((p.M + NT - 1) / NT, Hkv), dim3(NT), 0, s, p);
+  hipLaunchKernelGGL(table_f16_kernel<1>, dim3((p.M * R + NT - 1) / NT, Hkv), dim3(NT), 0, s, p);
   hipLaunchKernelGGL(select_clusters_kernel<1>, dim3((p.n_qb + kSelBlocks - 1) / kSelBlocks, p.n_units), dim3(NT),
                      0, s, p);
   return hipGetLastError();
 }
 
 size_t select_clusters_scratch_bytes(int M, int Hkv) {
-  return (size_t)Hkv * M * (2 * R * sizeof(__bf16) + sizeof(int32_t)) + (size_t)Hkv * sizeof(uint32_t) + kTablePad;
+  return (size_t)Hkv * M * (3 * R * sizeof(__bf16) + sizeof(int32_t)) + (size_t)Hkv * sizeof(uint32_t) + kTablePad;
 }
 
 hipError_t launch_select_block_reps(const SelectParams& p, int Hkv, int mode, hipStream_t s) {
@@ -911,9 +992,11 @@ hipError_t launch_select_block_reps(const SelectParams& p, int Hkv, int mode, hi
   hipLaunchKernelGGL(sel_clear_kernel, dim3(1), dim3(kMaxHeads), 0, s, p.cnorm, Hkv);
   if (mode == 2) {
     hipLaunchKernelGGL(block_prep_kernel<2>, prep, dim3(NT), 0, s, p);
+    hipLaunchKernelGGL(table_f16_kernel<2>, dim3((p.M * R * 2 + NT - 1) / NT, Hkv), dim3(NT), 0, s, p);
     hipLaunchKernelGGL(select_clusters_kernel<2>, grid, dim3(NT), 0, s, p);
   } else {
     hipLaunchKernelGGL(block_prep_kernel<1>, prep, dim3(NT), 0, s, p);
+    hipLaunchKernelGGL(table_f16_kernel<1>, dim3((p.M * R + NT - 1) / NT, Hkv), dim3(NT), 0, s, p);
     hipLaunchKernelGGL(select_clusters_kernel<1>, grid, dim3(NT), 0, s, p);
   }
   return hipGetLastError();
@@ -921,7 +1004,7 @@ hipError_t launch_select_block_reps(const SelectParams& p, int Hkv, int mode, hi
 
 size_t select_block_reps_scratch_bytes(int n_kb, int Hkv, int mode) {
   const size_t npart = mode == 2 ? 2 : 1;
-  return (size_t)Hkv * n_kb * (2 * R * npart * sizeof(__bf16) + sizeof(int32_t)) + (size_t)Hkv * sizeof(uint32_t) +
+  return (size_t)Hkv * n_kb * (3 * R * npart * sizeof(__bf16) + sizeof(int32_t)) + (size_t)Hkv * sizeof(uint32_t) +
          kTablePad;
 }
 
