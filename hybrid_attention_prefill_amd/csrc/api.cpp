@@ -441,6 +441,10 @@ int run_kmeans(const ha_layer_desc* d, const float* klow, float* cent, int32_t* 
   kp.c_hi = reinterpret_cast<_Float16*>(align_up(reinterpret_cast<uintptr_t>(kp.c_norm + Hkv * M)));
   kp.c_lo = kp.c_hi + Hkv * M * kRank;
   kp.amax = reinterpret_cast<uint32_t*>(kp.c_lo + Hkv * M * kRank);
+  kp.cmax = kp.amax + Hkv;
+  kp.almax = kp.cmax + Hkv;
+  kp.n_amb = kp.almax + Hkv;
+  kp.amb = reinterpret_cast<int32_t*>(align_up(reinterpret_cast<uintptr_t>(kp.n_amb + Hkv)));
   return dev_status(launch_kmeans(kp, d->n_kv_heads, d->kmeans_iters, s));
 }
 

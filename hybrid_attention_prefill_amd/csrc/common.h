@@ -135,6 +135,10 @@ struct KmeansParams {
   _Float16* c_lo;
   float* c_norm;       // scratch [Hkv, M]
   uint32_t* amax;      // scratch [Hkv]: largest |klow| component per KV head (fp32 bits)
+  uint32_t* cmax;      // scratch [Hkv]: largest scaled squared centroid norm of the iteration (fp32 bits)
+  uint32_t* almax;     // scratch [Hkv]: largest squared norm of the centroids' fp16 lo parts (fp32 bits)
+  uint32_t* n_amb;     // scratch [Hkv]: keys the approximate assignment left undecided
+  int32_t* amb;        // scratch [Hkv, N]: their positions
   int N, M, stride, n_chunks;
 };
 size_t kmeans_scratch_bytes(int N, int M, int Hkv);

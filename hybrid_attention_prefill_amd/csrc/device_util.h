@@ -9,6 +9,8 @@ namespace dev {
 constexpr int kNT = 256;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -37,6 +39,12 @@ __device__ __forceinline__ void split3(float x, __bf16& hi, __bf16& mid, __bf16&
 // equal, permlane32_swap returns (v[l % 32], v[32 + l % 32]) in lane l and
 // permlane16_swap returns (v[l & ~16], v[l | 16]), so both lanes of a pair
 // combine the same two values in the same order.
+// The value lane l ^ 32 holds: the swap returns the pair's two values, and
+// one of them is this lane's own.
+__device__ __forceinline__ uint32_t pair32_other(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return r[0] ^ r[1] ^ v;
+}
 __device__ __forceinline__ float pair32_max(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));

@@ -10,7 +10,10 @@
 //
 // Every step is deterministic, so a run of t iterations reproduces the state
 // after t iterations of a longer run:
-//   assign   one lane per key, centroid tiles in LDS, d = |C|^2 - 2 k.C on MFMA
+//   assign   one lane per key, centroid tiles in LDS, d = |C|^2 - 2 k.C on MFMA:
+//            one fp16 product pass decides every key whose two best
+//            distances lie further apart than the pass's error bound; the
+//            others get the exact three-product pass
 //   CSR      stable counting sort of key positions by cluster: per-chunk
 //            histograms, a column scan, then an in-order scatter (ranks among
 //            equal clusters inside a 256-key batch come from an LDS scan)
@@ -73,24 +76,51 @@ __device__ __forceinline__ float key_scale(uint32_t amax_bits) {
 
 // Per iteration: centroids (times the KV head's key scale) split into two
 // fp16 parts and their squared norms, for the MFMA distance pass.
+// The largest scaled squared norm goes to cmax and the largest squared norm
+// of the lo parts to almax (wave maxima, one atomic per wave; both start at
+// zero, km_clear_kernel).
 __global__ __launch_bounds__(NT) void km_prep_kernel(KmeansParams p) {
   const int g = blockIdx.y;
   const int m = blockIdx.x * NT + threadIdx.x;
-  if (m >= p.M) return;
-  const float sc = key_scale(p.amax[g]);
-  const size_t o = ((size_t)g * p.M + m) * R;
-  const float* c = p.cent + o;
-  float nrm = 0.f;
+  float nrm = 0.f, lnrm = 0.f;
+  if (m < p.M) {
+    const float sc = key_scale(p.amax[g]);
+    const size_t o = ((size_t)g * p.M + m) * R;
+    const float* c = p.cent + o;
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const float v = c[r] * sc;
-    nrm = fmaf(v, v, nrm);
-    dev::split2_f16(v, p.c_hi[o + r], p.c_lo[o + r]);
+    for (int r = 0; r < R; ++r) {
+      const float v = c[r] * sc;
+      nrm = fmaf(v, v, nrm);
+      _Float16 h, l;
+      dev::split2_f16(v, h, l);
+      p.c_hi[o + r] = h;
+      p.c_lo[o + r] = l;
+      lnrm = fmaf((float)l, (float)l, lnrm);
+    }
+    p.c_norm[(size_t)g * p.M + m] = nrm;
   }
-  p.c_norm[(size_t)g * p.M + m] = nrm;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    nrm = fmaxf(nrm, __shfl_xor(nrm, o));
+    lnrm = fmaxf(lnrm, __shfl_xor(lnrm, o));
+  }
+  if ((threadIdx.x & 63) == 0) {
+    atomicMax(&p.cmax[g], __float_as_uint(nrm));
+    atomicMax(&p.almax[g], __float_as_uint(lnrm));
+  }
 }
 
-// Assignment: each wave owns 32*KT keys (KT column blocks of 32), the
+// Per iteration, before km_prep: the per-head maximum and the count of
+// undecided keys start at zero.
+__global__ void km_clear_kernel(KmeansParams p, int Hkv) {
+  if ((int)threadIdx.x < Hkv) {
+    p.cmax[threadIdx.x] = 0u;
+    p.almax[threadIdx.x] = 0u;
+    p.n_amb[threadIdx.x] = 0u;
+  }
+}
+
+// Exact assignment: each wave owns 32*KT keys (KT column blocks of 32), the
 // workgroup 4 waves.  Centroids are staged in LDS 256 at a time: the two fp16
 // parts of C_m as 16-bit rows, and |C_m|^2 in fp32.  For every tile of 32
 // centroids and key block, one chain of three MFMAs gives
@@ -112,18 +142,25 @@ constexpr int kCStr = 24;         // 16-bit row stride of a staged part (48 B: c
 constexpr int KT = 4;             // 32-key blocks per wave
 constexpr float kPadNorm = 1e30f; // norm of the padding rows of a partial tile
 
-__global__ __launch_bounds__(NT) void km_assign_kernel(KmeansParams p) {
+// It assigns the keys the approximate pass (km_assign_approx_kernel) left
+// undecided, p.amb[g][0 .. p.n_amb[g]); workgroups past the count exit at
+// once.
+__global__ __launch_bounds__(NT) void km_assign_exact_kernel(KmeansParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t cs[2][kCChunk * kCStr];
   __shared__ __attribute__((aligned(16))) float cns[kCChunk];   // |C_m|^2 of the staged centroids
   const int g = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, lr = lane & 31, lh = lane >> 5;
+  const int n_keys = (int)p.n_amb[g];
+  if ((int)blockIdx.x * 4 * 32 * KT >= n_keys) return;
   const int j0 = (blockIdx.x * 4 + wave) * (32 * KT);
   const float ksc = -2.f * key_scale(p.amax[g]);
+  // key of slot i (slots past the count repeat the last key and write nothing)
+  auto key_of = [&](int i) { return (int)p.amb[(size_t)g * p.N + min(n_keys - 1, i)]; };
   dev::f16x8 kh[KT], kl[KT];
 #pragma unroll
   for (int kt = 0; kt < KT; ++kt) {
-    const int j = min(p.N - 1, j0 + kt * 32 + lr);
+    const int j = key_of(j0 + kt * 32 + lr);
     const float* kp = p.klow + ((size_t)g * p.N + j) * R + lh * 8;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -216,8 +253,180 @@ __global__ __launch_bounds__(NT) void km_assign_kernel(KmeansParams p) {
     const float ob = __shfl_xor(best[kt], 32);
     const int oa = __shfl_xor(arg[kt], 32);
     if (ob < best[kt] || (ob == best[kt] && oa < arg[kt])) arg[kt] = oa;
+    const int i = j0 + kt * 32 + lr;
+    if (lh == 0 && i < n_keys) p.assign[(size_t)g * p.N + key_of(i)] = arg[kt];
+  }
+}
+
+// Approximate assignment with certification; the exact kernel above defines
+// the result.  One fp16 product per (key, centroid), ah * kh, gives
+//   d~ = |C'|^2 + k' . C'      (C' = s C, k' = -2 s k, s the key scale)
+// within eps of the three-product value the exact kernel compares, where
+//   eps = 1.002 (max|al| |k'| + max|C'| |kl|) + 2^-17 (max|C'|^2 + |k'| max|C'|)
+//         + 2^-10 (|k'| + max|C'|)
+// (al, kl: the lo parts the exact kernel uses; by Cauchy-Schwarz the dropped
+// al . kh + ah . kl are at most |al| |kh| + |ah| |kl|, and |kh| <= |k'|
+// (1 + 2^-11), |ah| <= |C'| (1 + 2^-11); fp32 accumulation of up to 64
+// terms plus the recompute below, 2^-17 of the magnitudes; fp16 subnormals
+// and flushes cost at most 2^-14 per component, under the last term).  Per key and lane
+// half the pass keeps the smallest d~ (b1, in tile x1) and the second
+// smallest tile minimum (b2: med3 of b1, b2 and the tile's minimum).  Then
+// the lane recomputes its 16 values of tile x1 with fp32 dot products of the
+// same fp16 operands (only the accumulation order differs) for the index of
+// b1 (lowest on equal values) and the tile's second smallest value w2.  The
+// halves merge; when the second smallest over all centroids exceeds b1 by
+// more than 2 eps, the best centroid under the exact distances is that one,
+// alone, and is written.  Otherwise the key is appended to p.amb for the
+// exact kernel (the list order varies; each key's result does not).
+//
+// The accumulator seed |C'_m|^2 comes from one more MFMA instead of 16 LDS
+// floats per lane: the norm split into three bf16 parts (exact: 24 bits) in
+// row m, k = 0..2 of a bf16 operand, times a column of ones, summed exactly
+// in fp32, so the seed is the fp32 norm itself.
+__global__ __launch_bounds__(NT, 4) void km_assign_approx_kernel(KmeansParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t cs[kCChunk * kCStr];
+  __shared__ __attribute__((aligned(16))) uint16_t cs3[kCChunk * kCStr];   // norm parts, then zeros
+  const int g = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, lr = lane & 31, lh = lane >> 5;
+  const int j0 = (blockIdx.x * 4 + wave) * (32 * KT);
+  const float ksc = -2.f * key_scale(p.amax[g]);
+  // per key: the fp16 key and the certification bound eps (both lane halves)
+  const float cmx = sqrtf(__uint_as_float(p.cmax[g])), alx = sqrtf(__uint_as_float(p.almax[g]));
+  dev::f16x8 kh[KT];
+  float eps[KT];
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+    const int j = min(p.N - 1, j0 + kt * 32 + lr);
+    const float* kp = p.klow + ((size_t)g * p.N + j) * R + lh * 8;
+    float ss = 0.f, sl = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = ksc * kp[e];
+      ss = fmaf(v, v, ss);
+      _Float16 h, l;
+      dev::split2_f16(v, h, l);
+      kh[kt][e] = h;
+      sl = fmaf((float)l, (float)l, sl);
+    }
+    const float kn = sqrtf(dev::pair32_sum(ss)), kln = sqrtf(dev::pair32_sum(sl));
+    eps[kt] = 1.002f * (alx * kn + cmx * kln) + 0x1p-17f * (cmx * cmx + kn * cmx) + 0x1p-10f * (kn + cmx);
+  }
+  const __bf16 one = (__bf16)1.f, zero = (__bf16)0.f;
+  const dev::bf16x8 ones3 = {one, one, one, zero, zero, zero, zero, zero};
+  float b1[KT], b2[KT];
+  int x1[KT];
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+    b1[kt] = __builtin_inff();
+    b2[kt] = __builtin_inff();
+    x1[kt] = 0;
+  }
+  const _Float16* chi = p.c_hi + (size_t)g * p.M * R;
+  const float* cn = p.c_norm + (size_t)g * p.M;
+  for (int c0 = 0; c0 < p.M; c0 += kCChunk) {
+    const int nc = min(kCChunk, p.M - c0);
+    __syncthreads();
+    {
+      // thread t stages centroid c0 + t: its hi part and its norm
+      const int m = c0 + tid;
+      const bool ok = tid < nc;
+      const uint4* src = reinterpret_cast<const uint4*>(chi + (size_t)(ok ? m : c0) * R);
+      const uint4 v0 = src[0], v1 = src[1];
+      uint4* dst = reinterpret_cast<uint4*>(&cs[tid * kCStr]);
+      dst[0] = v0;
+      dst[1] = v1;
+      __bf16 nh, nm, nl;
+      dev::split3(ok ? cn[m] : kPadNorm, nh, nm, nl);
+      const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, nh) | ((uint32_t)__builtin_bit_cast(uint16_t, nm) << 16);
+      uint4* dn = reinterpret_cast<uint4*>(&cs3[tid * kCStr]);
+      dn[0] = make_uint4(w0, (uint32_t)__builtin_bit_cast(uint16_t, nl), 0u, 0u);
+      dn[1] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    __syncthreads();
+    const int n_tiles = (nc + 31) / 32;
+    for (int x = 0; x < n_tiles; ++x) {
+      const int r0 = x * 32;
+      const dev::f16x8 ah = *reinterpret_cast<const dev::f16x8*>(&cs[(r0 + lr) * kCStr + lh * 8]);
+      const dev::bf16x8 a3 = *reinterpret_cast<const dev::bf16x8*>(&cs3[(r0 + lr) * kCStr + lh * 8]);
+      const dev::f32x16 nv = dev::mfma32(a3, ones3, dev::f32x16{});
+      dev::f32x16 acc[KT];
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) acc[kt] = dev::mfma32_f16(ah, kh[kt], nv);
+      const int tile = (c0 + r0) >> 5;
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        float tm = __builtin_inff();
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) tm = __builtin_fminf(__builtin_fminf(tm, acc[kt][e]), acc[kt][e + 1]);
+        const bool lt = tm < b1[kt];
+        b2[kt] = __builtin_amdgcn_fmed3f(b1[kt], b2[kt], tm);
+        x1[kt] = lt ? tile : x1[kt];
+        b1[kt] = lt ? tm : b1[kt];
+      }
+      // the products first (separate accumulators), then their minima
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, KT + 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);
+    }
+  }
+  uint32_t* list = reinterpret_cast<uint32_t*>(p.amb) + (size_t)g * p.N;
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+    // the key's 16 components: this lane's 8 and the other half's
+    const auto kw = __builtin_bit_cast(dev::u32x4, kh[kt]);
+    dev::u32x4 ko;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ko[q] = dev::pair32_other(kw[q]);
+    const dev::u32x4 klo = lh ? ko : kw, khi = lh ? kw : ko;
+    // tile x1's 16 values of this lane, recomputed
+    float w1 = __builtin_inff(), w2 = __builtin_inff();
+    int i1 = 0;
+    const int mb = x1[kt] * 32 + lh * 4;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int m = mb + (e >> 2) * 8 + (e & 3);
+      if (m < p.M) {
+        const dev::u32x4* cp = reinterpret_cast<const dev::u32x4*>(chi + (size_t)m * R);
+        const dev::u32x4 c0v = cp[0], c1v = cp[1];
+        float d = cn[m];
+        // (vector elements are copied to scalars before the bit casts: a bit
+        // cast of an element access reads element 0 with this compiler)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t ca = c0v[q], cb = c1v[q], ka = klo[q], kb = khi[q];
+          d = __builtin_amdgcn_fdot2(__builtin_bit_cast(dev::f16x2, ca), __builtin_bit_cast(dev::f16x2, ka), d, false);
+          d = __builtin_amdgcn_fdot2(__builtin_bit_cast(dev::f16x2, cb), __builtin_bit_cast(dev::f16x2, kb), d, false);
+        }
+        if (d < w1) {
+          w2 = w1;
+          w1 = d;
+          i1 = m;
+        } else {
+          w2 = fminf(w2, d);
+        }
+      }
+    }
+    // merge the halves (lane lr and lr + 32 hold the same key)
+    const float sb1 = b1[kt], sb2 = fminf(b2[kt], w2);
+    const float ob1 = __uint_as_float(dev::pair32_other(__float_as_uint(sb1)));
+    const float ob2 = __uint_as_float(dev::pair32_other(__float_as_uint(sb2)));
+    const int oi1 = (int)dev::pair32_other((uint32_t)i1);
+    const float B1 = fminf(sb1, ob1), B2 = fminf(fmaxf(sb1, ob1), fminf(sb2, ob2));
+    const int I1 = (sb1 < ob1 || (sb1 == ob1 && i1 < oi1)) ? i1 : oi1;
+    const bool cert = B2 - B1 > 2.f * eps[kt];
     const int j = j0 + kt * 32 + lr;
-    if (lh == 0 && j < p.N) p.assign[(size_t)g * p.N + j] = arg[kt];
+    const bool mine = lh == 0 && j < p.N;
+    if (mine && cert) p.assign[(size_t)g * p.N + j] = I1;
+    // undecided keys: one atomic per wave, slots in lane order
+    const bool amb = mine && !cert;
+    const uint64_t bal = __ballot(amb);
+    if (bal != 0ull) {
+      uint32_t base = 0u;
+      if (lane == 0) base = atomicAdd(&p.n_amb[g], (uint32_t)__popcll(bal));
+      base = __shfl(base, 0);
+      if (amb) list[base + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull))] = (uint32_t)j;
+    }
   }
 }
 
@@ -950,7 +1159,8 @@ __global__ __launch_bounds__(NT, 2) void select_clusters_kernel(SelectParams p) 
 size_t kmeans_scratch_bytes(int N, int M, int Hkv) {
   const size_t n_chunks = (size_t)(N + kChunk - 1) / kChunk;
   return (size_t)Hkv * n_chunks * M * sizeof(int32_t) + (size_t)Hkv * M * sizeof(int32_t) +
-         (size_t)Hkv * M * (2 * R * sizeof(_Float16) + sizeof(float)) + (size_t)Hkv * sizeof(uint32_t) + 256;
+         (size_t)Hkv * M * (2 * R * sizeof(_Float16) + sizeof(float)) + 4 * (size_t)Hkv * sizeof(uint32_t) +
+         (size_t)Hkv * N * sizeof(int32_t) + 512;
 }
 
 hipError_t launch_kmeans(KmeansParams p, int Hkv, int iters, hipStream_t s) {
@@ -959,9 +1169,12 @@ hipError_t launch_kmeans(KmeansParams p, int Hkv, int iters, hipStream_t s) {
   const int amax_blocks = (int)std::min<size_t>(kAmaxBlocks, ((size_t)p.N * R / 4 + NT - 1) / NT);
   hipLaunchKernelGGL(km_amax_kernel, dim3(amax_blocks, Hkv), dim3(NT), 0, s, p);
   hipError_t e = hipGetLastError();
+  const dim3 assign_grid((p.N + 4 * 32 * KT - 1) / (4 * 32 * KT), Hkv);
   for (int it = 0; it < iters && e == hipSuccess; ++it) {
+    hipLaunchKernelGGL(km_clear_kernel, dim3(1), dim3(kMaxHeads), 0, s, p, Hkv);
     hipLaunchKernelGGL(km_prep_kernel, dim3((p.M + NT - 1) / NT, Hkv), dim3(NT), 0, s, p);
-    hipLaunchKernelGGL(km_assign_kernel, dim3((p.N + 4 * 32 * KT - 1) / (4 * 32 * KT), Hkv), dim3(NT), 0, s, p);
+    hipLaunchKernelGGL(km_assign_approx_kernel, assign_grid, dim3(NT), 0, s, p);
+    hipLaunchKernelGGL(km_assign_exact_kernel, assign_grid, dim3(NT), 0, s, p);
     hipLaunchKernelGGL(km_hist_kernel, dim3(p.n_chunks, Hkv), dim3(NT), 0, s, p);
     hipLaunchKernelGGL(km_colscan_kernel, dim3((p.M + NT - 1) / NT, Hkv), dim3(NT), 0, s, p);
     hipLaunchKernelGGL(km_offsets_kernel, dim3(Hkv), dim3(NT), 0, s, p);
