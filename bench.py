@@ -249,14 +249,16 @@ def stage_rooflines(w, stage_ms, work, window_ms=None):
                               "fp32-accurate contraction run as three bf16 MFMA passes over hi/lo splits, so the "
                               "peak is 2.5 PFLOP/s / 3")
         elif name == "kmeans":
-            out[name] = _roof("mfma", 32 * w.kmeans_iters * Hkv * N * w.n_clusters, sec, PEAK_SPLIT3_TFLOPS,
-                              "TFLOP/s", "2 r FLOP per (key, centroid) pair per Lloyd iteration; an fp32-accurate "
-                              "contraction run as three fp16 MFMA passes (peak 2.5 PFLOP/s / 3); the update is "
-                              "HBM / integer work")
+            out[name] = _roof("mfma", 32 * w.kmeans_iters * Hkv * N * w.n_clusters, sec, PEAK_BF16_TFLOPS,
+                              "TFLOP/s", "2 r FLOP per (key, centroid) pair per Lloyd iteration; one fp16 MFMA pass "
+                              "decides every key whose two best distances lie further apart than its error bound "
+                              "(peak 2.5 PFLOP/s), the undecided keys (~15% at 1M) take the three-pass split "
+                              "products; the update is HBM / integer work")
         elif name == "select_clusters":
             out[name] = _roof("mfma", 32 * Hret * N * w.n_clusters, sec, PEAK_BF16_TFLOPS, "TFLOP/s",
-                              "2 r FLOP per (query row, centroid) pair, one bf16 MFMA pass (peak 2.5 PFLOP/s); "
-                              "the few candidates near the k-th score are re-scored in fp32")
+                              "2 r FLOP per (query row, centroid) pair, one fp16 MFMA pass on power-of-two-scaled "
+                              "copies (peak 2.5 PFLOP/s); the candidates within its error bound of the threshold "
+                              "(~100 per query block at 1M) are re-scored with the three-pass split products")
         elif name == "attn_band":
             out[name] = _roof("mfma", 512 * band_pairs(w), sec, PEAK_BF16_TFLOPS, "TFLOP/s",
                               "4 D FLOP per (query, key) pair of the band heads' key sets")
