@@ -445,6 +445,7 @@ int run_kmeans(const ha_layer_desc* d, const float* klow, float* cent, int32_t* 
   kp.almax = kp.cmax + Hkv;
   kp.n_amb = kp.almax + Hkv;
   kp.amb = reinterpret_cast<int32_t*>(align_up(reinterpret_cast<uintptr_t>(kp.n_amb + Hkv)));
+  kp.best = reinterpret_cast<uint64_t*>(align_up(reinterpret_cast<uintptr_t>(kp.amb + Hkv * (size_t)d->n_tokens)));
   return dev_status(launch_kmeans(kp, d->n_kv_heads, d->kmeans_iters, s));
 }
 

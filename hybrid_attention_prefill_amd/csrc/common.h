@@ -139,6 +139,7 @@ struct KmeansParams {
   uint32_t* almax;     // scratch [Hkv]: largest squared norm of the centroids' fp16 lo parts (fp32 bits)
   uint32_t* n_amb;     // scratch [Hkv]: keys the approximate assignment left undecided
   int32_t* amb;        // scratch [Hkv, N]: their positions
+  uint64_t* best;      // scratch [Hkv, N]: per undecided key, min over centroid ranges of (ordered distance, index)
   int N, M, stride, n_chunks;
 };
 size_t kmeans_scratch_bytes(int N, int M, int Hkv);

@@ -142,9 +142,21 @@ constexpr int kCStr = 24;         // 16-bit row stride of a staged part (48 B: c
 constexpr int KT = 4;             // 32-key blocks per wave
 constexpr float kPadNorm = 1e30f; // norm of the padding rows of a partial tile
 
-// It assigns the keys the approximate pass (km_assign_approx_kernel) left
-// undecided, p.amb[g][0 .. p.n_amb[g]); workgroups past the count exit at
-// once.
+// It scores the keys the approximate pass (km_assign_approx_kernel) left
+// undecided, p.amb[g][0 .. p.n_amb[g]), against one of kExactSplit ranges of
+// centroids (blockIdx.z; few keys are undecided, so the ranges spread them
+// over the chip): per key the range's minimum and its index, lowest index on
+// equal distances, go into p.best[g][slot] by a 64-bit atomic minimum of
+// (order key of the distance, index), which keeps the lowest index of the
+// overall minimum whatever the ranges' order; km_assign_commit_kernel writes
+// them out.  Workgroups step over the key blocks, so the grid needs no
+// count of them.
+constexpr int kExactSplit = 8;
+constexpr int kExactBlocks = 64;   // workgroups per KV head and range (at most)
+__device__ __forceinline__ uint32_t order_key(float d) {
+  const uint32_t u = __float_as_uint(d);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
 __global__ __launch_bounds__(NT) void km_assign_exact_kernel(KmeansParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t cs[2][kCChunk * kCStr];
   __shared__ __attribute__((aligned(16))) float cns[kCChunk];   // |C_m|^2 of the staged centroids
@@ -152,9 +164,12 @@ __global__ __launch_bounds__(NT) void km_assign_exact_kernel(KmeansParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, lr = lane & 31, lh = lane >> 5;
   const int n_keys = (int)p.n_amb[g];
-  if ((int)blockIdx.x * 4 * 32 * KT >= n_keys) return;
-  const int j0 = (blockIdx.x * 4 + wave) * (32 * KT);
+  const int span = ((p.M + kExactSplit - 1) / kExactSplit + 31) / 32 * 32;
+  const int c_lo = (int)blockIdx.z * span, c_hi = min(p.M, c_lo + span);
+  if (c_lo >= c_hi) return;
   const float ksc = -2.f * key_scale(p.amax[g]);
+  for (int kb = blockIdx.x; kb * 4 * 32 * KT < n_keys; kb += gridDim.x) {
+  const int j0 = (kb * 4 + wave) * (32 * KT);
   // key of slot i (slots past the count repeat the last key and write nothing)
   auto key_of = [&](int i) { return (int)p.amb[(size_t)g * p.N + min(n_keys - 1, i)]; };
   dev::f16x8 kh[KT], kl[KT];
@@ -179,8 +194,8 @@ __global__ __launch_bounds__(NT) void km_assign_exact_kernel(KmeansParams p) {
   }
   const _Float16* parts[2] = {p.c_hi + (size_t)g * p.M * R, p.c_lo + (size_t)g * p.M * R};
   const float* cn = p.c_norm + (size_t)g * p.M;
-  for (int c0 = 0; c0 < p.M; c0 += kCChunk) {
-    const int nc = min(kCChunk, p.M - c0);
+  for (int c0 = c_lo; c0 < c_hi; c0 += kCChunk) {
+    const int nc = min(kCChunk, c_hi - c0);
     __syncthreads();
     {
       // thread t stages centroid c0 + t: two 32-B parts and the norm row
@@ -252,10 +267,23 @@ __global__ __launch_bounds__(NT) void km_assign_exact_kernel(KmeansParams p) {
   for (int kt = 0; kt < KT; ++kt) {
     const float ob = __shfl_xor(best[kt], 32);
     const int oa = __shfl_xor(arg[kt], 32);
-    if (ob < best[kt] || (ob == best[kt] && oa < arg[kt])) arg[kt] = oa;
+    const bool take = ob < best[kt] || (ob == best[kt] && oa < arg[kt]);
+    const float b = take ? ob : best[kt];
+    const int a = take ? oa : arg[kt];
     const int i = j0 + kt * 32 + lr;
-    if (lh == 0 && i < n_keys) p.assign[(size_t)g * p.N + key_of(i)] = arg[kt];
+    if (lh == 0 && i < n_keys)
+      atomicMin(reinterpret_cast<unsigned long long*>(p.best + (size_t)g * p.N + i),
+                ((unsigned long long)order_key(b) << 32) | (uint32_t)a);
   }
+  }
+}
+
+// The undecided keys' assignments: the index half of p.best.
+__global__ __launch_bounds__(NT) void km_assign_commit_kernel(KmeansParams p) {
+  const int g = blockIdx.y;
+  const int n_keys = (int)p.n_amb[g];
+  for (int i = blockIdx.x * NT + threadIdx.x; i < n_keys; i += gridDim.x * NT)
+    p.assign[(size_t)g * p.N + p.amb[(size_t)g * p.N + i]] = (int32_t)(uint32_t)p.best[(size_t)g * p.N + i];
 }
 
 // Approximate assignment with certification; the exact kernel above defines
@@ -323,6 +351,7 @@ __global__ __launch_bounds__(NT, 4) void km_assign_approx_kernel(KmeansParams p)
     x1[kt] = 0;
   }
   const _Float16* chi = p.c_hi + (size_t)g * p.M * R;
+  const _Float16* clo = p.c_lo + (size_t)g * p.M * R;
   const float* cn = p.c_norm + (size_t)g * p.M;
   for (int c0 = 0; c0 < p.M; c0 += kCChunk) {
     const int nc = min(kCChunk, p.M - c0);
@@ -412,10 +441,47 @@ __global__ __launch_bounds__(NT, 4) void km_assign_approx_kernel(KmeansParams p)
     const float ob1 = __uint_as_float(dev::pair32_other(__float_as_uint(sb1)));
     const float ob2 = __uint_as_float(dev::pair32_other(__float_as_uint(sb2)));
     const int oi1 = (int)dev::pair32_other((uint32_t)i1);
-    const float B1 = fminf(sb1, ob1), B2 = fminf(fmaxf(sb1, ob1), fminf(sb2, ob2));
+    const float B2 = fminf(fmaxf(sb1, ob1), fminf(sb2, ob2));
     const int I1 = (sb1 < ob1 || (sb1 == ob1 && i1 < oi1)) ? i1 : oi1;
-    const bool cert = B2 - B1 > 2.f * eps[kt];
+    // the winner's three-product value (hi.hi + hi.lo + lo.hi over the same
+    // fp16 parts as the exact kernel, fp32 dot products), each lane half
+    // taking its 8 components
     const int j = j0 + kt * 32 + lr;
+    float dw, kn;
+    {
+      const float* kp = p.klow + ((size_t)g * p.N + min(p.N - 1, j)) * R + lh * 8;
+      dev::f16x8 kl8;
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = ksc * kp[e];
+        ss = fmaf(v, v, ss);
+        _Float16 h, l;
+        dev::split2_f16(v, h, l);
+        kl8[e] = l;
+      }
+      kn = sqrtf(dev::pair32_sum(ss));
+      const dev::u32x4 klw = __builtin_bit_cast(dev::u32x4, kl8);
+      const dev::u32x4 chw = *reinterpret_cast<const dev::u32x4*>(chi + (size_t)I1 * R + lh * 8);
+      const dev::u32x4 clw = *reinterpret_cast<const dev::u32x4*>(clo + (size_t)I1 * R + lh * 8);
+      float part = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t a = chw[q], b = clw[q], x = kw[q], y = klw[q];
+        part = __builtin_amdgcn_fdot2(__builtin_bit_cast(dev::f16x2, a), __builtin_bit_cast(dev::f16x2, x), part, false);
+        part = __builtin_amdgcn_fdot2(__builtin_bit_cast(dev::f16x2, a), __builtin_bit_cast(dev::f16x2, y), part, false);
+        part = __builtin_amdgcn_fdot2(__builtin_bit_cast(dev::f16x2, b), __builtin_bit_cast(dev::f16x2, x), part, false);
+      }
+      const float other = __uint_as_float(dev::pair32_other(__float_as_uint(part)));
+      dw = cn[I1] + (lh ? other + part : part + other);
+    }
+    // every other centroid's approximate value is within eps of its exact
+    // one, and dw within tw of the winner's exact value (the same terms in
+    // another fp32 order, and fp16 subnormal handling): if the second
+    // smallest approximate value, lowered by eps, still exceeds dw + tw,
+    // the winner is the exact kernel's unique minimum
+    const float tw = 0x1p-17f * (cmx * cmx + kn * cmx) + 0x1p-10f * (kn + cmx);
+    const bool cert = B2 - eps[kt] > dw + tw;
     const bool mine = lh == 0 && j < p.N;
     if (mine && cert) p.assign[(size_t)g * p.N + j] = I1;
     // undecided keys: one atomic per wave, slots in lane order
@@ -425,7 +491,11 @@ __global__ __launch_bounds__(NT, 4) void km_assign_approx_kernel(KmeansParams p)
       uint32_t base = 0u;
       if (lane == 0) base = atomicAdd(&p.n_amb[g], (uint32_t)__popcll(bal));
       base = __shfl(base, 0);
-      if (amb) list[base + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull))] = (uint32_t)j;
+      if (amb) {
+        const uint32_t slot = base + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
+        list[slot] = (uint32_t)j;
+        p.best[(size_t)g * p.N + slot] = ~0ull;
+      }
     }
   }
 }
@@ -1160,7 +1230,7 @@ size_t kmeans_scratch_bytes(int N, int M, int Hkv) {
   const size_t n_chunks = (size_t)(N + kChunk - 1) / kChunk;
   return (size_t)Hkv * n_chunks * M * sizeof(int32_t) + (size_t)Hkv * M * sizeof(int32_t) +
          (size_t)Hkv * M * (2 * R * sizeof(_Float16) + sizeof(float)) + 4 * (size_t)Hkv * sizeof(uint32_t) +
-         (size_t)Hkv * N * sizeof(int32_t) + 512;
+         (size_t)Hkv * N * sizeof(int32_t) + (size_t)Hkv * N * sizeof(uint64_t) + 768;
 }
 
 hipError_t launch_kmeans(KmeansParams p, int Hkv, int iters, hipStream_t s) {
@@ -1170,11 +1240,14 @@ hipError_t launch_kmeans(KmeansParams p, int Hkv, int iters, hipStream_t s) {
   hipLaunchKernelGGL(km_amax_kernel, dim3(amax_blocks, Hkv), dim3(NT), 0, s, p);
   hipError_t e = hipGetLastError();
   const dim3 assign_grid((p.N + 4 * 32 * KT - 1) / (4 * 32 * KT), Hkv);
+  const dim3 exact_grid(std::min<int>(kExactBlocks, assign_grid.x), Hkv, kExactSplit);
+  const dim3 commit_grid(std::min<int>(256, (p.N + NT - 1) / NT), Hkv);
   for (int it = 0; it < iters && e == hipSuccess; ++it) {
     hipLaunchKernelGGL(km_clear_kernel, dim3(1), dim3(kMaxHeads), 0, s, p, Hkv);
     hipLaunchKernelGGL(km_prep_kernel, dim3((p.M + NT - 1) / NT, Hkv), dim3(NT), 0, s, p);
     hipLaunchKernelGGL(km_assign_approx_kernel, assign_grid, dim3(NT), 0, s, p);
-    hipLaunchKernelGGL(km_assign_exact_kernel, assign_grid, dim3(NT), 0, s, p);
+    hipLaunchKernelGGL(km_assign_exact_kernel, exact_grid, dim3(NT), 0, s, p);
+    hipLaunchKernelGGL(km_assign_commit_kernel, commit_grid, dim3(NT), 0, s, p);
     hipLaunchKernelGGL(km_hist_kernel, dim3(p.n_chunks, Hkv), dim3(NT), 0, s, p);
     hipLaunchKernelGGL(km_colscan_kernel, dim3((p.M + NT - 1) / NT, Hkv), dim3(NT), 0, s, p);
     hipLaunchKernelGGL(km_offsets_kernel, dim3(Hkv), dim3(NT), 0, s, p);
