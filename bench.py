@@ -48,8 +48,8 @@ PEAK_SPLIT3_TFLOPS = PEAK_BF16_TFLOPS / 3   # fp32-accurate products as three 16
 # were taken on (digest of the listed sources plus the hipcc flags).
 TRAFFIC = {
     ("dense_llama8b_128k", "attn_band"): {
-        "bytes": 20746561494, "sources": ("attn.hip", "common.h", "device_util.h"),
-        "digest": "53272c80a7b935ed"},
+        "bytes": 20714940490, "sources": ("attn.hip", "common.h", "device_util.h"),
+        "digest": "90d95074a0c3a465"},
 }
 
 
@@ -252,7 +252,7 @@ def stage_rooflines(w, stage_ms, work, window_ms=None):
             out[name] = _roof("mfma", 32 * w.kmeans_iters * Hkv * N * w.n_clusters, sec, PEAK_BF16_TFLOPS,
                               "TFLOP/s", "2 r FLOP per (key, centroid) pair per Lloyd iteration; one fp16 MFMA pass "
                               "decides every key whose two best distances lie further apart than its error bound "
-                              "(peak 2.5 PFLOP/s), the undecided keys (~15% at 1M) take the three-pass split "
+                              "(peak 2.5 PFLOP/s), the undecided keys (3-5% at 1M) take the three-pass split "
                               "products; the update is HBM / integer work")
         elif name == "select_clusters":
             out[name] = _roof("mfma", 32 * Hret * N * w.n_clusters, sec, PEAK_BF16_TFLOPS, "TFLOP/s",

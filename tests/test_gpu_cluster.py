@@ -124,6 +124,43 @@ def test_kmeans_ragged_chunks_and_empty_clusters():
     _kmeans_staged(w, li, 3)
 
 
+def test_kmeans_equal_centroids_in_different_ranges_take_the_lowest_index():
+    # Centroid seeds 5, 700 and 1000 coincide (their key rows are equal) and
+    # lie in different ones of the 8 centroid ranges the exact assignment
+    # pass spreads its keys over; no key near them can be decided by the
+    # one-product pass (best and second equal), so the lowest-index rule must
+    # hold across ranges.  Iteration 1: no key may go to 700 or 1000, and the
+    # three equal keys go to 5.  Iteration 2: 5 has moved to its members'
+    # mean, 700 and 1000 are empty and still equal, so no key may go to 1000
+    # and the three equal keys (distance 0 to 700) go to 700.
+    w = synth.configs.shrink(synth.WORKLOADS["allsparse_1m"], 16384, n_clusters=1024, window=512, n_needles=0)
+    w = w.with_(kmeans_stride=16)
+    print(f"\n[case] kmeans equal centroids across ranges N={w.n_tokens} M={w.n_clusters}", flush=True)
+    li = synth.make_layer_inputs(w, with_q=False)
+    dup = [5 * 16, 700 * 16, 1000 * 16]
+    for j in dup[1:]:
+        li.K[j] = li.K[dup[0]]
+    K = _gpu.dev_bf16(li.K)
+    d = ha.make_desc(w.n_tokens, w.n_q_heads, w.n_kv_heads, w.head_dim, window=w.window, topk=w.topk)
+    klow = torch.empty((w.n_kv_heads, w.n_tokens, 16), dtype=torch.float32, device="cuda")
+    ha.ha_index_project(d, w.head_kind, None, K, _gpu.dev_f32(li.P), None, klow)
+    torch.cuda.synchronize()
+    X = klow.cpu().numpy()
+    C1, a1, _, _ = _kmeans_gpu(w, klow, 1)
+    _, a2, _, _ = _kmeans_gpu(w, klow, 2)
+    for g in range(w.n_kv_heads):
+        assert np.array_equal(X[g][dup[0]], X[g][dup[1]]) and np.array_equal(X[g][dup[0]], X[g][dup[2]])
+        assert not np.isin(a1[g], [700, 1000]).any(), f"kv {g}: iteration 1 used a higher equal centroid"
+        assert (a1[g][dup] == 5).all(), f"kv {g}: {a1[g][dup]}"
+        assert np.array_equal(C1[g][700], C1[g][1000])
+        assert not (a2[g] == 1000).any(), f"kv {g}: iteration 2 used centroid 1000 over the equal 700"
+        # 5 has moved clearly away (other members) in these inputs: the equal
+        # keys, at distance 0 from 700, are no near-tie with it
+        c = C1[g].astype(np.float64)
+        assert np.sum((c[5] - c[700]) ** 2) > 1e-4 * np.dot(c[700], c[700])
+        assert (a2[g][dup] == 700).all(), f"kv {g}: {a2[g][dup]}"
+
+
 @pytest.mark.parametrize("scale", [1e4, 2.0 ** 14, 1e-3, 2.0 ** -14, 1e20, 1e-20])
 def test_kmeans_key_range(scale):
     # Low-rank keys far from unit scale: each KV head is brought into range by
