@@ -521,7 +521,19 @@ __global__ __launch_bounds__(NT) void km_colscan_kernel(KmeansParams p) {
   if (m >= p.M) return;
   int32_t* col = p.hist + (size_t)g * p.n_chunks * p.M + m;
   int run = 0;
-  for (int c = 0; c < p.n_chunks; ++c) {
+  int c = 0;
+  // eight chunks' counts in flight at a time
+  for (; c + 8 <= p.n_chunks; c += 8) {
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = col[(size_t)(c + u) * p.M];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      col[(size_t)(c + u) * p.M] = run;
+      run += v[u];
+    }
+  }
+  for (; c < p.n_chunks; ++c) {
     const int v = col[(size_t)c * p.M];
     col[(size_t)c * p.M] = run;
     run += v;
@@ -529,33 +541,45 @@ __global__ __launch_bounds__(NT) void km_colscan_kernel(KmeansParams p) {
   p.count[(size_t)g * p.M + m] = run;
 }
 
-// offsets: exclusive scan of the counts over clusters (one workgroup per KV head)
+// offsets: exclusive scan of the counts over clusters (one workgroup per KV
+// head): each thread sums a contiguous run of counts, a workgroup scan of
+// the sums gives every run's start, and the run is written out
 __global__ __launch_bounds__(NT) void km_offsets_kernel(KmeansParams p) {
-  __shared__ int part[NT];
+  __shared__ int tmp[NT / 64];
   const int g = blockIdx.x, tid = threadIdx.x;
   const int per = (p.M + NT - 1) / NT;
   const int a = min(p.M, tid * per), b = min(p.M, a + per);
   const int32_t* cnt = p.count + (size_t)g * p.M;
   int s = 0;
-  for (int m = a; m < b; ++m) s += cnt[m];
-  part[tid] = s;
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int t = 0; t < NT; ++t) {
-      const int v = part[t];
-      part[t] = run;
-      run += v;
+  int m = a;
+  for (; m + 8 <= b; m += 8) {
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = cnt[m + u];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; m < b; ++m) s += cnt[m];
+  int total;
+  const int base = dev::block_excl_scan<NT / 64>(s, tmp, &total);
+  int32_t* off = p.csr_off + (size_t)g * (p.M + 1);
+  int run = base;
+  m = a;
+  for (; m + 8 <= b; m += 8) {
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = cnt[m + u];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      off[m + u] = run;
+      run += v[u];
     }
   }
-  __syncthreads();
-  int32_t* off = p.csr_off + (size_t)g * (p.M + 1);
-  int run = part[tid];
-  for (int m = a; m < b; ++m) {
+  for (; m < b; ++m) {
     off[m] = run;
     run += cnt[m];
   }
-  if (tid == NT - 1) off[p.M] = run;
+  if (tid == 0) off[p.M] = total;
 }
 
 // stable scatter of key positions into CSR order, one workgroup per chunk
@@ -608,7 +632,19 @@ __global__ __launch_bounds__(NT) void km_update_kernel(KmeansParams p) {
   if (hi <= lo) return;
   const float* kl = p.klow + (size_t)g * p.N * R;
   float s = 0.f;
-  for (int x = lo; x < hi; ++x) s += kl[(size_t)mem[x] * R + r];
+  int x = lo;
+  // eight members' loads in flight, added in member order
+  for (; x + 8 <= hi; x += 8) {
+    int j[8];
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) j[u] = mem[x + u];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = kl[(size_t)j[u] * R + r];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; x < hi; ++x) s += kl[(size_t)mem[x] * R + r];
   p.cent[((size_t)g * p.M + m) * R + r] = s / (float)(hi - lo);
 }
 
