@@ -152,7 +152,7 @@ constexpr float kPadNorm = 1e30f; // norm of the padding rows of a partial tile
 // them out.  Workgroups step over the key blocks, so the grid needs no
 // count of them.
 constexpr int kExactSplit = 8;
-constexpr int kExactBlocks = 64;   // workgroups per KV head and range (at most)
+constexpr int kExactBlocks = 128;  // workgroups per KV head and range (at most)
 __device__ __forceinline__ uint32_t order_key(float d) {
   const uint32_t u = __float_as_uint(d);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
