@@ -597,14 +597,24 @@ __global__ __launch_bounds__(NT) void km_scatter_kernel(KmeansParams p) {
   const int a = ch * kChunk, b = min(p.N, a + kChunk);
   const int32_t* as = p.assign + (size_t)g * p.N;
   int32_t* mem = p.csr_mem + (size_t)g * p.N;
+  // the chunk's assignments, all loads in flight at once (thread t holds
+  // positions a + t + NT i)
+  constexpr int kPer = kChunk / NT;
+  int cl[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int j = a + tid + NT * i;
+    cl[i] = j < b ? as[j] : -1;
+  }
   // Keys in position order, NT at a time.  In each round the lowest thread
   // still holding a key of cluster c (the earliest position) takes c's next
   // slot, so every cluster's members stay in ascending position; a round
   // places one key per distinct cluster, and a batch rarely holds the same
   // cluster twice.
-  for (int j0 = a; j0 < b; j0 += NT) {
-    const int j = j0 + tid;
-    const int c = j < b ? as[j] : -1;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int j = a + tid + NT * i;
+    const int c = cl[i];
     bool left = c >= 0;
     while (__syncthreads_or(left)) {
       if (left) atomicMin(&owner[c], tid);
