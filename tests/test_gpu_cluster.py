@@ -161,6 +161,19 @@ def test_kmeans_equal_centroids_in_different_ranges_take_the_lowest_index():
         assert (a2[g][dup] == 700).all(), f"kv {g}: {a2[g][dup]}"
 
 
+@pytest.mark.parametrize("M", [1, 33, 257, 1000])
+def test_kmeans_cluster_counts_and_centroid_ranges(M):
+    # cluster counts that leave the exact pass one range (1), ranges smaller
+    # than a tile (33), a partial last range (257: ranges of 64) and a partial
+    # last tile inside the last of 8 ranges (1000: ranges of 128)
+    N = 4096 + 7
+    w = synth.configs.shrink(synth.WORKLOADS["allsparse_1m"], N, n_clusters=M, window=256, n_needles=0)
+    w = w.with_(kmeans_stride=N // M)
+    print(f"\n[case] kmeans N={w.n_tokens} M={M}", flush=True)
+    li = synth.make_layer_inputs(w, with_q=False)
+    _kmeans_staged(w, li, 3)
+
+
 @pytest.mark.parametrize("scale", [1e4, 2.0 ** 14, 1e-3, 2.0 ** -14, 1e20, 1e-20])
 def test_kmeans_key_range(scale):
     # Low-rank keys far from unit scale: each KV head is brought into range by
