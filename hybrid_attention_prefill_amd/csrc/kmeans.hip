@@ -302,10 +302,16 @@ __global__ __launch_bounds__(NT) void km_assign_commit_kernel(KmeansParams p) {
 // the lane recomputes its 16 values of tile x1 with fp32 dot products of the
 // same fp16 operands (only the accumulation order differs) for the index of
 // b1 (lowest on equal values) and the tile's second smallest value w2.  The
-// halves merge; when the second smallest over all centroids exceeds b1 by
-// more than 2 eps, the best centroid under the exact distances is that one,
-// alone, and is written.  Otherwise the key is appended to p.amb for the
-// exact kernel (the list order varies; each key's result does not).
+// halves merge into the winner I1 and the second smallest value B2 over all
+// other centroids.  The winner's own three-product value dw (hi.hi + hi.lo +
+// lo.hi over the exact kernel's fp16 parts, fp32 dot products) lies within
+// tw = 2^-17 (max|C'|^2 + |k'| max|C'|) + 2^-10 (|k'| + max|C'|) of the
+// exact kernel's value (another summation order, fp16 subnormal handling),
+// and every other centroid's exact value is at least its approximate value
+// minus eps; so when B2 - eps > dw + tw, I1 is the exact kernel's unique
+// minimum and is written.  Otherwise the key is appended to p.amb (its
+// p.best entry set to all ones) for the exact kernel (the list order
+// varies; each key's result does not).
 //
 // The accumulator seed |C'_m|^2 comes from one more MFMA instead of 16 LDS
 // floats per lane: the norm split into three bf16 parts (exact: 24 bits) in
